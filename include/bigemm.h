@@ -1,0 +1,152 @@
+/*
+ * bigemm — batch-invariant matrix multiply Y = X * W for AMD Instinct MI355X (gfx950).
+ *
+ * Batch invariance is the property the CANN ops-transformer issue defines in
+ * its problem statement: output row i is a function of input row i and the
+ * shared weight only, y[i] = f(x[i], W), never of the other rows. The
+ * nondeterminism blog (section "batch-invariant matrix multiplication")
+ * gives the recipe: keep the whole K reduction of each output tile inside one
+ * worker, never split K, and compile exactly one kernel configuration that
+ * every shape uses. This library is that recipe on CDNA4: one fixed tile
+ * configuration per input type, the K blocks walked in ascending order by a
+ * single workgroup, one MFMA shape at every M, no atomics, no workspace.
+ *
+ * Consequences the caller can rely on (per handle, device and library build):
+ *   - the bytes of Y[i, :] depend only on the bytes of X[i, :] (and of
+ *     X_scale[i, :] for MXFP8), on W (and W_scale), on N, K and the
+ *     leading dimensions' validity — not on M, not on the contents of other
+ *     rows, not on i itself (the row's position in the batch);
+ *   - repeated calls on the same inputs give identical bytes.
+ *
+ * All functions are C ABI, never throw, and return a bigemm_status.
+ */
+#ifndef BIGEMM_H
+#define BIGEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BIGEMM_ABI_VERSION 1
+
+/* Exported entry points (the library is built with hidden visibility by default). */
+#if defined(__GNUC__)
+#define BIGEMM_API __attribute__((visibility("default")))
+#else
+#define BIGEMM_API
+#endif
+
+typedef struct bigemm_s* bigemm_t;
+
+typedef enum {
+  BIGEMM_OK = 0,
+  BIGEMM_ERR_ARG = 1,          /* invalid argument; nothing was launched                    */
+  BIGEMM_ERR_UNSUPPORTED = 2,  /* device is not gfx950, or dtype combination not provided   */
+  BIGEMM_ERR_DEVICE = 3,       /* a HIP call or the kernel launch failed                     */
+  BIGEMM_ERR_NOMEM = 4         /* host allocation of the handle failed                       */
+} bigemm_status;
+
+typedef enum {
+  BIGEMM_BF16 = 1,  /* bfloat16: the top 16 bits of an IEEE binary32                            */
+  BIGEMM_F32 = 2,   /* IEEE binary32                                                           */
+  BIGEMM_E4M3 = 3,  /* OCP E4M3FN (bias 7, 3 mantissa bits, no infinities, S.1111.111 = NaN)    */
+  BIGEMM_E8M0 = 4   /* OCP E8M0 block scale, 2^(byte - 127), 0xFF = NaN                         */
+} bigemm_dtype;
+
+/*
+ * Operation descriptor. Two combinations are provided:
+ *   bf16:  x_type = w_type = BIGEMM_BF16, y_type = BIGEMM_F32, scale_block = 0
+ *   MXFP8: x_type = w_type = BIGEMM_E4M3, y_type = BIGEMM_F32, scale_block = 32
+ *          (one E8M0 scale per 32 consecutive K elements — the MXFP8 path with a
+ *          K-varying scale named in the CANN issue's background and grid)
+ * Fields are int32_t (holding bigemm_dtype values) to keep the struct layout fixed.
+ */
+typedef struct {
+  int32_t x_type;
+  int32_t w_type;
+  int32_t y_type;
+  int32_t scale_block;
+} bigemm_desc;
+
+/*
+ * Create a handle for the current HIP device.
+ * Takes no M, N or K: the configuration cannot depend on the problem shape.
+ * Returns BIGEMM_ERR_UNSUPPORTED on any device other than gfx950 and for any
+ * descriptor other than the two above — it never falls back to another path.
+ * Ownership: the handle owns only immutable configuration; free it with
+ * bigemm_destroy. *out is set to NULL on failure.
+ */
+BIGEMM_API bigemm_status bigemm_create(const bigemm_desc* desc, bigemm_t* out);
+
+/*
+ * Enqueue Y = X * W on `stream` (a hipStream_t; NULL = the null stream) and
+ * return without synchronising.
+ *
+ * Shapes and layouts (row-major, leading dimensions in ELEMENTS):
+ *   X [M, K], leading dimension ldx >= K     (bf16 bits or E4M3 bytes)
+ *   W [K, N], leading dimension ldw >= N     (bf16 bits or E4M3 bytes)
+ *   Y [M, N], leading dimension ldy >= N     (float32, written, never read)
+ *   MXFP8 only:
+ *   X_scale [M, K/32], leading dimension ldxs >= K/32   (E8M0 bytes)
+ *   W_scale [K/32, N], leading dimension ldws >= N      (E8M0 bytes)
+ * Each X element at [i, k] is multiplied by 2^(X_scale[i, k/32] - 127) and
+ * each W element at [k, j] by 2^(W_scale[k/32, j] - 127).
+ *
+ * Requirements (violations return BIGEMM_ERR_ARG synchronously; nothing is
+ * launched and Y is untouched):
+ *   M >= 0, N >= 1, K >= 1; M == 0 is a successful no-op;
+ *   bf16:  K % 8 == 0, N % 8 == 0;  MXFP8: K % 32 == 0, N % 16 == 0;
+ *   X, W, Y non-NULL when M > 0, 16-byte aligned; ldx, ldw, ldy such that
+ *   every row starts 16-byte aligned (ldx*esize, ldw*esize, ldy*4 multiples of 16);
+ *   MXFP8: X_scale, W_scale non-NULL (no alignment requirement);
+ *   bf16:  X_scale and W_scale NULL;
+ *   128 * ldx * esize, 128 * ldw * esize, 128 * ldy * 4 below 2^31.
+ * Y must not overlap X, W or the scales (not checked).
+ *
+ * Memory: all buffers are device memory owned by the caller. The library
+ * allocates nothing per call (there is no split-K and hence no workspace).
+ * Errors: BIGEMM_ERR_ARG as above; BIGEMM_ERR_DEVICE if the launch fails (the
+ * HIP error is consumed). Concurrent calls on different streams are safe;
+ * bigemm_destroy must not race with calls in flight.
+ */
+BIGEMM_API bigemm_status bigemm_run(bigemm_t h, int64_t M, int64_t N, int64_t K,
+                         const void* X, int64_t ldx,
+                         const void* W, int64_t ldw,
+                         void* Y, int64_t ldy,
+                         const void* X_scale, int64_t ldxs,
+                         const void* W_scale, int64_t ldws,
+                         void* stream);
+
+/* Release a handle. NULL is accepted. */
+BIGEMM_API bigemm_status bigemm_destroy(bigemm_t h);
+
+/* Static, NUL-terminated description of a status code. */
+BIGEMM_API const char* bigemm_status_str(bigemm_status s);
+
+/*
+ * The one compiled tile configuration behind a handle (evidence that it is
+ * fixed): output tile bm x bn and K-block bk. Any output pointer may be NULL.
+ */
+BIGEMM_API bigemm_status bigemm_get_config(bigemm_t h, int32_t* bm, int32_t* bn, int32_t* bk);
+
+/*
+ * The argument checks bigemm_run performs, as a pure host function: no HIP
+ * call, no device access, pointers are only tested for NULL and alignment.
+ */
+BIGEMM_API bigemm_status bigemm_check_args(const bigemm_desc* desc, int64_t M, int64_t N, int64_t K,
+                                const void* X, int64_t ldx,
+                                const void* W, int64_t ldw,
+                                const void* Y, int64_t ldy,
+                                const void* X_scale, int64_t ldxs,
+                                const void* W_scale, int64_t ldws);
+
+/* BIGEMM_ABI_VERSION of the loaded library. */
+BIGEMM_API int32_t bigemm_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BIGEMM_H */

@@ -1,0 +1,212 @@
+"""Python binding of libbigemm (the batch-invariant GEMM for MI355X / gfx950).
+
+The functions named ``bigemm_*`` mirror the C ABI in ``include/bigemm.h``
+one to one and only marshal arguments (integers for device pointers and
+streams). ``mm`` is a convenience wrapper over them for torch tensors; torch
+supplies device memory and the current stream, nothing else — every step of
+the product runs in the HIP kernels of ``libbigemm.so``.
+
+There is no fallback: if the library is missing or the device is not gfx950
+the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+__all__ = [
+    "BIGEMM_OK", "BIGEMM_ERR_ARG", "BIGEMM_ERR_UNSUPPORTED", "BIGEMM_ERR_DEVICE", "BIGEMM_ERR_NOMEM",
+    "BIGEMM_BF16", "BIGEMM_F32", "BIGEMM_E4M3", "BIGEMM_E8M0",
+    "BigemmError", "bigemm_desc", "library_path", "load",
+    "bigemm_create", "bigemm_run", "bigemm_destroy", "bigemm_status_str", "bigemm_get_config",
+    "bigemm_check_args", "bigemm_abi_version", "mm",
+]
+
+BIGEMM_OK = 0
+BIGEMM_ERR_ARG = 1
+BIGEMM_ERR_UNSUPPORTED = 2
+BIGEMM_ERR_DEVICE = 3
+BIGEMM_ERR_NOMEM = 4
+
+BIGEMM_BF16 = 1
+BIGEMM_F32 = 2
+BIGEMM_E4M3 = 3
+BIGEMM_E8M0 = 4
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libbigemm.so")
+_lib = None
+_lock = threading.Lock()
+
+
+class BigemmError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {_status_str(status)} (status {status})")
+
+
+class bigemm_desc(ctypes.Structure):
+    _fields_ = [("x_type", ctypes.c_int32), ("w_type", ctypes.c_int32),
+                ("y_type", ctypes.c_int32), ("scale_block", ctypes.c_int32)]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load libbigemm.so (built in-tree by ``__graft_entry__.build()``); raise if absent."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is not built; run __graft_entry__.build() first")
+        lib = ctypes.CDLL(_LIB_PATH)
+        i64, vp, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32
+        lib.bigemm_create.restype = ctypes.c_int
+        lib.bigemm_create.argtypes = [ctypes.POINTER(bigemm_desc), ctypes.POINTER(vp)]
+        lib.bigemm_run.restype = ctypes.c_int
+        lib.bigemm_run.argtypes = [vp, i64, i64, i64, vp, i64, vp, i64, vp, i64, vp, i64, vp, i64, vp]
+        lib.bigemm_destroy.restype = ctypes.c_int
+        lib.bigemm_destroy.argtypes = [vp]
+        lib.bigemm_status_str.restype = ctypes.c_char_p
+        lib.bigemm_status_str.argtypes = [ctypes.c_int]
+        lib.bigemm_get_config.restype = ctypes.c_int
+        lib.bigemm_get_config.argtypes = [vp, ctypes.POINTER(i32), ctypes.POINTER(i32), ctypes.POINTER(i32)]
+        lib.bigemm_check_args.restype = ctypes.c_int
+        lib.bigemm_check_args.argtypes = [ctypes.POINTER(bigemm_desc), i64, i64, i64, vp, i64, vp, i64,
+                                          vp, i64, vp, i64, vp, i64]
+        lib.bigemm_abi_version.restype = i32
+        lib.bigemm_abi_version.argtypes = []
+        _lib = lib
+        return lib
+
+
+def _status_str(status: int) -> str:
+    try:
+        return load().bigemm_status_str(int(status)).decode()
+    except Exception:  # noqa: BLE001 - only used to format an error message
+        return "unknown"
+
+
+def bigemm_status_str(status: int) -> str:
+    return load().bigemm_status_str(int(status)).decode()
+
+
+def bigemm_abi_version() -> int:
+    return int(load().bigemm_abi_version())
+
+
+def _desc(x_type, w_type, y_type, scale_block):
+    return bigemm_desc(int(x_type), int(w_type), int(y_type), int(scale_block))
+
+
+def bigemm_create(x_type: int, w_type: int, y_type: int = BIGEMM_F32, scale_block: int = 0) -> int:
+    """Create a handle on the current HIP device; returns it as an integer. Raises BigemmError."""
+    h = ctypes.c_void_p()
+    d = _desc(x_type, w_type, y_type, scale_block)
+    st = load().bigemm_create(ctypes.byref(d), ctypes.byref(h))
+    if st != BIGEMM_OK:
+        raise BigemmError(st, "bigemm_create")
+    return int(h.value)
+
+
+def bigemm_destroy(h: int) -> int:
+    return int(load().bigemm_destroy(ctypes.c_void_p(h) if h else None))
+
+
+def bigemm_run(h: int, M: int, N: int, K: int, X: int, ldx: int, W: int, ldw: int, Y: int, ldy: int,
+               X_scale: int = 0, ldxs: int = 0, W_scale: int = 0, ldws: int = 0, stream: int = 0,
+               check: bool = True) -> int:
+    """Enqueue Y = X W (device pointers as integers). Raises BigemmError unless check=False."""
+    st = load().bigemm_run(ctypes.c_void_p(h) if h else None, M, N, K,
+                           X or None, ldx, W or None, ldw, Y or None, ldy,
+                           X_scale or None, ldxs, W_scale or None, ldws, stream or None)
+    if check and st != BIGEMM_OK:
+        raise BigemmError(st, "bigemm_run")
+    return int(st)
+
+
+def bigemm_get_config(h: int):
+    bm, bn, bk = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    st = load().bigemm_get_config(ctypes.c_void_p(h) if h else None, ctypes.byref(bm), ctypes.byref(bn),
+                                  ctypes.byref(bk))
+    if st != BIGEMM_OK:
+        raise BigemmError(st, "bigemm_get_config")
+    return bm.value, bn.value, bk.value
+
+
+def bigemm_check_args(x_type: int, w_type: int, y_type: int, scale_block: int, M: int, N: int, K: int,
+                      X: int, ldx: int, W: int, ldw: int, Y: int, ldy: int,
+                      X_scale: int = 0, ldxs: int = 0, W_scale: int = 0, ldws: int = 0) -> int:
+    """The library's argument validation (pure host function); returns the status code."""
+    d = _desc(x_type, w_type, y_type, scale_block)
+    return int(load().bigemm_check_args(ctypes.byref(d), M, N, K, X or None, ldx, W or None, ldw,
+                                        Y or None, ldy, X_scale or None, ldxs, W_scale or None, ldws))
+
+
+# ------------------------------------------------------------------ torch wrapper
+_handles = {}
+
+
+def _handle(kind: str, device_index: int) -> int:
+    import torch
+
+    key = (kind, device_index)
+    h = _handles.get(key)
+    if h is None:
+        with torch.cuda.device(device_index):
+            if kind == "bf16":
+                h = bigemm_create(BIGEMM_BF16, BIGEMM_BF16, BIGEMM_F32, 0)
+            else:
+                h = bigemm_create(BIGEMM_E4M3, BIGEMM_E4M3, BIGEMM_F32, 32)
+        _handles[key] = h
+    return h
+
+
+def mm(x, w, x_scale=None, w_scale=None, out=None, stream=None):
+    """Y = X W on the GPU through libbigemm.
+
+    bf16: ``x`` [M, K] and ``w`` [K, N] are torch.bfloat16 (or int16/uint16 bit
+    patterns). MXFP8: ``x``/``w`` are torch.float8_e4m3fn (or uint8 codes) and
+    ``x_scale`` [M, K/32], ``w_scale`` [K/32, N] are uint8 E8M0 bytes. Rows
+    must be contiguous; the leading dimension is taken from ``stride(0)``.
+    Returns ``out`` (float32 [M, N], allocated if None).
+    """
+    import torch
+
+    if x.dim() != 2 or w.dim() != 2:
+        raise ValueError("x and w must be 2-D")
+    M, K = x.shape
+    K2, N = w.shape
+    if K != K2:
+        raise ValueError(f"inner dimensions differ: {K} vs {K2}")
+    for t in (x, w):
+        if not t.is_cuda or (t.shape[1] > 1 and t.stride(1) != 1):
+            raise ValueError("operands must be CUDA tensors with contiguous rows")
+    mx = x_scale is not None or w_scale is not None
+    if mx:
+        if x.element_size() != 1 or w.element_size() != 1:
+            raise ValueError("MXFP8 operands must be 1-byte E4M3 codes")
+        if x_scale is None or w_scale is None:
+            raise ValueError("MXFP8 needs both x_scale and w_scale")
+    elif x.element_size() != 2 or w.element_size() != 2:
+        raise ValueError("bf16 operands must be 2-byte bf16 bit patterns")
+    dev = x.device.index if x.device.index is not None else torch.cuda.current_device()
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    if out.dtype != torch.float32 or tuple(out.shape) != (M, N) or (N > 1 and out.stride(1) != 1):
+        raise ValueError("out must be float32 [M, N] with contiguous rows")
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    h = _handle("mx" if mx else "bf16", dev)
+    if mx:
+        bigemm_run(h, M, N, K, x.data_ptr(), x.stride(0), w.data_ptr(), w.stride(0), out.data_ptr(),
+                   out.stride(0), x_scale.data_ptr(), x_scale.stride(0), w_scale.data_ptr(),
+                   w_scale.stride(0), stream)
+    else:
+        bigemm_run(h, M, N, K, x.data_ptr(), x.stride(0), w.data_ptr(), w.stride(0), out.data_ptr(),
+                   out.stride(0), 0, 0, 0, 0, stream)
+    return out

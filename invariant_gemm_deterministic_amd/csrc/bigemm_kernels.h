@@ -1,0 +1,21 @@
+// Internal interface between the C-ABI layer and the gfx950 kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bigemm {
+
+// The one tile configuration of each kernel.
+constexpr int kTileM = 128;
+constexpr int kTileN = 128;
+constexpr int kTileKBf16 = 64;
+constexpr int kTileKMx = 128;
+
+hipError_t launch_bf16(const void* X, const void* W, void* Y, int64_t M, int64_t N, int64_t K,
+                       int64_t ldx, int64_t ldw, int64_t ldy, hipStream_t stream);
+
+hipError_t launch_mxfp8(const void* X, const void* W, void* Y, const void* XS, const void* WS,
+                        int64_t M, int64_t N, int64_t K, int64_t ldx, int64_t ldw, int64_t ldy,
+                        int64_t ldxs, int64_t ldws, hipStream_t stream);
+
+}  // namespace bigemm

@@ -1,0 +1,514 @@
+// Batch-invariant GEMM kernels for CDNA4 (gfx950).
+//
+// The method is the one the nondeterminism blog gives in its section on
+// batch-invariant matrix multiplication: split the output into 2-D tiles, give
+// each tile to one worker that performs the whole K reduction itself, and use
+// a single compiled configuration for every shape. The CANN ops-transformer
+// issue (background) adds the failure mode to avoid: two kernel classes with
+// different K-loop schedules for different rows. So here:
+//
+//   * one tile shape (128 x 128 outputs, 4 waves of 64 x 64) and one MFMA shape
+//     per input type, whatever M, N or K;
+//   * every output element is produced by one lane of one wave, accumulating in
+//     fp32 registers over the K blocks in ascending order, then ascending MFMA
+//     steps inside the block — the same chain for interior and edge tiles;
+//   * rows >= M, columns >= N and K blocks past K are handled only through
+//     addresses: loads use out-of-range buffer offsets (which return zero) and
+//     stores use out-of-range offsets (which are dropped). There is no
+//     full-tile fast path and no branch on M.
+//
+// The grid size depends on M (ceil(M/128) * ceil(N/128) workgroups); the
+// workgroup -> tile map below only decides placement (which CU and XCD runs a
+// tile), never the arithmetic inside a tile.
+//
+// Data movement: global -> LDS with buffer_load_dwordx4 ... lds (no VGPR
+// staging), a 3-stage ring of LDS buffers, one barrier per K block. Operand
+// fragments come from LDS with ds_read_b128 (row operand, K contiguous) and
+// the transposing ds_read_b64_tr_b16 / ds_read_b64_tr_b8 (the W operand, which
+// is N-contiguous in memory). Both LDS tiles are XOR-swizzled at 16-byte
+// granularity so the fragment reads do not collide on LDS banks.
+//
+// Lane layouts used below (checked with exact small-integer products on the
+// device):
+//   v_mfma_f32_32x32x16_bf16: A lane l holds row l%32, k = 8*(l/32) + 0..7;
+//     B lane l holds column l%32, the same k; D register r of lane l is
+//     row 8*(r/4) + 4*(l/32) + r%4, column l%32.
+//   v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3): lane l holds row (or column)
+//     l%32; its bytes 0..15 are k = 16*(l/32) + 0..15 and bytes 16..31 are
+//     k = 32 + 16*(l/32) + 0..15; its scale operand is the E8M0 scale of that
+//     row (column) for the 32-wide K block l/32. D as above.
+//   ds_read_b64_tr_b16: in each 16-lane group, lane i element e is element
+//     i%4 of the 8 bytes addressed by lane 4e + i/4.
+//   ds_read_b64_tr_b8: in each 16-lane group, lane i byte e is byte i%8 of
+//     the 8 bytes addressed by lane 2e + i/8.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "bigemm_kernels.h"
+
+namespace bigemm {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+#define LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+constexpr int kThreads = 256;                 // 4 waves of 64, arranged 2 x 2
+constexpr int kTileBytes = 16384;             // one operand tile per stage (both dtypes)
+// Pipeline: three LDS stages (stage0..2 in each kernel), 96 KiB per workgroup.
+constexpr int kStageBytes = 2 * kTileBytes;   // X tile + W tile
+constexpr uint32_t kOob = 0x80000000u;        // buffer offset that is always out of range
+constexpr int kNumRecords = 0x7FFFFFFF;       // every in-range offset is below 2^31
+constexpr int kRsrcWord3 = 0x00020000;        // raw buffer, 32-bit data format (CDNA)
+constexpr int kXcds = 8;                      // MI355X dispatches workgroups round-robin over 8 XCDs
+constexpr int kGroupM = 4;                    // tile rows that share W tiles inside one XCD
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, kNumRecords, kRsrcWord3);
+}
+
+// Placement only: undo the round-robin XCD dispatch so that consecutive tiles
+// land on one XCD (its L2 then serves the shared X and W tiles), and walk the
+// tiles in groups of kGroupM tile-rows so that the XCD's concurrent tiles form
+// a compact block.
+__device__ __forceinline__ void tile_of(int bid, int nblocks, int tiles_m, int tiles_n, int& tm, int& tn) {
+  int t = bid;
+  const int per = nblocks / kXcds;
+  if (bid < per * kXcds) t = (bid % kXcds) * per + bid / kXcds;
+  const int group = t / (kGroupM * tiles_n);
+  const int first_m = group * kGroupM;
+  const int gm = min(tiles_m - first_m, kGroupM);
+  const int in = t - group * kGroupM * tiles_n;
+  tm = first_m + in % gm;
+  tn = in / gm;
+}
+
+// 16-byte-chunk swizzle of a 128-byte-row operand tile (X tiles, and the MXFP8
+// W tile): chunk c of row r is stored in slot c ^ swz128(r).
+__device__ __forceinline__ int swz_x(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+// bf16 W tile rows are 256 bytes (16 chunks).
+__device__ __forceinline__ int swz_w16(int k) { return 4 * (k & 3); }
+// MXFP8 W tile rows are 128 bytes (8 chunks).
+__device__ __forceinline__ int swz_w8(int k) { return k & 7; }
+
+// The pipeline waits are written out explicitly: each thread first waits for
+// its own LDS-DMA loads of the stage it is about to read (vmcnt counts them in
+// issue order), then the workgroup barrier makes every thread's loads visible.
+// A plain __syncthreads() would carry a release fence that waits for every
+// outstanding load, including the prefetches that should stay in flight.
+// s_waitcnt immediate (gfx9): vmcnt in bits [3:0] and [15:14], expcnt [6:4],
+// lgkmcnt [11:8]; only vmcnt is constrained here. The builtin (rather than
+// inline asm) lets the compiler's own wait insertion see that the wait happened.
+#define BIGEMM_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
+#define BIGEMM_BARRIER() asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory")
+
+// ------------------------------------------------------------------------ bf16
+//
+// K block 64, MFMA 32x32x16 bf16, fp32 accumulate. Per stage: X tile 128 x 64
+// bf16 (rows of 128 B), W tile 64 x 128 bf16 (rows of 256 B).
+constexpr int kBkBf16 = 64;
+
+__global__ __launch_bounds__(kThreads, 1)
+void bigemm_bf16_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
+                        float* __restrict__ Y, int M, int N, int K,
+                        int64_t ldx, int64_t ldw, int64_t ldy, int tiles_m, int tiles_n) {
+  // One LDS array per pipeline stage: distinct objects let the compiler see
+  // that reads of one stage do not depend on the loads in flight into another.
+  __shared__ __attribute__((aligned(1024))) uint8_t stage0[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t stage1[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t stage2[kStageBytes];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  int tm, tn;
+  tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+  const int row0 = tm * 128;
+  const int col0 = tn * 128;
+  const int rows_valid = min(128, M - row0);
+  const int cols_valid = min(128, N - col0);
+  const int nkb = (K + kBkBf16 - 1) / kBkBf16;
+
+  // Load assignment: chunk p = i*256 + tid of each tile (i = 0..3). With
+  // buffer_load ... lds a wave's 64 lanes fill 1 KiB of LDS contiguously, so
+  // the LDS slot is fixed by p and the swizzle is applied to the global side.
+  // xk/wk: the K offset of the chunk inside the block, or a huge value when
+  // the chunk's row (column) is outside the matrix, so that one compare with
+  // the K remaining in the block decides in-range.
+  uint32_t xoff[4], woff[4];
+  int xk[4], wk[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int p = i * kThreads + tid;
+    const int r = p >> 3, s = p & 7, c = s ^ swz_x(r);
+    xoff[i] = (uint32_t)((r * ldx + c * 8) * 2);
+    xk[i] = r < rows_valid ? c * 8 : 0x7FFFFFFF;
+    const int kr = p >> 4, sw = p & 15, cw = sw ^ swz_w16(kr);
+    woff[i] = (uint32_t)((kr * ldw + cw * 8) * 2);
+    wk[i] = cw * 8 < cols_valid ? kr : 0x7FFFFFFF;
+  }
+  const uint16_t* Xt = X + (int64_t)row0 * ldx;
+  const uint16_t* Wt = W + col0;
+
+  // Issue the 8 LDS-DMA loads of K block kb into `stage`. A block past the
+  // end (kb >= nkb) is still issued, entirely out of range: it loads zeros
+  // into a stage nobody reads again, and keeps every pipeline step the same
+  // instruction sequence (so the number of loads in flight is fixed).
+  auto issue = [&](int kb, uint8_t* stage) {
+    const bool live = kb < nkb;
+    const int k0 = live ? kb * kBkBf16 : 0;
+    const int kleft = live ? K - k0 : 0;
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(Xt + k0);
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(Wt + (int64_t)k0 * ldw);
+    uint8_t* sx = stage;
+    uint8_t* sw = stage + kTileBytes;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t o = xk[i] < kleft ? xoff[i] : kOob;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, LDS(void, sx + i * 4096 + wave * 1024), 16, o, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t o = wk[i] < kleft ? woff[i] : kOob;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, LDS(void, sw + i * 4096 + wave * 1024), 16, o, 0, 0, 0);
+    }
+  };
+
+  // Fragment addresses (bytes inside a stage's tiles).
+  const int wm = wave >> 1, wn = wave & 1;
+  int a_addr[2][4];   // [fm][kk]
+  int b_addr[2][4][2];  // [fn][kk][half]
+#pragma unroll
+  for (int f = 0; f < 2; ++f) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int r = wm * 64 + f * 32 + (lane & 31);
+      const int c = kk * 2 + (lane >> 5);
+      a_addr[f][kk] = r * 128 + ((c ^ swz_x(r)) << 4);
+      const int g = lane >> 4, j = lane & 15;
+      const int col = wn * 64 + f * 32 + (g & 1) * 16 + (j & 3) * 4;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int kr = kk * 16 + (g >> 1) * 8 + h * 4 + (j >> 2);
+        b_addr[f][kk][h] = kTileBytes + kr * 256 + (((col >> 3) ^ swz_w16(kr)) << 4) + (col & 7) * 2;
+      }
+    }
+  }
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+
+  // One K block: wait for this stage, refill the stage read two blocks ago,
+  // then run the MFMA chain on this stage.
+  auto step = [&](int kb, const uint8_t* st, uint8_t* refill) {
+    BIGEMM_WAIT_VMCNT(8);  // only block kb+1's 8 loads may still be in flight
+    BIGEMM_BARRIER();
+    issue(kb + 2, refill);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      bf16x8 a[2], b[2];
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        a[f] = *LDS(const bf16x8, st + a_addr[f][kk]);
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS(i16x4, st + b_addr[f][kk][0]));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS(i16x4, st + b_addr[f][kk][1]));
+        const i32x2 lo2 = __builtin_bit_cast(i32x2, lo), hi2 = __builtin_bit_cast(i32x2, hi);
+        const i32x4 v = {lo2[0], lo2[1], hi2[0], hi2[1]};
+        b[f] = __builtin_bit_cast(bf16x8, v);
+      }
+#pragma unroll
+      for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < 2; ++fn)
+          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[fm], b[fn], acc[fm][fn], 0, 0, 0);
+    }
+  };
+
+  // Prologue: a dummy (entirely out-of-range) fill of stage 2, then blocks 0
+  // and 1. The dummy makes the loads in flight at the loop head target the
+  // stages in the same order on entry as on every later iteration.
+  issue(nkb, stage2);
+  issue(0, stage0);
+  issue(1, stage1);
+  // Unrolled by 6 so that each stage is a fixed LDS object in every step.
+  // (The compiler cannot track which stage the loads in flight target across
+  // the loop back-edge and drains them before the first step of an iteration;
+  // a longer body makes that the exception.)
+  for (int kb = 0;;) {
+    step(kb, stage0, stage2);
+    if (++kb == nkb) break;
+    step(kb, stage1, stage0);
+    if (++kb == nkb) break;
+    step(kb, stage2, stage1);
+    if (++kb == nkb) break;
+    step(kb, stage0, stage2);
+    if (++kb == nkb) break;
+    step(kb, stage1, stage0);
+    if (++kb == nkb) break;
+    step(kb, stage2, stage1);
+    if (++kb == nkb) break;
+  }
+  BIGEMM_WAIT_VMCNT(0);  // no LDS-DMA load may outlive the workgroup
+
+  // Epilogue: plain fp32 stores, masked through the buffer range check.
+  const __amdgpu_buffer_rsrc_t ry = make_rsrc(Y + (int64_t)row0 * ldy + col0);
+#pragma unroll
+  for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < 2; ++fn)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int rl = wm * 64 + fm * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        const int cl = wn * 64 + fn * 32 + (lane & 31);
+        const uint32_t o = (rl < rows_valid && cl < cols_valid) ? (uint32_t)((rl * ldy + cl) * 4) : kOob;
+        // Copy the element out first: bit-casting an ext_vector element
+        // expression directly reads element 0 with this compiler.
+        const float v = acc[fm][fn][r];
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), ry, o, 0, 0);
+      }
+}
+
+// ----------------------------------------------------------------------- MXFP8
+//
+// K block 128 (four 32-wide scale blocks), MFMA 32x32x64 E4M3 with E8M0 scales
+// applied inside the instruction, fp32 accumulate. Per stage: X tile 128 x 128
+// bytes, W tile 128 x 128 bytes (both rows of 128 B).
+constexpr int kBkMx = 128;
+
+__global__ __launch_bounds__(kThreads, 1)
+void bigemm_mxfp8_kernel(const uint8_t* __restrict__ X, const uint8_t* __restrict__ W,
+                         float* __restrict__ Y, const uint8_t* __restrict__ XS,
+                         const uint8_t* __restrict__ WS, int M, int N, int K,
+                         int64_t ldx, int64_t ldw, int64_t ldy, int64_t ldxs, int64_t ldws,
+                         int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(1024))) uint8_t stage0[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t stage1[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t stage2[kStageBytes];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  int tm, tn;
+  tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+  const int row0 = tm * 128;
+  const int col0 = tn * 128;
+  const int rows_valid = min(128, M - row0);
+  const int cols_valid = min(128, N - col0);
+  const int nkb = (K + kBkMx - 1) / kBkMx;
+  const int nsb = K / 32;  // scale blocks along K
+
+  uint32_t xoff[4], woff[4];
+  int xk[4], wk[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int p = i * kThreads + tid;
+    const int r = p >> 3, s = p & 7, c = s ^ swz_x(r);
+    xoff[i] = (uint32_t)(r * ldx + c * 16);
+    xk[i] = r < rows_valid ? c * 16 : 0x7FFFFFFF;
+    const int kr = p >> 3, cw = s ^ swz_w8(kr);
+    woff[i] = (uint32_t)(kr * ldw + cw * 16);
+    wk[i] = cw * 16 < cols_valid ? kr : 0x7FFFFFFF;
+  }
+  const uint8_t* Xt = X + (int64_t)row0 * ldx;
+  const uint8_t* Wt = W + col0;
+
+  auto issue = [&](int kb, uint8_t* stage) {
+    const bool live = kb < nkb;
+    const int k0 = live ? kb * kBkMx : 0;
+    const int kleft = live ? K - k0 : 0;
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(Xt + k0);
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(Wt + (int64_t)k0 * ldw);
+    uint8_t* sx = stage;
+    uint8_t* sw = stage + kTileBytes;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t o = xk[i] < kleft ? xoff[i] : kOob;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, LDS(void, sx + i * 4096 + wave * 1024), 16, o, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t o = wk[i] < kleft ? woff[i] : kOob;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, LDS(void, sw + i * 4096 + wave * 1024), 16, o, 0, 0, 0);
+    }
+  };
+
+  const int wm = wave >> 1, wn = wave & 1;
+  const int g = lane >> 5;   // which 16-wide K quarter of a 64-wide MFMA step this lane holds
+  // A fragment: two 16-byte reads per (fm, kk): k = kk*64 + g*16 and kk*64 + 32 + g*16
+  int a_addr[2][2][2];   // [fm][kk][half]
+  // B fragment: four 8-byte transposing reads per (fn, kk)
+  int b_addr[2][2][4];   // [fn][kk][read]
+#pragma unroll
+  for (int f = 0; f < 2; ++f) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int r = wm * 64 + f * 32 + (lane & 31);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int c = kk * 4 + h * 2 + g;
+        a_addr[f][kk][h] = r * 128 + ((c ^ swz_x(r)) << 4);
+      }
+      const int G = lane >> 4, j = lane & 15;
+      const int col = wn * 64 + f * 32 + (G & 1) * 16 + (j & 1) * 8;
+#pragma unroll
+      for (int rd = 0; rd < 4; ++rd) {
+        const int kr = kk * 64 + (rd >> 1) * 32 + (G >> 1) * 16 + (rd & 1) * 8 + (j >> 1);
+        b_addr[f][kk][rd] = kTileBytes + kr * 128 + (((col >> 4) ^ swz_w8(kr)) << 4) + (col & 15);
+      }
+    }
+  }
+
+  // Scale sources: lane holds the scale of its row (column) for K block
+  // kb*4 + kk*2 + g. Out-of-range rows, columns or K blocks read as 0 (2^-127,
+  // multiplying zero data).
+  const __amdgpu_buffer_rsrc_t rxs = make_rsrc(XS + (int64_t)row0 * ldxs);
+  const __amdgpu_buffer_rsrc_t rws = make_rsrc(WS + col0);
+  // xs_base/ws_base: the lane's offset for K block 0; xs_lim/ws_lim: the
+  // number of K blocks it may read (0 for rows/columns outside the matrix).
+  uint32_t xs_base[2], ws_base[2];
+  int xs_lim[2], ws_lim[2];
+#pragma unroll
+  for (int f = 0; f < 2; ++f) {
+    const int r = wm * 64 + f * 32 + (lane & 31);
+    xs_base[f] = (uint32_t)(r * ldxs);
+    xs_lim[f] = r < rows_valid ? nsb : 0;
+    const int c = wn * 64 + f * 32 + (lane & 31);
+    ws_base[f] = (uint32_t)c;
+    ws_lim[f] = c < cols_valid ? nsb : 0;
+  }
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+
+  // Scale registers of one K block: [fragment][MFMA step]. Blocks past K read
+  // as out of range (zero).
+  auto load_scales = [&](int kb, int (&sa)[2][2], int (&sb)[2][2]) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int blk = kb * 4 + kk * 2 + g;
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        const uint32_t oa = blk < xs_lim[f] ? xs_base[f] + (uint32_t)blk : kOob;
+        const uint32_t ob = blk < ws_lim[f] ? ws_base[f] + (uint32_t)(blk * ldws) : kOob;
+        sa[f][kk] = __builtin_amdgcn_raw_buffer_load_b8(rxs, oa, 0, 0);
+        sb[f][kk] = __builtin_amdgcn_raw_buffer_load_b8(rws, ob, 0, 0);
+      }
+    }
+  };
+
+  int sa_cur[2][2], sb_cur[2][2], sa_nxt[2][2], sb_nxt[2][2];
+
+  // One K block. Loads in flight after this stage's 8 LDS-DMA loads are at
+  // most: the previous block's 8 scale loads, the next stage's 8 DMA loads and
+  // the next block's... (issued later), so vmcnt <= 16 means this stage landed.
+  auto step = [&](int kb, const uint8_t* st, uint8_t* refill) {
+    BIGEMM_WAIT_VMCNT(16);
+    BIGEMM_BARRIER();
+    issue(kb + 2, refill);
+    load_scales(kb + 1, sa_nxt, sb_nxt);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      i32x8 a[2], b[2];
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        const i32x4 a0 = *LDS(const i32x4, st + a_addr[f][kk][0]);
+        const i32x4 a1 = *LDS(const i32x4, st + a_addr[f][kk][1]);
+        a[f] = i32x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+        i32x2 bv[4];
+#pragma unroll
+        for (int rd = 0; rd < 4; ++rd)
+          bv[rd] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(LDS(i32x2, st + b_addr[f][kk][rd]));
+        b[f] = i32x8{bv[0][0], bv[0][1], bv[1][0], bv[1][1], bv[2][0], bv[2][1], bv[3][0], bv[3][1]};
+      }
+#pragma unroll
+      for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < 2; ++fn)
+          acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              a[fm], b[fn], acc[fm][fn], 0 /*A: E4M3*/, 0 /*B: E4M3*/, 0, sa_cur[fm][kk], 0, sb_cur[fn][kk]);
+    }
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        sa_cur[f][kk] = sa_nxt[f][kk];
+        sb_cur[f][kk] = sb_nxt[f][kk];
+      }
+  };
+
+  issue(nkb, stage2);
+  issue(0, stage0);
+  load_scales(0, sa_cur, sb_cur);
+  issue(1, stage1);
+  // Unrolled by 6 so that each stage is a fixed LDS object in every step.
+  // (The compiler cannot track which stage the loads in flight target across
+  // the loop back-edge and drains them before the first step of an iteration;
+  // a longer body makes that the exception.)
+  for (int kb = 0;;) {
+    step(kb, stage0, stage2);
+    if (++kb == nkb) break;
+    step(kb, stage1, stage0);
+    if (++kb == nkb) break;
+    step(kb, stage2, stage1);
+    if (++kb == nkb) break;
+    step(kb, stage0, stage2);
+    if (++kb == nkb) break;
+    step(kb, stage1, stage0);
+    if (++kb == nkb) break;
+    step(kb, stage2, stage1);
+    if (++kb == nkb) break;
+  }
+  BIGEMM_WAIT_VMCNT(0);  // no LDS-DMA load may outlive the workgroup
+
+  const __amdgpu_buffer_rsrc_t ry = make_rsrc(Y + (int64_t)row0 * ldy + col0);
+#pragma unroll
+  for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < 2; ++fn)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int rl = wm * 64 + fm * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        const int cl = wn * 64 + fn * 32 + (lane & 31);
+        const uint32_t o = (rl < rows_valid && cl < cols_valid) ? (uint32_t)((rl * ldy + cl) * 4) : kOob;
+        // Copy the element out first: bit-casting an ext_vector element
+        // expression directly reads element 0 with this compiler.
+        const float v = acc[fm][fn][r];
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), ry, o, 0, 0);
+      }
+}
+
+// ------------------------------------------------------------------ launchers
+
+hipError_t launch_bf16(const void* X, const void* W, void* Y, int64_t M, int64_t N, int64_t K,
+                       int64_t ldx, int64_t ldw, int64_t ldy, hipStream_t stream) {
+  const int tiles_m = (int)((M + 127) / 128);
+  const int tiles_n = (int)((N + 127) / 128);
+  hipLaunchKernelGGL(bigemm_bf16_kernel, dim3(tiles_m * tiles_n), dim3(kThreads), 0, stream,
+                     (const uint16_t*)X, (const uint16_t*)W, (float*)Y, (int)M, (int)N, (int)K,
+                     ldx, ldw, ldy, tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
+hipError_t launch_mxfp8(const void* X, const void* W, void* Y, const void* XS, const void* WS,
+                        int64_t M, int64_t N, int64_t K, int64_t ldx, int64_t ldw, int64_t ldy,
+                        int64_t ldxs, int64_t ldws, hipStream_t stream) {
+  const int tiles_m = (int)((M + 127) / 128);
+  const int tiles_n = (int)((N + 127) / 128);
+  hipLaunchKernelGGL(bigemm_mxfp8_kernel, dim3(tiles_m * tiles_n), dim3(kThreads), 0, stream,
+                     (const uint8_t*)X, (const uint8_t*)W, (float*)Y, (const uint8_t*)XS,
+                     (const uint8_t*)WS, (int)M, (int)N, (int)K, ldx, ldw, ldy, ldxs, ldws,
+                     tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
+}  // namespace bigemm

@@ -1,0 +1,181 @@
+/*
+ * CPU oracle for the batch-invariant GEMM — TEST INFRASTRUCTURE ONLY.
+ *
+ * Only the tests, the smoke check and the bench's CPU-baseline leg may load
+ * this library. It shares no code, header or table with the GPU path; it
+ * includes no HIP header and is built with plain gcc.
+ *
+ * What it computes is the plain definition of the matrix product that the
+ * nondeterminism blog states in its section on batch-invariant matrix
+ * multiplication: C_ij = sum_k A_ik B_kj, with the whole K reduction of one
+ * output element done by one worker. Here the reduction is carried out in
+ * IEEE binary64 with k ascending, after decoding every operand exactly:
+ *
+ *   - bf16: the 16 bits are the top half of an IEEE binary32 (exact widening);
+ *   - OCP E4M3FN (the element format of MXFP8, the CANN issue's quantised
+ *     path): 1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits, no
+ *     infinities, S.1111.111 is NaN, exponent field 0 is subnormal m/8*2^-6;
+ *   - E8M0 (the MXFP8 block scale, one per 32 consecutive K elements): the
+ *     byte e encodes 2^(e-127), 0xFF is NaN.
+ *
+ * Every product is exact in binary64 (bf16*bf16 has at most 16 significant
+ * bits; a scaled E4M3*E4M3 product has at most 8). The only rounding is the
+ * binary64 accumulation, bounded by the blog's sequential-sum bound
+ * (section "unit roundoff"): |s_hat - s| <= gamma_{K-1} * sum_k |x_ik w_kj|,
+ * gamma_n = n u / (1 - n u), u = 2^-53.
+ *
+ * The oracle also returns S_ij = sum_k |x_ik w_kj| (exact products, fp64 sum),
+ * the scale against which GPU results are judged.
+ *
+ * Layouts (row-major, leading dimensions in elements):
+ *   X[M,K] (ldx), W[K,N] (ldw), Y[M,N] and S[M,N] (ldy) in double,
+ *   MX scales: XS[M, K/32] (ldxs), WS[K/32, N] (ldws), one byte each.
+ *
+ * Threads: OpenMP over output rows; each row's arithmetic is the same
+ * sequence whatever the thread count.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stddef.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ---------------------------------------------------------------- decoders */
+
+double oracle_decode_bf16(uint16_t bits) {
+  uint32_t u = (uint32_t)bits << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+/* E4M3FN from its definition (exponent bias 7, 3 mantissa bits). */
+double oracle_decode_e4m3(uint8_t code) {
+  int s = code >> 7;
+  int e = (code >> 3) & 15;
+  int m = code & 7;
+  double v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0)
+    v = ldexp((double)m, -9);           /* m/8 * 2^(1-7) */
+  else
+    v = ldexp((double)(8 + m), e - 10); /* (1 + m/8) * 2^(e-7) */
+  return s ? -v : v;
+}
+
+double oracle_decode_e8m0(uint8_t code) {
+  if (code == 0xFF) return NAN;
+  return ldexp(1.0, (int)code - 127);
+}
+
+static double e4m3_table[256];
+static int e4m3_table_ready = 0;
+
+static void build_e4m3_table(void) {
+  if (e4m3_table_ready) return;
+  for (int c = 0; c < 256; ++c) e4m3_table[c] = oracle_decode_e4m3((uint8_t)c);
+  e4m3_table_ready = 1;
+}
+
+/* ---------------------------------------------------------- shared driver */
+
+/*
+ * Plain fp64 GEMM over already-decoded operands: for each row i, for k
+ * ascending, for each column j: acc[j] += a_ik * b_kj. Y and (optionally) S
+ * receive acc and the absolute-value sums. Exposed so the accumulation core
+ * can be pinned on fp64 inputs (the blog's unrounded linspace example).
+ */
+int oracle_gemm_f64(int64_t M, int64_t N, int64_t K,
+                    const double* A, int64_t lda,
+                    const double* B, int64_t ldb,
+                    double* Y, int64_t ldy, double* S, int64_t lds) {
+  if (M < 0 || N < 0 || K < 0) return 1;
+  if (M == 0 || N == 0) return 0;
+  if (!A || !B || !Y) return 1;
+  int64_t i;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (i = 0; i < M; ++i) {
+    double* acc = Y + i * ldy;
+    double* sabs = S ? S + i * lds : NULL;
+    for (int64_t j = 0; j < N; ++j) acc[j] = 0.0;
+    if (sabs)
+      for (int64_t j = 0; j < N; ++j) sabs[j] = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+      const double a = A[i * lda + k];
+      const double* brow = B + k * ldb;
+      for (int64_t j = 0; j < N; ++j) acc[j] += a * brow[j];
+      if (sabs)
+        for (int64_t j = 0; j < N; ++j) sabs[j] += fabs(a * brow[j]);
+    }
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------- bf16 */
+
+int oracle_gemm_bf16(int64_t M, int64_t N, int64_t K,
+                     const uint16_t* X, int64_t ldx,
+                     const uint16_t* W, int64_t ldw,
+                     double* Y, int64_t ldy, double* S, int64_t lds) {
+  if (M < 0 || N < 0 || K < 0 || ldx < K || ldw < N || ldy < N) return 1;
+  if (M == 0 || N == 0) return 0;
+  double* A = (double*)malloc(sizeof(double) * (size_t)(M * K + 1));
+  double* B = (double*)malloc(sizeof(double) * (size_t)(K * N + 1));
+  if (!A || !B) { free(A); free(B); return 2; }
+  for (int64_t i = 0; i < M; ++i)
+    for (int64_t k = 0; k < K; ++k) A[i * K + k] = oracle_decode_bf16(X[i * ldx + k]);
+  for (int64_t k = 0; k < K; ++k)
+    for (int64_t j = 0; j < N; ++j) B[k * N + j] = oracle_decode_bf16(W[k * ldw + j]);
+  int rc = oracle_gemm_f64(M, N, K, A, K, B, N, Y, ldy, S, lds);
+  free(A);
+  free(B);
+  return rc;
+}
+
+/* ------------------------------------------------------------------ MXFP8 */
+
+/*
+ * x~_ik = e4m3(X_ik) * 2^(XS[i, k/32] - 127),  w~_kj = e4m3(W_kj) * 2^(WS[k/32, j] - 127),
+ * then the fp64 product of the scaled operands. Scaling by a power of two is
+ * exact, so this equals applying the two block scales to each block's
+ * partial sum.
+ */
+int oracle_gemm_mxfp8(int64_t M, int64_t N, int64_t K,
+                      const uint8_t* X, int64_t ldx,
+                      const uint8_t* W, int64_t ldw,
+                      const uint8_t* XS, int64_t ldxs,
+                      const uint8_t* WS, int64_t ldws,
+                      double* Y, int64_t ldy, double* S, int64_t lds) {
+  if (M < 0 || N < 0 || K < 0 || (K % 32) != 0 || ldx < K || ldw < N || ldy < N) return 1;
+  if (ldxs < K / 32 || ldws < N) return 1;
+  if (M == 0 || N == 0) return 0;
+  build_e4m3_table();
+  double* A = (double*)malloc(sizeof(double) * (size_t)(M * K + 1));
+  double* B = (double*)malloc(sizeof(double) * (size_t)(K * N + 1));
+  if (!A || !B) { free(A); free(B); return 2; }
+  for (int64_t i = 0; i < M; ++i)
+    for (int64_t k = 0; k < K; ++k)
+      A[i * K + k] = e4m3_table[X[i * ldx + k]] * oracle_decode_e8m0(XS[i * ldxs + k / 32]);
+  for (int64_t k = 0; k < K; ++k)
+    for (int64_t j = 0; j < N; ++j)
+      B[k * N + j] = e4m3_table[W[k * ldw + j]] * oracle_decode_e8m0(WS[(k / 32) * ldws + j]);
+  int rc = oracle_gemm_f64(M, N, K, A, K, B, N, Y, ldy, S, lds);
+  free(A);
+  free(B);
+  return rc;
+}
+
+/* ------------------------------------------------------------------ misc */
+
+int oracle_set_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+  return omp_get_max_threads();
+#else
+  (void)n;
+  return 1;
+#endif
+}
