@@ -1,0 +1,162 @@
+"""Bench: batch-invariant bf16 GEMM throughput on one MI355X.
+
+Headline (``value``): TFLOP/s of Y[4096,4096] = X[4096,4096] . W[4096,4096]
+(bf16 in, fp32 accumulate, fp32 out; X ~ N(0,1), W ~ N(0,0.02), the
+projection workload at K = N = 4096), one step = one GEMM call through the C
+ABI with inputs resident in HBM. Also reported:
+
+* ``m_sweep``: TFLOP/s and % of the bf16 MFMA peak for M = 1 ... 4096 at
+  K = N = 4096 (small M rotates among buffer sets larger than the 256 MB
+  last-level cache, so W is read from HBM), with achieved algorithmic HBM GB/s;
+* ``invariance_byte_diffs``: every row of every sweep result compared with the
+  same row of the M = 4096 result (must be 0);
+* ``roofline``: the kernel's algorithmic flops per launch over its average
+  launch time (HIP events on the launch stream) against the datasheet peak;
+* ``cpu_baseline``: the CPU oracle timed on a bounded sample of rows of the
+  same workload (rank 0, one GPU only).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+M_SWEEP = [1, 16, 64, 128, 256, 512, 1024, 2048, 4096]
+K = N = 4096
+
+
+def _events(torch, stream, fn, reps):
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record(stream)
+    for i in range(reps):
+        fn(i)
+    e.record(stream)
+    e.synchronize()
+    return s.elapsed_time(e) / reps  # ms per call
+
+
+def cpu_baseline(X, W, target_s: float = 15.0):
+    """The oracle (fp64, OpenMP) timed on a bounded sample of rows of the workload."""
+    import oracle
+    threads = oracle.set_threads(0)
+    probe_rows = 32
+    t0 = time.perf_counter()
+    oracle.gemm_bf16(X[:probe_rows], W, want_s=False)
+    dt = time.perf_counter() - t0
+    rows = int(min(X.shape[0], max(probe_rows, probe_rows * target_s / max(dt, 1e-6))))
+    t0 = time.perf_counter()
+    oracle.gemm_bf16(X[:rows], W, want_s=False)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows * W.shape[0] * W.shape[1]
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{rows} of {X.shape[0]} rows of the M=4096 K=N=4096 bf16 workload "
+                      f"({flops / 1e9:.1f} GFLOP in {dt:.1f} s, fp64 accumulate)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the GEMM shards by rows "
+              f"or columns with no exchange, which this build does not launch.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import invariant_gemm_deterministic_amd as bg
+    from bigemm_inputs import SEED_W, SEED_X, normal_bf16
+
+    assert torch.cuda.is_available(), "bench needs a GPU"
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream(dev)
+    Xh = normal_bf16(SEED_X, (4096, K))
+    Wh = normal_bf16(SEED_W, (K, N), 0.02)
+    X = torch.from_numpy(Xh.view(np.int16)).to(dev)
+    W = torch.from_numpy(Wh.view(np.int16)).to(dev)
+    Y = torch.empty((4096, N), dtype=torch.float32, device=dev)
+
+    # ---------------------------------------------------------------- headline
+    M = 4096
+    for _ in range(args.warmup):
+        bg.mm(X, W, out=Y)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ms = _events(torch, stream, lambda i: bg.mm(X, W, out=Y), args.steps)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    flops = 2.0 * M * N * K
+    tflops = flops / (ms * 1e-3) / 1e12
+    Yfull = Y.clone()
+
+    # ------------------------------------------------------------------ sweep
+    sweep = []
+    diffs = 0
+    if not args.no_sweep:
+        for m in M_SWEEP:
+            # enough buffer sets to exceed the 256 MB last-level cache for small M
+            set_bytes = 2 * m * K + 2 * K * N + 4 * m * N
+            nsets = 1 if m >= 1024 else max(2, int(np.ceil(600e6 / set_bytes)))
+            Ws = [W] + [W.clone() for _ in range(nsets - 1)]
+            Xs = [X[:m]] + [X[:m].clone() for _ in range(nsets - 1)]
+            Ys = [torch.empty((m, N), dtype=torch.float32, device=dev) for _ in range(nsets)]
+            for i in range(2 * nsets):
+                bg.mm(Xs[i % nsets], Ws[i % nsets], out=Ys[i % nsets])
+            reps = max(20, 2 * nsets)
+            t = _events(torch, stream, lambda i: bg.mm(Xs[i % nsets], Ws[i % nsets], out=Ys[i % nsets]), reps)
+            torch.cuda.synchronize()
+            for y in Ys:
+                diffs += int((y.view(torch.int32) != Yfull[:m].view(torch.int32)).sum().item())
+            f = 2.0 * m * N * K
+            byts = 2 * m * K + 2 * K * N + 4 * m * N
+            sweep.append({"M": m, "us": round(t * 1e3, 2), "tflops": round(f / (t * 1e-3) / 1e12, 1),
+                          "pct_peak": round(100 * f / (t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 1),
+                          "hbm_gbs_algorithmic": round(byts / (t * 1e-3) / 1e9, 0),
+                          "cold_llc": nsets > 1})
+            del Ws, Xs, Ys
+            torch.cuda.empty_cache()
+
+    line = {
+        "metric": "TFLOP/s vs M (1-4096) at K=N=4096, % MFMA peak; invariance byte-diffs=0",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "bf16 projection GEMM Y[4096,4096] = X[4096,4096] . W[4096,4096], "
+                               "X~N(0,1), W~N(0,0.02), fp32 accumulate and output, batch-invariant fixed tile",
+                   "M": M, "N": N, "K": K, "tile": list(bg.bigemm_get_config(bg._handle("bf16", 0)))},
+        "pct_mfma_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
+        "m_sweep": sweep,
+        "invariance_byte_diffs": diffs if sweep else None,
+        "timed_wall_s": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(Xh, Wh)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -150,8 +150,8 @@ def e8m0_kvar_scales(seed: int, n_kblocks: int, n_other: int, k_axis: int, lo: i
     rng = np.random.default_rng(seed)
     v = (127 + rng.integers(lo, hi + 1, size=n_kblocks)).astype(np.uint8)
     if k_axis == 1:   # X scales [rows, K/32]
-        return np.ascontiguousarray(np.broadcast_to(v[None, :], (n_other, n_kblocks)))
-    return np.ascontiguousarray(np.broadcast_to(v[:, None], (n_kblocks, n_other)))
+        return np.tile(v[None, :], (n_other, 1))
+    return np.tile(v[:, None], (1, n_other))
 
 
 # --------------------------------------------------------------------------- cells

@@ -166,6 +166,11 @@ def _handle(kind: str, device_index: int) -> int:
     return h
 
 
+def _ld(t) -> int:
+    """Leading dimension in elements (a single row's stride is arbitrary in torch; use its width)."""
+    return int(t.stride(0)) if t.shape[0] > 1 else int(t.shape[1])
+
+
 def mm(x, w, x_scale=None, w_scale=None, out=None, stream=None):
     """Y = X W on the GPU through libbigemm.
 
@@ -203,10 +208,12 @@ def mm(x, w, x_scale=None, w_scale=None, out=None, stream=None):
         stream = torch.cuda.current_stream(x.device).cuda_stream
     h = _handle("mx" if mx else "bf16", dev)
     if mx:
-        bigemm_run(h, M, N, K, x.data_ptr(), x.stride(0), w.data_ptr(), w.stride(0), out.data_ptr(),
-                   out.stride(0), x_scale.data_ptr(), x_scale.stride(0), w_scale.data_ptr(),
-                   w_scale.stride(0), stream)
+        for t in (x_scale, w_scale):
+            if not t.is_cuda or t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+                raise ValueError("scales must be 2-D CUDA tensors with contiguous rows")
+        bigemm_run(h, M, N, K, x.data_ptr(), _ld(x), w.data_ptr(), _ld(w), out.data_ptr(), _ld(out),
+                   x_scale.data_ptr(), _ld(x_scale), w_scale.data_ptr(), _ld(w_scale), stream)
     else:
-        bigemm_run(h, M, N, K, x.data_ptr(), x.stride(0), w.data_ptr(), w.stride(0), out.data_ptr(),
-                   out.stride(0), 0, 0, 0, 0, stream)
+        bigemm_run(h, M, N, K, x.data_ptr(), _ld(x), w.data_ptr(), _ld(w), out.data_ptr(), _ld(out),
+                   0, 0, 0, 0, stream)
     return out

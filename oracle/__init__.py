@@ -6,16 +6,16 @@ code with the HIP path: the arithmetic lives in ``oracle.c`` (plain C built
 with gcc, loaded here through ctypes) and in ``exact.py`` (pure-Python exact
 sums for tiny shapes).
 
-What it computes (the blog's batch-invariant matrix multiplication section,
-C_ij = sum_k A_ik B_kj) and how closely the GPU must agree:
+What it computes (the nondeterminism blog, section on batch-invariant matrix
+multiplication: C_ij = sum_k A_ik B_kj) and how closely the GPU must agree:
 
 * ``gemm_bf16`` / ``gemm_mxfp8`` return the fp64-accumulated product of the
-  exactly decoded operands and S_ij = sum_k |x_ik w_kj|.
+  exactly decoded operands, summed with k ascending, and
+  S_ij = sum_k |x_ik w_kj|.
 * ``max_normalized_error`` is the parity metric: max_ij |y_gpu - y| / S_ij
   (elements with S_ij = 0 must be exactly 0). Any fp32 accumulation of the
   exact products, in any order, satisfies e <= gamma_{K-1}(fp32) by the blog's
-  sequential-sum bound (section "unit roundoff"); the gate used by the tests
-  is 2e-3.
+  sequential-sum bound (section on unit roundoff); the gate is 2e-3.
 """
 from __future__ import annotations
 
@@ -27,10 +27,8 @@ import threading
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRC = os.path.join(_HERE, "oracle.c")
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
-_lib = None
-_lock = threading.Lock()
+SOURCE = os.path.join(_HERE, "oracle.c")
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
 PARITY_TOL = 2e-3  # max normalised error allowed for bf16/MXFP8 inputs with fp32 accumulation
 
@@ -38,119 +36,153 @@ _i64 = ctypes.c_int64
 _p = ctypes.c_void_p
 
 
-def build(force: bool = True) -> str:
-    """Compile oracle.c into liboracle.so with gcc (no fast-math)."""
-    if force or not os.path.exists(_LIB_PATH):
-        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+def build(force: bool = True, src: str = SOURCE, out: str = LIB_PATH) -> str:
+    """Compile an oracle C source into a shared library with gcc (no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(out):
+        tmp = out + ".tmp%d" % os.getpid()
         cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-Wall", "-Wextra",
-               "-fno-fast-math", "-ffp-contract=off", _SRC, "-o", tmp, "-lm"]
+               "-fno-fast-math", "-ffp-contract=off", src, "-o", tmp, "-lm"]
         subprocess.run(cmd, check=True)
-        os.replace(tmp, _LIB_PATH)
-    return _LIB_PATH
-
-
-def _load():
-    global _lib
-    with _lock:
-        if _lib is None:
-            if not os.path.exists(_LIB_PATH):
-                build(force=False)
-            lib = ctypes.CDLL(_LIB_PATH)
-            lib.oracle_decode_bf16.restype = ctypes.c_double
-            lib.oracle_decode_bf16.argtypes = [ctypes.c_uint16]
-            lib.oracle_decode_e4m3.restype = ctypes.c_double
-            lib.oracle_decode_e4m3.argtypes = [ctypes.c_uint8]
-            lib.oracle_decode_e8m0.restype = ctypes.c_double
-            lib.oracle_decode_e8m0.argtypes = [ctypes.c_uint8]
-            lib.oracle_gemm_f64.restype = ctypes.c_int
-            lib.oracle_gemm_f64.argtypes = [_i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i64]
-            lib.oracle_gemm_bf16.restype = ctypes.c_int
-            lib.oracle_gemm_bf16.argtypes = [_i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i64]
-            lib.oracle_gemm_mxfp8.restype = ctypes.c_int
-            lib.oracle_gemm_mxfp8.argtypes = [_i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i64,
-                                              _p, _i64, _p, _i64]
-            lib.oracle_set_threads.restype = ctypes.c_int
-            lib.oracle_set_threads.argtypes = [ctypes.c_int]
-            _lib = lib
-    return _lib
+        os.replace(tmp, out)
+    return out
 
 
 def _ptr(a: np.ndarray):
     return a.ctypes.data_as(ctypes.c_void_p)
 
 
+class Oracle:
+    """One loaded copy of the oracle library."""
+
+    def __init__(self, path: str):
+        lib = ctypes.CDLL(path)
+        lib.oracle_decode_bf16.restype = ctypes.c_double
+        lib.oracle_decode_bf16.argtypes = [ctypes.c_uint16]
+        lib.oracle_decode_e4m3.restype = ctypes.c_double
+        lib.oracle_decode_e4m3.argtypes = [ctypes.c_uint8]
+        lib.oracle_decode_e8m0.restype = ctypes.c_double
+        lib.oracle_decode_e8m0.argtypes = [ctypes.c_uint8]
+        lib.oracle_gemm_f64.restype = ctypes.c_int
+        lib.oracle_gemm_f64.argtypes = [_i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i64]
+        lib.oracle_gemm_bf16.restype = ctypes.c_int
+        lib.oracle_gemm_bf16.argtypes = [_i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i64]
+        lib.oracle_gemm_mxfp8.restype = ctypes.c_int
+        lib.oracle_gemm_mxfp8.argtypes = [_i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i64,
+                                          _p, _i64, _p, _i64]
+        lib.oracle_set_threads.restype = ctypes.c_int
+        lib.oracle_set_threads.argtypes = [ctypes.c_int]
+        self.lib = lib
+        self.path = path
+
+    def set_threads(self, n: int) -> int:
+        """Set the OpenMP thread count (n <= 0 keeps it); returns the count in effect."""
+        return self.lib.oracle_set_threads(int(n))
+
+    def decode_bf16(self, bits) -> np.ndarray:
+        b = np.asarray(bits, dtype=np.uint16)
+        f = self.lib.oracle_decode_bf16
+        return np.array([f(int(v)) for v in b.ravel()], dtype=np.float64).reshape(b.shape)
+
+    def decode_e4m3(self, codes) -> np.ndarray:
+        c = np.asarray(codes, dtype=np.uint8)
+        f = self.lib.oracle_decode_e4m3
+        return np.array([f(int(v)) for v in c.ravel()], dtype=np.float64).reshape(c.shape)
+
+    def decode_e8m0(self, codes) -> np.ndarray:
+        c = np.asarray(codes, dtype=np.uint8)
+        f = self.lib.oracle_decode_e8m0
+        return np.array([f(int(v)) for v in c.ravel()], dtype=np.float64).reshape(c.shape)
+
+    def gemm_f64(self, A, B, want_s: bool = True):
+        """fp64 product of fp64 operands (the oracle's accumulation core)."""
+        A = np.ascontiguousarray(A, dtype=np.float64)
+        B = np.ascontiguousarray(B, dtype=np.float64)
+        M, K = A.shape
+        K2, N = B.shape
+        assert K == K2, (A.shape, B.shape)
+        Y = np.empty((M, N), dtype=np.float64)
+        S = np.empty((M, N), dtype=np.float64) if want_s else None
+        rc = self.lib.oracle_gemm_f64(M, N, K, _ptr(A), K, _ptr(B), N, _ptr(Y), N,
+                                      _ptr(S) if want_s else None, N)
+        if rc != 0:
+            raise RuntimeError(f"oracle_gemm_f64 failed rc={rc}")
+        return (Y, S) if want_s else Y
+
+    def gemm_bf16(self, X, W, want_s: bool = True):
+        """bf16 X[M,K] (uint16 bits) times bf16 W[K,N]; returns (Y, S) in fp64."""
+        X = np.ascontiguousarray(X, dtype=np.uint16)
+        W = np.ascontiguousarray(W, dtype=np.uint16)
+        M, K = X.shape
+        K2, N = W.shape
+        assert K == K2, (X.shape, W.shape)
+        Y = np.empty((M, N), dtype=np.float64)
+        S = np.empty((M, N), dtype=np.float64) if want_s else None
+        rc = self.lib.oracle_gemm_bf16(M, N, K, _ptr(X), K, _ptr(W), N, _ptr(Y), N,
+                                       _ptr(S) if want_s else None, N)
+        if rc != 0:
+            raise RuntimeError(f"oracle_gemm_bf16 failed rc={rc}")
+        return (Y, S) if want_s else Y
+
+    def gemm_mxfp8(self, X, W, XS, WS, want_s: bool = True):
+        """MXFP8: E4M3 codes X[M,K], W[K,N]; E8M0 scales XS[M,K/32], WS[K/32,N]."""
+        X = np.ascontiguousarray(X, dtype=np.uint8)
+        W = np.ascontiguousarray(W, dtype=np.uint8)
+        XS = np.ascontiguousarray(XS, dtype=np.uint8)
+        WS = np.ascontiguousarray(WS, dtype=np.uint8)
+        M, K = X.shape
+        K2, N = W.shape
+        assert K == K2 and K % 32 == 0, (X.shape, W.shape)
+        assert XS.shape == (M, K // 32) and WS.shape == (K // 32, N), (XS.shape, WS.shape)
+        Y = np.empty((M, N), dtype=np.float64)
+        S = np.empty((M, N), dtype=np.float64) if want_s else None
+        rc = self.lib.oracle_gemm_mxfp8(M, N, K, _ptr(X), K, _ptr(W), N, _ptr(XS), K // 32, _ptr(WS), N,
+                                        _ptr(Y), N, _ptr(S) if want_s else None, N)
+        if rc != 0:
+            raise RuntimeError(f"oracle_gemm_mxfp8 failed rc={rc}")
+        return (Y, S) if want_s else Y
+
+
+_default = None
+_lock = threading.Lock()
+
+
+def default() -> Oracle:
+    """The oracle built from oracle.c (compiled on first use if no library is there)."""
+    global _default
+    with _lock:
+        if _default is None:
+            if not os.path.exists(LIB_PATH):
+                build(force=False)
+            _default = Oracle(LIB_PATH)
+    return _default
+
+
 def set_threads(n: int) -> int:
-    """Set the OpenMP thread count (n <= 0 keeps it); returns the count in effect."""
-    return _load().oracle_set_threads(int(n))
+    return default().set_threads(n)
 
 
-def decode_bf16(bits) -> np.ndarray:
-    lib = _load()
-    b = np.asarray(bits, dtype=np.uint16)
-    return np.array([lib.oracle_decode_bf16(int(v)) for v in b.ravel()], dtype=np.float64).reshape(b.shape)
+def decode_bf16(bits):
+    return default().decode_bf16(bits)
 
 
-def decode_e4m3(codes) -> np.ndarray:
-    lib = _load()
-    c = np.asarray(codes, dtype=np.uint8)
-    return np.array([lib.oracle_decode_e4m3(int(v)) for v in c.ravel()], dtype=np.float64).reshape(c.shape)
+def decode_e4m3(codes):
+    return default().decode_e4m3(codes)
 
 
-def decode_e8m0(codes) -> np.ndarray:
-    lib = _load()
-    c = np.asarray(codes, dtype=np.uint8)
-    return np.array([lib.oracle_decode_e8m0(int(v)) for v in c.ravel()], dtype=np.float64).reshape(c.shape)
+def decode_e8m0(codes):
+    return default().decode_e8m0(codes)
 
 
 def gemm_f64(A, B, want_s: bool = True):
-    """fp64 product of fp64 operands (the oracle's accumulation core)."""
-    A = np.ascontiguousarray(A, dtype=np.float64)
-    B = np.ascontiguousarray(B, dtype=np.float64)
-    M, K = A.shape
-    K2, N = B.shape
-    assert K == K2
-    Y = np.empty((M, N), dtype=np.float64)
-    S = np.empty((M, N), dtype=np.float64) if want_s else None
-    rc = _load().oracle_gemm_f64(M, N, K, _ptr(A), K, _ptr(B), N, _ptr(Y), N,
-                                 _ptr(S) if want_s else None, N)
-    if rc != 0:
-        raise RuntimeError(f"oracle_gemm_f64 failed rc={rc}")
-    return (Y, S) if want_s else Y
+    return default().gemm_f64(A, B, want_s)
 
 
 def gemm_bf16(X, W, want_s: bool = True):
-    """Oracle for bf16 X[M,K] (uint16 bits) times bf16 W[K,N]; returns (Y, S) in fp64."""
-    X = np.ascontiguousarray(X, dtype=np.uint16)
-    W = np.ascontiguousarray(W, dtype=np.uint16)
-    M, K = X.shape
-    K2, N = W.shape
-    assert K == K2, (X.shape, W.shape)
-    Y = np.empty((M, N), dtype=np.float64)
-    S = np.empty((M, N), dtype=np.float64) if want_s else None
-    rc = _load().oracle_gemm_bf16(M, N, K, _ptr(X), K, _ptr(W), N, _ptr(Y), N,
-                                  _ptr(S) if want_s else None, N)
-    if rc != 0:
-        raise RuntimeError(f"oracle_gemm_bf16 failed rc={rc}")
-    return (Y, S) if want_s else Y
+    return default().gemm_bf16(X, W, want_s)
 
 
 def gemm_mxfp8(X, W, XS, WS, want_s: bool = True):
-    """Oracle for MXFP8: E4M3 codes X[M,K], W[K,N]; E8M0 scales XS[M,K/32], WS[K/32,N]."""
-    X = np.ascontiguousarray(X, dtype=np.uint8)
-    W = np.ascontiguousarray(W, dtype=np.uint8)
-    XS = np.ascontiguousarray(XS, dtype=np.uint8)
-    WS = np.ascontiguousarray(WS, dtype=np.uint8)
-    M, K = X.shape
-    K2, N = W.shape
-    assert K == K2 and K % 32 == 0
-    assert XS.shape == (M, K // 32) and WS.shape == (K // 32, N), (XS.shape, WS.shape)
-    Y = np.empty((M, N), dtype=np.float64)
-    S = np.empty((M, N), dtype=np.float64) if want_s else None
-    rc = _load().oracle_gemm_mxfp8(M, N, K, _ptr(X), K, _ptr(W), N, _ptr(XS), K // 32, _ptr(WS), N,
-                                   _ptr(Y), N, _ptr(S) if want_s else None, N)
-    if rc != 0:
-        raise RuntimeError(f"oracle_gemm_mxfp8 failed rc={rc}")
-    return (Y, S) if want_s else Y
+    return default().gemm_mxfp8(X, W, XS, WS, want_s)
 
 
 # ------------------------------------------------------------------ tolerance
@@ -160,7 +192,7 @@ def unit_roundoff(p: int) -> float:
 
 
 def gamma(n: int, u: float) -> float:
-    """gamma_n = n u / (1 - n u), the blog's sequential-sum constant."""
+    """gamma_n = n u / (1 - n u), the constant of the blog's sequential-sum bound."""
     nu = n * u
     if nu >= 1.0:
         return float("inf")

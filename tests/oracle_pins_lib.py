@@ -1,0 +1,275 @@
+"""Pins for the CPU oracle: checks against facts the pages and mathematics fix.
+
+Every check takes an ``oracle.Oracle`` so that the same checks can be run on
+deliberately broken copies of the oracle (tests/test_oracle_mutations.py):
+each plausible mistake must make at least one of them fail.
+
+Sources of truth used here, none of which is the oracle itself:
+  * exact arithmetic (``fractions.Fraction``, ``math.fsum``) on tiny inputs;
+  * integer-valued inputs, whose products and sums are exact in binary64;
+  * closed forms derived from the blog's linspace experiment (section on
+    batch invariance: a = linspace(-1000, 1000, 2048*4096) reshaped [2048, 4096],
+    b = linspace(-1000, 1000, 4096*4096) reshaped [4096, 4096]);
+  * the blog's floating-point non-associativity example (its section on
+    non-associativity), which fixes the summation order;
+  * the row-separability identity [A; B] C = [A C; B C] (blog, section on
+    batch invariance);
+  * torch's CPU float8_e4m3fn / float8_e8m0fnu / bfloat16 conversions
+    (library routines) for the decoders;
+  * invariances of power-of-two block scaling (exact in binary64).
+"""
+from __future__ import annotations
+
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import torch
+
+import oracle
+from oracle import exact
+from bigemm_inputs import (normal_bf16, int_bf16, linspace_bf16, normal_e4m3, int_e4m3,
+                           e8m0_scales, f32_to_bf16_bits)
+
+U64 = 2.0 ** -53
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# ------------------------------------------------------------ reference decoders (torch, CPU)
+def t_bf16(bits) -> np.ndarray:
+    b = np.ascontiguousarray(np.asarray(bits, dtype=np.uint16))
+    return torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+
+
+def t_e4m3(codes) -> np.ndarray:
+    c = np.ascontiguousarray(np.asarray(codes, dtype=np.uint8))
+    return torch.from_numpy(c).view(torch.float8_e4m3fn).to(torch.float32).to(torch.float64).numpy()
+
+
+def t_e8m0(codes) -> np.ndarray:
+    c = np.ascontiguousarray(np.asarray(codes, dtype=np.uint8))
+    return torch.from_numpy(c).view(torch.float8_e8m0fnu).to(torch.float32).to(torch.float64).numpy()
+
+
+def _close(got, want, bound, what):
+    err = np.abs(np.asarray(got, np.float64) - np.asarray(want, np.float64))
+    bad = err > bound
+    assert not bad.any(), f"{what}: {int(bad.sum())} elements outside bound, worst excess {float((err - bound).max())}"
+
+
+# ------------------------------------------------------------------------- checks
+def check_sum_order(orc: oracle.Oracle):
+    """The blog's (0.1 + 1e20) - 1e20 = 0 versus 0.1 + (1e20 - 1e20) = 0.1: with the
+    terms as a row of A and a column of ones as B, an oracle that sums k ascending
+    must reproduce the left-to-right result of each listed order."""
+    with open(os.path.join(GOLDEN, "fp_nonassoc.txt")) as f:
+        rows = [ln.split() for ln in f if ln.strip() and not ln.startswith("#")]
+    for r in rows:
+        terms = [float(v) for v in r[:3]]
+        expect = float(r[3])
+        Y = orc.gemm_f64(np.array([terms]), np.ones((3, 1)), want_s=False)
+        assert Y[0, 0] == expect, (terms, Y[0, 0], expect)
+
+
+def check_bruteforce_bf16(orc: oracle.Oracle, trials: int = 12):
+    rng = np.random.default_rng(1234)
+    for t in range(trials):
+        M, N, K = int(rng.integers(1, 7)), int(rng.integers(1, 7)), int(rng.integers(1, 65))
+        X = normal_bf16(100 + t, (M, K))
+        W = normal_bf16(200 + t, (K, N))
+        Y, S = orc.gemm_bf16(X, W)
+        Yf, Sf = exact.fsum_gemm_bf16(X, W)
+        g = oracle.gamma(max(K - 1, 0), U64)
+        _close(Y, Yf, g * Sf, f"bf16 brute force M={M} N={N} K={K}")
+        _close(S, Sf, g * Sf, f"bf16 S brute force M={M} N={N} K={K}")
+    # exact rationals agree with the correctly rounded fsum on one case
+    X = normal_bf16(7, (2, 24))
+    W = normal_bf16(8, (24, 3))
+    Q = exact.fraction_gemm_bf16(X, W)
+    Yf, _ = exact.fsum_gemm_bf16(X, W)
+    for i in range(2):
+        for j in range(3):
+            assert float(Q[i][j]) == Yf[i, j]
+
+
+def check_bruteforce_mx(orc: oracle.Oracle, trials: int = 8):
+    rng = np.random.default_rng(4321)
+    for t in range(trials):
+        M, N = int(rng.integers(1, 6)), int(rng.integers(1, 6))
+        K = 32 * int(rng.integers(1, 5))
+        X = normal_e4m3(300 + t, (M, K))
+        W = normal_e4m3(400 + t, (K, N))
+        XS = e8m0_scales(500 + t, (M, K // 32), "var")
+        WS = e8m0_scales(600 + t, (K // 32, N), "var")
+        Y, S = orc.gemm_mxfp8(X, W, XS, WS)
+        Yf, Sf = exact.fsum_gemm_mxfp8(X, W, XS, WS)
+        g = oracle.gamma(K - 1, U64)
+        _close(Y, Yf, g * Sf, f"mx brute force M={M} N={N} K={K}")
+        _close(S, Sf, g * Sf, f"mx S brute force M={M} N={N} K={K}")
+
+
+def check_integer_bf16(orc: oracle.Oracle):
+    """Integer operands: every product and partial sum is an exact integer, so the
+    oracle must equal int64 arithmetic exactly. Non-square shapes expose transposes."""
+    for (M, K, N, s) in [(5, 40, 19, 0), (1, 8, 3, 1), (9, 200, 7, 2), (3, 3, 11, 3)]:
+        X = int_bf16(700 + s, (M, K))
+        W = int_bf16(800 + s, (K, N))
+        Xi = t_bf16(X).astype(np.int64)
+        Wi = t_bf16(W).astype(np.int64)
+        Y = orc.gemm_bf16(X, W, want_s=False)
+        assert np.array_equal(Y, (Xi @ Wi).astype(np.float64)), f"integer bf16 {M}x{K}x{N}"
+
+
+def check_integer_mx(orc: oracle.Oracle):
+    """E4M3 integers with K-varying E8M0 scales 2^[-4, 4]: x~ * 2^4 and w~ * 2^4 are
+    integers, so 256 * Y must equal an int64 product exactly."""
+    for (M, K, N, s) in [(4, 96, 6, 0), (2, 256, 5, 1), (7, 32, 9, 2)]:
+        X = int_e4m3(900 + s, (M, K))
+        W = int_e4m3(950 + s, (K, N))
+        XS = e8m0_scales(990 + s, (M, K // 32), "var")
+        WS = e8m0_scales(995 + s, (K // 32, N), "var")
+        xs_e = XS.astype(np.int64) - 127 + 4      # exponent + 4 >= 0
+        ws_e = WS.astype(np.int64) - 127 + 4
+        Xi = t_e4m3(X).astype(np.int64) * (1 << np.repeat(xs_e, 32, axis=1))
+        Wi = t_e4m3(W).astype(np.int64) * (1 << np.repeat(ws_e, 32, axis=0))
+        Y = orc.gemm_mxfp8(X, W, XS, WS, want_s=False)
+        assert np.array_equal(Y * 256.0, (Xi @ Wi).astype(np.float64)), f"integer mx {M}x{K}x{N}"
+
+
+def check_decoders(orc: oracle.Oracle):
+    codes = np.arange(256, dtype=np.uint8)
+    mine = orc.decode_e4m3(codes)
+    ref = t_e4m3(codes)
+    assert np.array_equal(np.isnan(mine), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(mine[ok], ref[ok]) and np.array_equal(np.signbit(mine[ok]), np.signbit(ref[ok]))
+    # OCP E4M3FN landmarks: 1.0, max 448, min subnormal 2^-9, min normal 2^-6, NaN at S.1111.111
+    assert mine[0x38] == 1.0 and mine[0x7E] == 448.0 and mine[0x01] == 2.0 ** -9 and mine[0x08] == 2.0 ** -6
+    assert np.isnan(mine[0x7F]) and np.isnan(mine[0xFF]) and mine[0xFE] == -448.0
+    e8 = orc.decode_e8m0(codes)
+    r8 = t_e8m0(codes)
+    assert np.array_equal(np.isnan(e8), np.isnan(r8)) and np.array_equal(e8[:255], r8[:255])
+    assert e8[127] == 1.0 and e8[0] == 2.0 ** -127 and np.isnan(e8[255])
+    allb = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    mb = orc.decode_bf16(allb)
+    rb = t_bf16(allb)
+    assert np.array_equal(np.isnan(mb), np.isnan(rb))
+    okb = ~np.isnan(rb)
+    assert np.array_equal(mb[okb], rb[okb]) and np.array_equal(np.signbit(mb[okb]), np.signbit(rb[okb]))
+
+
+def _linspace_cols(n_total, D, cols, lo=-1000.0, hi=1000.0, dtype=np.float64):
+    """Columns `cols` of linspace(lo, hi, n_total).reshape(-1, D) in fp64 (same formula as the generator)."""
+    k = np.arange(n_total // D, dtype=np.float64)[:, None]
+    idx = k * D + np.asarray(cols, dtype=np.float64)[None, :]
+    return lo + ((hi - lo) * idx) / float(n_total - 1)
+
+
+def check_linspace_closed_form(orc: oracle.Oracle):
+    """Row 0 of a.b for the blog's unrounded linspace operands equals the closed form
+    D a0 b0(j) + (a0 b1 + a1 b0(j)) S1 + a1 b1 S2 (exact rationals), up to the
+    sequential-sum bound plus the operands' own rounding."""
+    B, D = 2048, 4096
+    cols = [0, 1, 2, 1000, 2047, 2048, 4094, 4095]
+    a_row = (-1000.0 + (2000.0 * np.arange(D, dtype=np.float64)) / float(B * D - 1))[None, :]
+    b_cols = _linspace_cols(D * D, D, cols)
+    Y, S = orc.gemm_f64(a_row, b_cols)
+    S1 = Fraction(D * (D - 1), 2)
+    S2 = Fraction((D - 1) * D * (2 * D - 1), 6)
+    a0, a1 = Fraction(-1000), Fraction(2000, B * D - 1)
+    b1 = Fraction(2000 * D, D * D - 1)
+    for t, j in enumerate(cols):
+        b0 = Fraction(-1000) + Fraction(2000 * j, D * D - 1)
+        exact_val = D * a0 * b0 + (a0 * b1 + a1 * b0) * S1 + a1 * b1 * S2
+        bound = (oracle.gamma(D - 1, U64) + 8 * U64) * S[0, t]
+        assert abs(Y[0, t] - float(exact_val)) <= bound, (j, Y[0, t], float(exact_val))
+
+
+def check_linspace_bf16_row0(orc: oracle.Oracle):
+    """bf16-rounded linspace: row 0 of a rounds to exactly -1000, so (a.b)[0, j] is
+    -1000 times the exact column sum of b; the exact sums are antisymmetric,
+    y[0, j] = -y[0, D-1-j], because b[k, j] = -b[D-1-k, D-1-j]."""
+    B, D = 2048, 4096
+    a_full_row0 = linspace_bf16(-1000.0, 1000.0, B * D)[:D]  # row 0 of a
+    assert np.all(t_bf16(a_full_row0) == -1000.0)
+    b = linspace_bf16(-1000.0, 1000.0, D * D, (D, D))
+    cols = [0, 1, 2047, 2048, 4094, 4095]
+    Y, S = orc.gemm_bf16(a_full_row0[None, :], np.ascontiguousarray(b[:, cols]))
+    bd = t_bf16(b[:, cols])
+    sums = np.array([math.fsum(bd[:, t]) for t in range(len(cols))])
+    _close(Y[0], -1000.0 * sums, oracle.gamma(D - 1, U64) * S[0], "bf16 linspace row 0")
+    assert sums[0] == -sums[5] and sums[1] == -sums[4] and sums[2] == -sums[3]
+
+
+def check_row_separability(orc: oracle.Oracle):
+    X = normal_bf16(11, (23, 96))
+    W = normal_bf16(12, (96, 40))
+    Y = orc.gemm_bf16(X, W, want_s=False)
+    for k in (1, 7, 16, 22):
+        Yk = np.concatenate([orc.gemm_bf16(X[:k], W, want_s=False), orc.gemm_bf16(X[k:], W, want_s=False)])
+        assert Yk.tobytes() == Y.tobytes(), k
+    Xm = normal_e4m3(13, (9, 64))
+    Wm = normal_e4m3(14, (64, 10))
+    XS = e8m0_scales(15, (9, 2), "var")
+    WS = e8m0_scales(16, (2, 10), "var")
+    Ym = orc.gemm_mxfp8(Xm, Wm, XS, WS, want_s=False)
+    for k in (1, 4, 8):
+        Yk = np.concatenate([orc.gemm_mxfp8(Xm[:k], Wm, XS[:k], WS, want_s=False),
+                             orc.gemm_mxfp8(Xm[k:], Wm, XS[k:], WS, want_s=False)])
+        assert Yk.tobytes() == Ym.tobytes(), k
+
+
+def check_mx_equals_prescaled_bf16(orc: oracle.Oracle):
+    """A scaled E4M3 value is exactly representable in bf16, so the MX oracle must equal
+    the bf16 oracle on operands pre-scaled elsewhere (torch decode, numpy ldexp)."""
+    M, K, N = 6, 128, 7
+    X = normal_e4m3(21, (M, K))
+    W = normal_e4m3(22, (K, N))
+    XS = e8m0_scales(23, (M, K // 32), "var")
+    WS = e8m0_scales(24, (K // 32, N), "var")
+    xt = np.ldexp(t_e4m3(X), np.repeat(XS.astype(np.int64) - 127, 32, axis=1))
+    wt = np.ldexp(t_e4m3(W), np.repeat(WS.astype(np.int64) - 127, 32, axis=0))
+    xb = f32_to_bf16_bits(xt.astype(np.float32))
+    wb = f32_to_bf16_bits(wt.astype(np.float32))
+    assert np.array_equal(t_bf16(xb), xt) and np.array_equal(t_bf16(wb), wt)  # exact re-encoding
+    Ym = orc.gemm_mxfp8(X, W, XS, WS, want_s=False)
+    Yb = orc.gemm_bf16(xb, wb, want_s=False)
+    assert Ym.tobytes() == Yb.tobytes()
+
+
+def check_scale_shift(orc: oracle.Oracle):
+    """Moving 2^s from X's block b to W's block b leaves Y bit-identical; adding s to
+    every X scale multiplies Y by exactly 2^s."""
+    M, K, N = 5, 160, 6
+    X = normal_e4m3(31, (M, K))
+    W = normal_e4m3(32, (K, N))
+    XS = e8m0_scales(33, (M, K // 32), "var")
+    WS = e8m0_scales(34, (K // 32, N), "var")
+    Y = orc.gemm_mxfp8(X, W, XS, WS, want_s=False)
+    for b, s in [(0, 3), (2, -2), (4, 1)]:
+        XS2 = XS.copy()
+        WS2 = WS.copy()
+        XS2[:, b] = (XS2[:, b].astype(np.int64) + s).astype(np.uint8)
+        WS2[b, :] = (WS2[b, :].astype(np.int64) - s).astype(np.uint8)
+        Y2 = orc.gemm_mxfp8(X, W, XS2, WS2, want_s=False)
+        assert Y2.tobytes() == Y.tobytes(), (b, s)
+    for s in (-3, 2):
+        XS3 = (XS.astype(np.int64) + s).astype(np.uint8)
+        Y3 = orc.gemm_mxfp8(X, W, XS3, WS, want_s=False)
+        assert np.array_equal(Y3, np.ldexp(Y, s)), s
+
+
+def check_degenerate(orc: oracle.Oracle):
+    Y, S = orc.gemm_bf16(np.zeros((0, 16), np.uint16), normal_bf16(1, (16, 4)))
+    assert Y.shape == (0, 4)
+    Y, S = orc.gemm_bf16(np.zeros((3, 16), np.uint16), normal_bf16(1, (16, 4)))
+    assert np.all(Y == 0) and np.all(S == 0)
+    X = normal_bf16(2, (4, 8))
+    Y = orc.gemm_bf16(X, normal_bf16(3, (8, 1)), want_s=False)
+    assert Y.shape == (4, 1)
+
+
+ALL_CHECKS = [check_sum_order, check_bruteforce_bf16, check_bruteforce_mx, check_integer_bf16,
+              check_integer_mx, check_decoders, check_linspace_closed_form, check_linspace_bf16_row0,
+              check_row_separability, check_mx_equals_prescaled_bf16, check_scale_shift, check_degenerate]

@@ -1,0 +1,95 @@
+"""The C-ABI library loads, exports every declared entry point, and validates
+arguments as its header states (host-only calls; no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import invariant_gemm_deterministic_amd as bg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bigemm.h")
+A = 1 << 20  # a 16-byte-aligned fake device address; check_args never dereferences pointers
+
+
+def declared_functions():
+    with open(HEADER) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"BIGEMM_API\s+[\w\s\*]+?\b(bigemm_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    fns = declared_functions()
+    for name in ("bigemm_create", "bigemm_run", "bigemm_destroy", "bigemm_status_str",
+                 "bigemm_get_config", "bigemm_check_args", "bigemm_abi_version"):
+        assert name in fns
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(bg.library_path())
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_abi_version_and_status_strings():
+    assert bg.bigemm_abi_version() == 1
+    for s in range(5):
+        assert bg.bigemm_status_str(s)
+    assert "unknown" in bg.bigemm_status_str(99)
+
+
+def test_null_handle_paths():
+    lib = bg.load()
+    assert lib.bigemm_destroy(None) == bg.BIGEMM_OK
+    assert bg.bigemm_run(0, 1, 8, 8, A, 8, A, 8, A, 8, check=False) == bg.BIGEMM_ERR_ARG
+    assert lib.bigemm_get_config(None, None, None, None) == bg.BIGEMM_ERR_ARG
+    assert lib.bigemm_create(None, None) == bg.BIGEMM_ERR_ARG
+
+
+BF = (bg.BIGEMM_BF16, bg.BIGEMM_BF16, bg.BIGEMM_F32, 0)
+MX = (bg.BIGEMM_E4M3, bg.BIGEMM_E4M3, bg.BIGEMM_F32, 32)
+
+
+def chk(desc, M, N, K, X=A, ldx=None, W=A, ldw=None, Y=A, ldy=None, XS=0, ldxs=0, WS=0, ldws=0):
+    return bg.bigemm_check_args(*desc, M, N, K, X, K if ldx is None else ldx, W, N if ldw is None else ldw,
+                                Y, N if ldy is None else ldy, XS, ldxs, WS, ldws)
+
+
+def test_check_args_accepts_valid_bf16():
+    assert chk(BF, 4096, 4096, 4096) == bg.BIGEMM_OK
+    assert chk(BF, 1, 128, 256) == bg.BIGEMM_OK
+    assert chk(BF, 0, 128, 256, X=0, W=0, Y=0) == bg.BIGEMM_OK       # M = 0 is a no-op
+    assert chk(BF, 5, 16, 8, ldx=64, ldw=32, ldy=20) == bg.BIGEMM_OK  # padded leading dims
+
+
+@pytest.mark.parametrize("kw", [
+    dict(M=-1), dict(N=0), dict(K=0), dict(K=12), dict(N=12),            # shape rules
+    dict(ldx=4), dict(ldw=4), dict(ldy=4),                               # ld < row width
+    dict(ldx=12, K=8), dict(ldy=10),                                     # rows not 16-byte aligned
+    dict(X=0), dict(W=0), dict(Y=0), dict(X=A + 2), dict(Y=A + 4),      # null / misaligned
+    dict(XS=A, ldxs=1),                                                  # scales on a bf16 handle
+    dict(ldx=(1 << 23)),                                                 # 128*ldx*2 >= 2^31
+])
+def test_check_args_rejects_bf16(kw):
+    base = dict(M=16, N=64, K=64)
+    base.update(kw)
+    M, N, K = base.pop("M"), base.pop("N"), base.pop("K")
+    assert chk(BF, M, N, K, **base) == bg.BIGEMM_ERR_ARG
+
+
+def test_check_args_mxfp8():
+    ok = dict(XS=A, ldxs=4, WS=A, ldws=64)
+    assert chk(MX, 16, 64, 128, **ok) == bg.BIGEMM_OK
+    assert chk(MX, 16, 64, 160, XS=A, ldxs=5, WS=A, ldws=64) == bg.BIGEMM_OK   # K % 128 != 0 is fine
+    assert chk(MX, 16, 64, 100, **ok) == bg.BIGEMM_ERR_ARG                     # K % 32 != 0
+    assert chk(MX, 16, 72, 128, XS=A, ldxs=4, WS=A, ldws=72) == bg.BIGEMM_ERR_ARG  # N % 16 != 0
+    assert chk(MX, 16, 64, 128, XS=0, ldxs=4, WS=A, ldws=64) == bg.BIGEMM_ERR_ARG
+    assert chk(MX, 16, 64, 128, XS=A, ldxs=3, WS=A, ldws=64) == bg.BIGEMM_ERR_ARG  # ldxs < K/32
+    assert chk(MX, 16, 64, 128, XS=A + 1, ldxs=4, WS=A + 3, ldws=64) == bg.BIGEMM_OK  # scales unaligned ok
+
+
+def test_check_args_rejects_unsupported_descriptors():
+    assert chk((bg.BIGEMM_BF16, bg.BIGEMM_E4M3, bg.BIGEMM_F32, 0), 4, 64, 64) == bg.BIGEMM_ERR_UNSUPPORTED
+    assert chk((bg.BIGEMM_BF16, bg.BIGEMM_BF16, bg.BIGEMM_BF16, 0), 4, 64, 64) == bg.BIGEMM_ERR_UNSUPPORTED
+    assert chk((bg.BIGEMM_E4M3, bg.BIGEMM_E4M3, bg.BIGEMM_F32, 16), 4, 64, 64) == bg.BIGEMM_ERR_UNSUPPORTED

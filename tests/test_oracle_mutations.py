@@ -1,0 +1,55 @@
+"""Plant plausible mistakes in copies of the oracle's C source and check that the
+pins catch every one of them (no GPU involved; the shipped oracle is untouched)."""
+import os
+import tempfile
+
+import pytest
+
+import oracle
+import oracle_pins_lib as pins
+
+# (name, text in oracle.c, replacement). Every replacement keeps memory accesses in bounds.
+MUTATIONS = [
+    ("drop_last_k", "for (int64_t k = 0; k < K; ++k) {\n      const double a = A[i * lda + k];",
+     "for (int64_t k = 0; k < K - 1; ++k) {\n      const double a = A[i * lda + k];"),
+    ("reverse_k_order", "for (int64_t k = 0; k < K; ++k) {\n      const double a = A[i * lda + k];",
+     "for (int64_t k = K - 1; k >= 0; --k) {\n      const double a = A[i * lda + k];"),
+    ("wrong_sign", "acc[j] += a * brow[j];", "acc[j] -= a * brow[j];"),
+    ("row_index", "const double a = A[i * lda + k];", "const double a = A[(i > 0 ? i - 1 : 0) * lda + k];"),
+    ("w_rows_reversed", "B[k * N + j] = oracle_decode_bf16(W[k * ldw + j]);",
+     "B[k * N + j] = oracle_decode_bf16(W[(K - 1 - k) * ldw + j]);"),
+    ("s_without_abs", "sabs[j] += fabs(a * brow[j]);", "sabs[j] += a * brow[j];"),
+    ("bf16_low_bit", "uint32_t u = (uint32_t)bits << 16;", "uint32_t u = (uint32_t)(bits & 0xFFFE) << 16;"),
+    ("e4m3_bias", "v = ldexp((double)(8 + m), e - 10);", "v = ldexp((double)(8 + m), e - 11);"),
+    ("e4m3_subnormal", "v = ldexp((double)m, -9);", "v = ldexp((double)m, -10);"),
+    ("e4m3_nan", "if (e == 15 && m == 7) return NAN;", "if (e == 15 && m == 7) return 480.0;"),
+    ("e8m0_bias", "return ldexp(1.0, (int)code - 127);", "return ldexp(1.0, (int)code - 126);"),
+    ("x_scale_block", "oracle_decode_e8m0(XS[i * ldxs + k / 32])", "oracle_decode_e8m0(XS[i * ldxs + (k % 32) % ldxs])"),
+    ("w_scale_column", "oracle_decode_e8m0(WS[(k / 32) * ldws + j])", "oracle_decode_e8m0(WS[(k / 32) * ldws + (N - 1 - j)])"),
+    ("x_scale_dropped", "A[i * K + k] = e4m3_table[X[i * ldx + k]] * oracle_decode_e8m0(XS[i * ldxs + k / 32]);",
+     "A[i * K + k] = e4m3_table[X[i * ldx + k]];"),
+]
+
+
+@pytest.fixture(scope="module")
+def source():
+    with open(oracle.SOURCE) as f:
+        return f.read()
+
+
+@pytest.mark.parametrize("name,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_pins_catch_mutation(source, name, old, new):
+    assert source.count(old) == 1, f"mutation {name} does not apply"
+    with tempfile.TemporaryDirectory() as d:
+        src = os.path.join(d, "oracle_mut.c")
+        with open(src, "w") as f:
+            f.write(source.replace(old, new))
+        lib = oracle.build(force=True, src=src, out=os.path.join(d, "liboracle_mut.so"))
+        orc = oracle.Oracle(lib)
+        failed = []
+        for check in pins.ALL_CHECKS:
+            try:
+                check(orc)
+            except AssertionError:
+                failed.append(check.__name__)
+        assert failed, f"no pin caught mutation {name}"
