@@ -7,8 +7,8 @@
 // issue (background) adds the failure mode to avoid: two kernel classes with
 // different K-loop schedules for different rows. So here:
 //
-//   * one tile shape (128 x 128 outputs, 4 waves of 64 x 64) and one MFMA shape
-//     per input type, whatever M, N or K;
+//   * one tile shape (128 x 128 outputs) and one MFMA shape per input type,
+//     whatever M, N or K;
 //   * every output element is produced by one lane of one wave, accumulating in
 //     fp32 registers over the K blocks in ascending order, then ascending MFMA
 //     steps inside the block — the same chain for interior and edge tiles;
@@ -22,7 +22,8 @@
 // tile), never the arithmetic inside a tile.
 //
 // Data movement: global -> LDS with buffer_load_dwordx4 ... lds (no VGPR
-// staging), a 3-stage ring of LDS buffers, one barrier per K block. Operand
+// staging), a ring of LDS buffers (several K blocks in flight), one barrier
+// per K block. Operand
 // fragments come from LDS with ds_read_b128 (row operand, K contiguous) and
 // the transposing ds_read_b64_tr_b16 / ds_read_b64_tr_b8 (the W operand, which
 // is N-contiguous in memory). Both LDS tiles are XOR-swizzled at 16-byte
@@ -57,9 +58,9 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 #define LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
 
-constexpr int kThreads = 256;                 // 4 waves of 64, arranged 2 x 2
+constexpr int kThreads = 256;                 // MXFP8 kernel: 4 waves of 64, arranged 2 x 2
 constexpr int kTileBytes = 16384;             // one operand tile per stage (both dtypes)
-// Pipeline: three LDS stages (stage0..2 in each kernel), 96 KiB per workgroup.
+// Pipeline stages: bf16 uses four (128 KiB), MXFP8 three (96 KiB).
 constexpr int kStageBytes = 2 * kTileBytes;   // X tile + W tile
 constexpr uint32_t kOob = 0x80000000u;        // buffer offset that is always out of range
 constexpr int kNumRecords = 0x7FFFFFFF;       // every in-range offset is below 2^31
@@ -108,11 +109,16 @@ __device__ __forceinline__ int swz_w8(int k) { return k & 7; }
 
 // ------------------------------------------------------------------------ bf16
 //
-// K block 64, MFMA 32x32x16 bf16, fp32 accumulate. Per stage: X tile 128 x 64
-// bf16 (rows of 128 B), W tile 64 x 128 bf16 (rows of 256 B).
+// K block 64, MFMA 32x32x16 bf16, fp32 accumulate. 512 threads: 8 waves in a
+// 2 x 4 grid, each wave owning a 64 x 32 block of the 128 x 128 output tile
+// (two 32 x 32 MFMA fragments stacked along M). Two waves share each SIMD,
+// so one can issue while the other waits on LDS. Per stage: X tile 128 x 64
+// bf16 (rows of 128 B), W tile 64 x 128 bf16 (rows of 256 B); four stages in
+// a ring (128 KiB), three K blocks in flight.
 constexpr int kBkBf16 = 64;
+constexpr int kThreadsBf16 = 512;
 
-__global__ __launch_bounds__(kThreads, 1)
+__global__ __launch_bounds__(kThreadsBf16, 1)
 void bigemm_bf16_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
                         float* __restrict__ Y, int M, int N, int K,
                         int64_t ldx, int64_t ldw, int64_t ldy, int tiles_m, int tiles_n) {
@@ -121,6 +127,8 @@ void bigemm_bf16_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
   __shared__ __attribute__((aligned(1024))) uint8_t stage0[kStageBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t stage1[kStageBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t stage2[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t stage3[kStageBytes];
+  uint8_t* const stg[4] = {stage0, stage1, stage2, stage3};
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -133,17 +141,17 @@ void bigemm_bf16_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
   const int cols_valid = min(128, N - col0);
   const int nkb = (K + kBkBf16 - 1) / kBkBf16;
 
-  // Load assignment: chunk p = i*256 + tid of each tile (i = 0..3). With
+  // Load assignment: chunk p = i*512 + tid of each tile (i = 0, 1). With
   // buffer_load ... lds a wave's 64 lanes fill 1 KiB of LDS contiguously, so
   // the LDS slot is fixed by p and the swizzle is applied to the global side.
   // xk/wk: the K offset of the chunk inside the block, or a huge value when
   // the chunk's row (column) is outside the matrix, so that one compare with
   // the K remaining in the block decides in-range.
-  uint32_t xoff[4], woff[4];
-  int xk[4], wk[4];
+  uint32_t xoff[2], woff[2];
+  int xk[2], wk[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int p = i * kThreads + tid;
+  for (int i = 0; i < 2; ++i) {
+    const int p = i * kThreadsBf16 + tid;
     const int r = p >> 3, s = p & 7, c = s ^ swz_x(r);
     xoff[i] = (uint32_t)((r * ldx + c * 8) * 2);
     xk[i] = r < rows_valid ? c * 8 : 0x7FFFFFFF;
@@ -154,7 +162,7 @@ void bigemm_bf16_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
   const uint16_t* Xt = X + (int64_t)row0 * ldx;
   const uint16_t* Wt = W + col0;
 
-  // Issue the 8 LDS-DMA loads of K block kb into `stage`. A block past the
+  // Issue the 4 LDS-DMA loads of K block kb into `stage`. A block past the
   // end (kb >= nkb) is still issued, entirely out of range: it loads zeros
   // into a stage nobody reads again, and keeps every pipeline step the same
   // instruction sequence (so the number of loads in flight is fixed).
@@ -164,115 +172,103 @@ void bigemm_bf16_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
     const int kleft = live ? K - k0 : 0;
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(Xt + k0);
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(Wt + (int64_t)k0 * ldw);
-    uint8_t* sx = stage;
-    uint8_t* sw = stage + kTileBytes;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 2; ++i) {
       const uint32_t o = xk[i] < kleft ? xoff[i] : kOob;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, LDS(void, sx + i * 4096 + wave * 1024), 16, o, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, LDS(void, stage + i * 8192 + wave * 1024), 16, o, 0, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 2; ++i) {
       const uint32_t o = wk[i] < kleft ? woff[i] : kOob;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, LDS(void, sw + i * 4096 + wave * 1024), 16, o, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, LDS(void, stage + kTileBytes + i * 8192 + wave * 1024), 16, o,
+                                                0, 0, 0);
     }
   };
 
-  // Fragment addresses (bytes inside a stage's tiles).
-  const int wm = wave >> 1, wn = wave & 1;
-  int a_addr[2][4];   // [fm][kk]
-  int b_addr[2][4][2];  // [fn][kk][half]
+  // Fragment addresses (bytes inside a stage): A for the wave's two 32-row
+  // fragments, B (transposing reads) for its 32 columns, per 16-wide K step kk.
+  const int wm = wave >> 2, wn = wave & 3;
+  int a_addr[2][4];     // [fm][kk]
+  int b_addr[4][2];     // [kk][half]
 #pragma unroll
-  for (int f = 0; f < 2; ++f) {
+  for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
+    for (int f = 0; f < 2; ++f) {
       const int r = wm * 64 + f * 32 + (lane & 31);
       const int c = kk * 2 + (lane >> 5);
       a_addr[f][kk] = r * 128 + ((c ^ swz_x(r)) << 4);
-      const int g = lane >> 4, j = lane & 15;
-      const int col = wn * 64 + f * 32 + (g & 1) * 16 + (j & 3) * 4;
+    }
+    const int g = lane >> 4, j = lane & 15;
+    const int col = wn * 32 + (g & 1) * 16 + (j & 3) * 4;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int kr = kk * 16 + (g >> 1) * 8 + h * 4 + (j >> 2);
-        b_addr[f][kk][h] = kTileBytes + kr * 256 + (((col >> 3) ^ swz_w16(kr)) << 4) + (col & 7) * 2;
-      }
+    for (int h = 0; h < 2; ++h) {
+      const int kr = kk * 16 + (g >> 1) * 8 + h * 4 + (j >> 2);
+      b_addr[kk][h] = kTileBytes + kr * 256 + (((col >> 3) ^ swz_w16(kr)) << 4) + (col & 7) * 2;
     }
   }
 
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+  f32x16 acc[2] = {f32x16{}, f32x16{}};
 
-  // One K block: wait for this stage, refill the stage read two blocks ago,
-  // then run the MFMA chain on this stage.
+  // One K block: wait for this stage (two more blocks, 4 loads each, may stay
+  // in flight), refill the stage read in the previous block, then run the
+  // MFMA chain on this stage: kk ascending, both fragments per kk.
   auto step = [&](int kb, const uint8_t* st, uint8_t* refill) {
-    BIGEMM_WAIT_VMCNT(8);  // only block kb+1's 8 loads may still be in flight
+    BIGEMM_WAIT_VMCNT(8);
     BIGEMM_BARRIER();
-    issue(kb + 2, refill);
+    issue(kb + 3, refill);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      bf16x8 a[2], b[2];
+      bf16x8 a[2];
 #pragma unroll
-      for (int f = 0; f < 2; ++f) {
-        a[f] = *LDS(const bf16x8, st + a_addr[f][kk]);
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS(i16x4, st + b_addr[f][kk][0]));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS(i16x4, st + b_addr[f][kk][1]));
-        const i32x2 lo2 = __builtin_bit_cast(i32x2, lo), hi2 = __builtin_bit_cast(i32x2, hi);
-        const i32x4 v = {lo2[0], lo2[1], hi2[0], hi2[1]};
-        b[f] = __builtin_bit_cast(bf16x8, v);
-      }
+      for (int f = 0; f < 2; ++f) a[f] = *LDS(const bf16x8, st + a_addr[f][kk]);
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS(i16x4, st + b_addr[kk][0]));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS(i16x4, st + b_addr[kk][1]));
+      const i32x2 lo2 = __builtin_bit_cast(i32x2, lo), hi2 = __builtin_bit_cast(i32x2, hi);
+      const i32x4 v = {lo2[0], lo2[1], hi2[0], hi2[1]};
+      const bf16x8 b = __builtin_bit_cast(bf16x8, v);
 #pragma unroll
-      for (int fm = 0; fm < 2; ++fm)
-#pragma unroll
-        for (int fn = 0; fn < 2; ++fn)
-          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[fm], b[fn], acc[fm][fn], 0, 0, 0);
+      for (int f = 0; f < 2; ++f) acc[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[f], b, acc[f], 0, 0, 0);
     }
   };
 
-  // Prologue: a dummy (entirely out-of-range) fill of stage 2, then blocks 0
-  // and 1. The dummy makes the loads in flight at the loop head target the
+  // Prologue: a dummy (entirely out-of-range) fill of stage 3, then blocks 0
+  // to 2. The dummy makes the loads in flight at the loop head target the
   // stages in the same order on entry as on every later iteration.
-  issue(nkb, stage2);
-  issue(0, stage0);
-  issue(1, stage1);
-  // Unrolled by 6 so that each stage is a fixed LDS object in every step.
+  issue(nkb, stg[3]);
+#pragma unroll
+  for (int s = 0; s < 3; ++s) issue(s, stg[s]);
+  // Unrolled by 8 so that each stage is a fixed LDS object in every step.
   // (The compiler cannot track which stage the loads in flight target across
   // the loop back-edge and drains them before the first step of an iteration;
   // a longer body makes that the exception.)
   for (int kb = 0;;) {
-    step(kb, stage0, stage2);
-    if (++kb == nkb) break;
-    step(kb, stage1, stage0);
-    if (++kb == nkb) break;
-    step(kb, stage2, stage1);
-    if (++kb == nkb) break;
-    step(kb, stage0, stage2);
-    if (++kb == nkb) break;
-    step(kb, stage1, stage0);
-    if (++kb == nkb) break;
-    step(kb, stage2, stage1);
-    if (++kb == nkb) break;
+    bool done = false;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      step(kb, stg[u & 3], stg[(u + 3) & 3]);
+      if (++kb == nkb) {
+        done = true;
+        break;
+      }
+    }
+    if (done) break;
   }
   BIGEMM_WAIT_VMCNT(0);  // no LDS-DMA load may outlive the workgroup
 
   // Epilogue: plain fp32 stores, masked through the buffer range check.
   const __amdgpu_buffer_rsrc_t ry = make_rsrc(Y + (int64_t)row0 * ldy + col0);
 #pragma unroll
-  for (int fm = 0; fm < 2; ++fm)
+  for (int f = 0; f < 2; ++f)
 #pragma unroll
-    for (int fn = 0; fn < 2; ++fn)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int rl = wm * 64 + fm * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        const int cl = wn * 64 + fn * 32 + (lane & 31);
-        const uint32_t o = (rl < rows_valid && cl < cols_valid) ? (uint32_t)((rl * ldy + cl) * 4) : kOob;
-        // Copy the element out first: bit-casting an ext_vector element
-        // expression directly reads element 0 with this compiler.
-        const float v = acc[fm][fn][r];
-        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), ry, o, 0, 0);
-      }
+    for (int r = 0; r < 16; ++r) {
+      const int rl = wm * 64 + f * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+      const int cl = wn * 32 + (lane & 31);
+      const uint32_t o = (rl < rows_valid && cl < cols_valid) ? (uint32_t)((rl * ldy + cl) * 4) : kOob;
+      // Copy the element out first: bit-casting an ext_vector element
+      // expression directly reads element 0 with this compiler.
+      const float v = acc[f][r];
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), ry, o, 0, 0);
+    }
 }
 
 // ----------------------------------------------------------------------- MXFP8
@@ -493,7 +489,7 @@ hipError_t launch_bf16(const void* X, const void* W, void* Y, int64_t M, int64_t
                        int64_t ldx, int64_t ldw, int64_t ldy, hipStream_t stream) {
   const int tiles_m = (int)((M + 127) / 128);
   const int tiles_n = (int)((N + 127) / 128);
-  hipLaunchKernelGGL(bigemm_bf16_kernel, dim3(tiles_m * tiles_n), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL(bigemm_bf16_kernel, dim3(tiles_m * tiles_n), dim3(kThreadsBf16), 0, stream,
                      (const uint16_t*)X, (const uint16_t*)W, (float*)Y, (int)M, (int)N, (int)K,
                      ldx, ldw, ldy, tiles_m, tiles_n);
   return hipGetLastError();
