@@ -46,6 +46,25 @@ def _events(torch, stream, fn, reps):
     return s.elapsed_time(e) / reps  # ms per call
 
 
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "bigemm_bf16_kernel_m4096_k4096_n4096_traffic.md")
+KERNEL_SOURCE = os.path.join(ROOT, "invariant_gemm_deterministic_amd", "csrc", "bigemm_kernels.hip")
+
+
+def measured_traffic():
+    """HBM-side bytes per launch at M=K=N=4096 from the committed FETCH_SIZE / WRITE_SIZE
+    summary, or None when the kernel source changed since the counters were taken."""
+    import hashlib
+    try:
+        text = open(TRAFFIC_SUMMARY).read()
+        digest = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    vals = dict(ln.split("=", 1) for ln in text.splitlines() if "=" in ln and not ln.startswith(("#", "`", "|")))
+    if vals.get("kernel_source_sha256", "").strip() != digest:
+        return None
+    return int(float(vals["traffic_bytes_per_launch"]))
+
+
 def cpu_baseline(X, W, target_s: float = 15.0):
     """The oracle (fp64, OpenMP) timed on a bounded sample of rows of the workload."""
     import oracle
@@ -71,6 +90,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--m", type=int, default=4096, help="rows of the timed headline call (profiling other M)")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="one 256 MiB device copy before the GEMMs (scale reference for byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the GEMM shards by rows "
@@ -90,13 +112,22 @@ def main():
     W = torch.from_numpy(Wh.view(np.int16)).to(dev)
     Y = torch.empty((4096, N), dtype=torch.float32, device=dev)
 
+    if args.calib_copy:
+        a = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
     # ---------------------------------------------------------------- headline
-    M = 4096
+    M = args.m
+    assert 1 <= M <= 4096
+    Xm, Ym = X[:M], Y[:M]
     for _ in range(args.warmup):
-        bg.mm(X, W, out=Y)
+        bg.mm(Xm, W, out=Ym)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ms = _events(torch, stream, lambda i: bg.mm(X, W, out=Y), args.steps)
+    ms = _events(torch, stream, lambda i: bg.mm(Xm, W, out=Ym), args.steps)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     flops = 2.0 * M * N * K
@@ -119,8 +150,9 @@ def main():
             reps = max(20, 2 * nsets)
             t = _events(torch, stream, lambda i: bg.mm(Xs[i % nsets], Ws[i % nsets], out=Ys[i % nsets]), reps)
             torch.cuda.synchronize()
-            for y in Ys:
-                diffs += int((y.view(torch.int32) != Yfull[:m].view(torch.int32)).sum().item())
+            if M == 4096:
+                for y in Ys:
+                    diffs += int((y.view(torch.int32) != Yfull[:m].view(torch.int32)).sum().item())
             f = 2.0 * m * N * K
             byts = 2 * m * K + 2 * K * N + 4 * m * N
             sweep.append({"M": m, "us": round(t * 1e3, 2), "tflops": round(f / (t * 1e-3) / 1e12, 1),
@@ -143,12 +175,13 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "bf16 projection GEMM Y[4096,4096] = X[4096,4096] . W[4096,4096], "
+        "config": {"workload": f"bf16 projection GEMM Y[{M},4096] = X[{M},4096] . W[4096,4096], "
                                "X~N(0,1), W~N(0,0.02), fp32 accumulate and output, batch-invariant fixed tile",
                    "M": M, "N": N, "K": K, "tile": list(bg.bigemm_get_config(bg._handle("bf16", 0)))},
         "pct_mfma_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic() if M == 4096 else None},
         "m_sweep": sweep,
         "invariance_byte_diffs": diffs if sweep else None,
         "timed_wall_s": round(wall, 3),

@@ -174,3 +174,33 @@ def test_mxfp8_msweep():
     Y = run(xd, wd)
     for M in _mboundaries() + [1024]:
         assert H.byte_diff(run(tuple(a[:M] for a in xd), wd), Y[:M]) == 0, M
+
+
+# ------------------------------------------------------ device negative control
+def test_nc4_device_split_k_is_caught():
+    """The M sweep on the GPU is not vacuous: a device GEMM whose K split depends on
+    M (tests/nc4) shows byte diffs across the 64-row boundaries at the projection
+    magnitudes, while libbigemm shows none on the same inputs."""
+    import ctypes
+    import nc4
+    lib = nc4.load()
+    K, N, Mmax = 4096, 128, 256
+    xd = dev_bf16(normal_bf16(SEED_X, (Mmax, K)))
+    wd = dev_bf16(normal_bf16(SEED_W, (K, N), 0.02))
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def nc4_run(m):
+        y = torch.empty((m, N), dtype=torch.float32, device=DEV)
+        assert lib.nc4_gemm_bf16(m, N, K, xd.data_ptr(), K, wd.data_ptr(), N, y.data_ptr(), N, stream) == 0
+        torch.cuda.synchronize()
+        return y
+
+    Yn = nc4_run(Mmax)
+    Yb = run((xd,), (wd,))
+    caught = {}
+    for M in _mboundaries():
+        assert H.byte_diff(run((xd[:M],), (wd,)), Yb[:M]) == 0, M
+        caught[M] = H.byte_diff(nc4_run(M), Yn[:M])
+    assert caught[256] == 0 and caught[193] == 0, caught          # same split count as the full batch
+    assert all(caught[M] > 0 for M in (1, 64, 65, 128, 129, 192)), caught
+    assert H.byte_diff(nc4_run(64), nc4_run(64)) == 0             # deterministic run to run
