@@ -113,10 +113,15 @@ __device__ __forceinline__ int swz_w8(int k) { return k & 7; }
 // 2 x 4 grid, each wave owning a 64 x 32 block of the 128 x 128 output tile
 // (two 32 x 32 MFMA fragments stacked along M). Two waves share each SIMD,
 // so one can issue while the other waits on LDS. Per stage: X tile 128 x 64
-// bf16 (rows of 128 B), W tile 64 x 128 bf16 (rows of 256 B); four stages in
-// a ring (128 KiB), three K blocks in flight.
+// bf16 (rows of 128 B), W tile 64 x 128 bf16 (rows of 256 B); kStagesBf16
+// stages in a ring, kStagesBf16 - 1 K blocks in flight.
 constexpr int kBkBf16 = 64;
 constexpr int kThreadsBf16 = 512;
+#ifndef BIGEMM_BF16_STAGES
+#define BIGEMM_BF16_STAGES 4
+#endif
+constexpr int kStagesBf16 = BIGEMM_BF16_STAGES;
+static_assert(kStagesBf16 >= 3 && kStagesBf16 <= 5, "LDS holds 3 to 5 stages of 32 KiB");
 
 __global__ __launch_bounds__(kThreadsBf16, 1)
 void bigemm_bf16_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
@@ -127,8 +132,9 @@ void bigemm_bf16_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
   __shared__ __attribute__((aligned(1024))) uint8_t stage0[kStageBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t stage1[kStageBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t stage2[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t stage3[kStageBytes];
-  uint8_t* const stg[4] = {stage0, stage1, stage2, stage3};
+  __shared__ __attribute__((aligned(1024))) uint8_t stage3[kStagesBf16 > 3 ? kStageBytes : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t stage4[kStagesBf16 > 4 ? kStageBytes : 16];
+  uint8_t* const stg[5] = {stage0, stage1, stage2, stage3, stage4};
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -209,13 +215,13 @@ void bigemm_bf16_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
 
   f32x16 acc[2] = {f32x16{}, f32x16{}};
 
-  // One K block: wait for this stage (two more blocks, 4 loads each, may stay
-  // in flight), refill the stage read in the previous block, then run the
-  // MFMA chain on this stage: kk ascending, both fragments per kk.
+  // One K block: wait for this stage (kStagesBf16 - 2 younger blocks, 4 loads
+  // each, may stay in flight), refill the stage read in the previous block,
+  // then run the MFMA chain on this stage: kk ascending, both fragments per kk.
   auto step = [&](int kb, const uint8_t* st, uint8_t* refill) {
-    BIGEMM_WAIT_VMCNT(8);
+    BIGEMM_WAIT_VMCNT(4 * (kStagesBf16 - 2));
     BIGEMM_BARRIER();
-    issue(kb + 3, refill);
+    issue(kb + kStagesBf16 - 1, refill);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       bf16x8 a[2];
@@ -231,21 +237,22 @@ void bigemm_bf16_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
     }
   };
 
-  // Prologue: a dummy (entirely out-of-range) fill of stage 3, then blocks 0
-  // to 2. The dummy makes the loads in flight at the loop head target the
-  // stages in the same order on entry as on every later iteration.
-  issue(nkb, stg[3]);
+  // Prologue: a dummy (entirely out-of-range) fill of the last stage, then
+  // blocks 0 to kStagesBf16 - 2. The dummy makes the loads in flight at the
+  // loop head target the stages in the same order on entry as on every later
+  // iteration.
+  issue(nkb, stg[kStagesBf16 - 1]);
 #pragma unroll
-  for (int s = 0; s < 3; ++s) issue(s, stg[s]);
-  // Unrolled by 8 so that each stage is a fixed LDS object in every step.
-  // (The compiler cannot track which stage the loads in flight target across
-  // the loop back-edge and drains them before the first step of an iteration;
-  // a longer body makes that the exception.)
+  for (int s = 0; s < kStagesBf16 - 1; ++s) issue(s, stg[s]);
+  // Unrolled by 2 * kStagesBf16 so that each stage is a fixed LDS object in
+  // every step. (The compiler cannot track which stage the loads in flight
+  // target across the loop back-edge and drains them before the first step of
+  // an iteration; a longer body makes that the exception.)
   for (int kb = 0;;) {
     bool done = false;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      step(kb, stg[u & 3], stg[(u + 3) & 3]);
+    for (int u = 0; u < 2 * kStagesBf16; ++u) {
+      step(kb, stg[u % kStagesBf16], stg[(u + kStagesBf16 - 1) % kStagesBf16]);
       if (++kb == nkb) {
         done = true;
         break;
