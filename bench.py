@@ -8,6 +8,8 @@ ABI with inputs resident in HBM. Also reported:
 * ``m_sweep``: TFLOP/s and % of the bf16 MFMA peak for M = 1 ... 4096 at
   K = N = 4096 (small M rotates among buffer sets larger than the 256 MB
   last-level cache, so W is read from HBM), with achieved algorithmic HBM GB/s;
+* ``mxfp8_k4096_n4096``: the MXFP8 kernel (E4M3, K-varying E8M0 scales) at
+  M = 1024 and 4096, against the dense FP8 MFMA peak (context, not the metric);
 * ``invariance_byte_diffs``: every row of every sweep result compared with the
   same row of the M = 4096 result (must be 0);
 * ``roofline``: the kernel's algorithmic flops per launch over its average
@@ -31,6 +33,7 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PEAK_FP8_TFLOPS = 5033.2    # MI355X dense FP8 / MXFP8 MFMA
 M_SWEEP = [1, 16, 64, 128, 256, 512, 1024, 2048, 4096]
 K = N = 4096
 
@@ -162,6 +165,23 @@ def main():
             del Ws, Xs, Ys
             torch.cuda.empty_cache()
 
+    # ------------------------------------------------------- MXFP8 (context)
+    mx = []
+    if not args.no_sweep:
+        from bigemm_inputs import SCALE_SEED_OFFSET, e8m0_scales, normal_e4m3
+        Xm = torch.from_numpy(normal_e4m3(SEED_X, (4096, K))).to(dev)
+        Wm = torch.from_numpy(normal_e4m3(SEED_W, (K, N))).to(dev)
+        XS = torch.from_numpy(e8m0_scales(SEED_X + SCALE_SEED_OFFSET, (4096, K // 32), "var")).to(dev)
+        WS = torch.from_numpy(e8m0_scales(SEED_W + SCALE_SEED_OFFSET, (K // 32, N), "var")).to(dev)
+        for m in (1024, 4096):
+            for _ in range(5):
+                bg.mm(Xm[:m], Wm, XS[:m], WS, out=Y[:m])
+            t = _events(torch, stream, lambda i: bg.mm(Xm[:m], Wm, XS[:m], WS, out=Y[:m]), 20)
+            f = 2.0 * m * N * K
+            mx.append({"M": m, "us": round(t * 1e3, 2), "tflops": round(f / (t * 1e-3) / 1e12, 1),
+                       "pct_fp8_peak": round(100 * f / (t * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 1)})
+        del Xm, Wm, XS, WS
+
     line = {
         "metric": "TFLOP/s vs M (1-4096) at K=N=4096, % MFMA peak; invariance byte-diffs=0",
         "value": round(tflops, 2),
@@ -183,6 +203,7 @@ def main():
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic() if M == 4096 else None},
         "m_sweep": sweep,
+        "mxfp8_k4096_n4096": mx,
         "invariance_byte_diffs": diffs if sweep else None,
         "timed_wall_s": round(wall, 3),
     }

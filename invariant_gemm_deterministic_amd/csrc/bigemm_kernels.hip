@@ -60,7 +60,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kThreads = 256;                 // MXFP8 kernel: 4 waves of 64, arranged 2 x 2
 constexpr int kTileBytes = 16384;             // one operand tile per stage (both dtypes)
-// Pipeline stages: bf16 uses four (128 KiB), MXFP8 three (96 KiB).
 constexpr int kStageBytes = 2 * kTileBytes;   // X tile + W tile
 constexpr uint32_t kOob = 0x80000000u;        // buffer offset that is always out of range
 constexpr int kNumRecords = 0x7FFFFFFF;       // every in-range offset is below 2^31
@@ -284,7 +283,13 @@ void bigemm_bf16_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
 // applied inside the instruction, fp32 accumulate. Per stage: X tile 128 x 128
 // bytes, W tile 128 x 128 bytes (both rows of 128 B).
 constexpr int kBkMx = 128;
+#ifndef BIGEMM_MX_STAGES
+#define BIGEMM_MX_STAGES 3
+#endif
+constexpr int kStagesMx = BIGEMM_MX_STAGES;
+static_assert(kStagesMx >= 3 && kStagesMx <= 4, "LDS holds 3 or 4 stages of 32 KiB");
 
+template <bool kVecXs>
 __global__ __launch_bounds__(kThreads, 1)
 void bigemm_mxfp8_kernel(const uint8_t* __restrict__ X, const uint8_t* __restrict__ W,
                          float* __restrict__ Y, const uint8_t* __restrict__ XS,
@@ -294,6 +299,8 @@ void bigemm_mxfp8_kernel(const uint8_t* __restrict__ X, const uint8_t* __restric
   __shared__ __attribute__((aligned(1024))) uint8_t stage0[kStageBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t stage1[kStageBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t stage2[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t stage3[kStagesMx > 3 ? kStageBytes : 16];
+  uint8_t* const stg[4] = {stage0, stage1, stage2, stage3};
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -393,32 +400,86 @@ void bigemm_mxfp8_kernel(const uint8_t* __restrict__ X, const uint8_t* __restric
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
-  // Scale registers of one K block: [fragment][MFMA step]. Blocks past K read
-  // as out of range (zero).
-  auto load_scales = [&](int kb, int (&sa)[2][2], int (&sb)[2][2]) {
+  // W scales of one K block, [fragment][MFMA step]: one byte per lane and
+  // step (32 columns of two scale rows per load). Blocks past K read as out of
+  // range (zero).
+  auto load_wscales = [&](int kb, int (&sb)[2][2]) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int blk = kb * 4 + kk * 2 + g;
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        const uint32_t ob = blk < ws_lim[f] ? ws_base[f] + (uint32_t)(blk * ldws) : kOob;
+        sb[f][kk] = __builtin_amdgcn_raw_buffer_load_b8(rws, ob, 0, 0);
+      }
+    }
+  };
+  // X scales, byte path: one byte per lane, fragment and step.
+  auto load_xscales = [&](int kb, int (&sa)[2][2]) {
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const int blk = kb * 4 + kk * 2 + g;
 #pragma unroll
       for (int f = 0; f < 2; ++f) {
         const uint32_t oa = blk < xs_lim[f] ? xs_base[f] + (uint32_t)blk : kOob;
-        const uint32_t ob = blk < ws_lim[f] ? ws_base[f] + (uint32_t)(blk * ldws) : kOob;
         sa[f][kk] = __builtin_amdgcn_raw_buffer_load_b8(rxs, oa, 0, 0);
-        sb[f][kk] = __builtin_amdgcn_raw_buffer_load_b8(rws, ob, 0, 0);
       }
     }
   };
+  // X scales, vector path (16-byte aligned scale rows, K a multiple of 512):
+  // the 16 scale bytes of K blocks 4q .. 4q+3 of the lane's row, one 16-byte
+  // load per fragment, so a scale line is requested once per four K blocks
+  // instead of once per block.
+  auto load_xquad = [&](int q, i32x4 (&xq)[2]) {
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+      const uint32_t o = q * 16 < xs_lim[f] ? xs_base[f] + (uint32_t)(q * 16) : kOob;
+      xq[f] = __builtin_amdgcn_raw_buffer_load_b128(rxs, o, 0, 0);
+    }
+  };
 
-  int sa_cur[2][2], sb_cur[2][2], sa_nxt[2][2], sb_nxt[2][2];
+  // Scale registers of the K blocks in flight, one ring slot per stage:
+  // [slot][fragment][MFMA step]. The vector path keeps the X scales of two
+  // groups of four K blocks instead: [group parity][fragment].
+  int sa[kStagesMx][2][2], sb[kStagesMx][2][2];
+  i32x4 xq[2][2];
+  // Unroll length of the K loop: a multiple of the stage count (LDS stages and
+  // scale slots) and, on the vector path, of 8 (two groups of four blocks).
+  constexpr int kUnroll = kVecXs ? (kStagesMx == 3 ? 24 : 8) : 2 * kStagesMx;
 
-  // One K block. Loads in flight after this stage's 8 LDS-DMA loads are at
-  // most: the previous block's 8 scale loads, the next stage's 8 DMA loads and
-  // the next block's... (issued later), so vmcnt <= 16 means this stage landed.
-  auto step = [&](int kb, const uint8_t* st, uint8_t* refill) {
-    BIGEMM_WAIT_VMCNT(16);
+  // One K block. Each block's scale loads are issued just before its LDS-DMA
+  // loads, kStagesMx - 1 blocks ahead, so the wait for this block's DMA also
+  // covers its scales; younger than them are the next kStagesMx - 2 blocks'
+  // 8 scale and 8 DMA loads each. Then the stage read in the previous block is
+  // refilled and the MFMA chain runs on this stage: kk ascending.
+  // u is the step's position in the unrolled loop (kb % kUnroll).
+  auto step = [&](int kb, int u, const uint8_t* st, uint8_t* refill, int (&sac)[2][2], const int (&sbc)[2][2],
+                  int (&san)[2][2], int (&sbn)[2][2]) {
+    // Loads younger than this block's DMA: per later block in flight, 4 W
+    // scale loads, 8 DMA loads and (byte path) 4 X scale loads. On the vector
+    // path a group's two X loads come on top every fourth block; the wait
+    // then covers two loads more than it needs to, which is harmless.
+    BIGEMM_WAIT_VMCNT((kVecXs ? 12 : 16) * (kStagesMx - 2));
     BIGEMM_BARRIER();
-    issue(kb + 2, refill);
-    load_scales(kb + 1, sa_nxt, sb_nxt);
+    const int nb = kb + kStagesMx - 1;
+    if (kVecXs) {
+      // The group that starts one block after the one being refilled (loaded
+      // a step early: the compiler delays these loads by up to a step).
+      if ((u + kStagesMx) % 4 == 0) load_xquad((nb + 1) / 4, xq[((u + kStagesMx) / 4) % 2]);
+    } else {
+      load_xscales(nb, san);
+    }
+    load_wscales(nb, sbn);
+    issue(nb, refill);
+    if (kVecXs) {
+      // This block's X scales: dword kb % 4 of its group, byte kk*2 + g.
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        const int d = xq[(u / 4) % 2][f][u % 4];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) sac[f][kk] = (d >> (8 * (kk * 2 + g))) & 0xFF;
+      }
+    }
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       i32x8 a[2], b[2];
@@ -438,38 +499,42 @@ void bigemm_mxfp8_kernel(const uint8_t* __restrict__ X, const uint8_t* __restric
 #pragma unroll
         for (int fn = 0; fn < 2; ++fn)
           acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              a[fm], b[fn], acc[fm][fn], 0 /*A: E4M3*/, 0 /*B: E4M3*/, 0, sa_cur[fm][kk], 0, sb_cur[fn][kk]);
+              a[fm], b[fn], acc[fm][fn], 0 /*A: E4M3*/, 0 /*B: E4M3*/, 0, sac[fm][kk], 0, sbc[fn][kk]);
     }
-#pragma unroll
-    for (int f = 0; f < 2; ++f)
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        sa_cur[f][kk] = sa_nxt[f][kk];
-        sb_cur[f][kk] = sb_nxt[f][kk];
-      }
   };
 
-  issue(nkb, stage2);
-  issue(0, stage0);
-  load_scales(0, sa_cur, sb_cur);
-  issue(1, stage1);
-  // Unrolled by 6 so that each stage is a fixed LDS object in every step.
-  // (The compiler cannot track which stage the loads in flight target across
-  // the loop back-edge and drains them before the first step of an iteration;
-  // a longer body makes that the exception.)
+  // Prologue: a dummy (entirely out-of-range) fill of the last stage, then
+  // blocks 0 to kStagesMx - 2 with their scales. The dummy makes the loads in
+  // flight at the loop head target the stages in the same order on entry as on
+  // every later iteration.
+  issue(nkb, stg[kStagesMx - 1]);
+#pragma unroll
+  for (int s = 0; s < kStagesMx - 1; ++s) {
+    if (kVecXs) {
+      if (s == 0) load_xquad(0, xq[0]);
+      if ((s + 1) % 4 == 0) load_xquad((s + 1) / 4, xq[((s + 1) / 4) % 2]);
+    } else {
+      load_xscales(s, sa[s]);
+    }
+    load_wscales(s, sb[s]);
+    issue(s, stg[s]);
+  }
+  // Unrolled by kUnroll so that each stage and scale slot is fixed in every
+  // step. (The compiler cannot track which stage the loads in flight
+  // target across the loop back-edge and drains them before the first step of
+  // an iteration; a longer body makes that the exception.)
   for (int kb = 0;;) {
-    step(kb, stage0, stage2);
-    if (++kb == nkb) break;
-    step(kb, stage1, stage0);
-    if (++kb == nkb) break;
-    step(kb, stage2, stage1);
-    if (++kb == nkb) break;
-    step(kb, stage0, stage2);
-    if (++kb == nkb) break;
-    step(kb, stage1, stage0);
-    if (++kb == nkb) break;
-    step(kb, stage2, stage1);
-    if (++kb == nkb) break;
+    bool done = false;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int c = u % kStagesMx, n = (u + kStagesMx - 1) % kStagesMx;
+      step(kb, u, stg[c], stg[n], sa[c], sb[c], sa[n], sb[n]);
+      if (++kb == nkb) {
+        done = true;
+        break;
+      }
+    }
+    if (done) break;
   }
   BIGEMM_WAIT_VMCNT(0);  // no LDS-DMA load may outlive the workgroup
 
@@ -507,7 +572,11 @@ hipError_t launch_mxfp8(const void* X, const void* W, void* Y, const void* XS, c
                         int64_t ldxs, int64_t ldws, hipStream_t stream) {
   const int tiles_m = (int)((M + 127) / 128);
   const int tiles_n = (int)((N + 127) / 128);
-  hipLaunchKernelGGL(bigemm_mxfp8_kernel, dim3(tiles_m * tiles_n), dim3(kThreads), 0, stream,
+  // The X-scale load path depends on the scale layout and K only (never on M);
+  // both paths read the same scale values.
+  const bool vec_xs = K % 512 == 0 && ((uintptr_t)XS & 15) == 0 && ldxs % 16 == 0;
+  hipLaunchKernelGGL(vec_xs ? bigemm_mxfp8_kernel<true> : bigemm_mxfp8_kernel<false>, dim3(tiles_m * tiles_n),
+                     dim3(kThreads), 0, stream,
                      (const uint8_t*)X, (const uint8_t*)W, (float*)Y, (const uint8_t*)XS,
                      (const uint8_t*)WS, (int)M, (int)N, (int)K, ldx, ldw, ldy, ldxs, ldws,
                      tiles_m, tiles_n);

@@ -204,6 +204,40 @@ def test_mxfp8_scale_shift_bit_identical():
     assert y0.tobytes() == y1.tobytes()
 
 
+@pytest.mark.parametrize("K", [1024, 2048])
+def test_mxfp8_scale_load_paths_bit_identical(K):
+    """X scales reach the kernel either as 16-byte rows (16-byte aligned scale
+    rows, K a multiple of 512) or one byte at a time (any other layout). Both
+    paths must give the same bytes: compare packed scales with the same values
+    in padded rows and at an odd base address."""
+    M, N = 200, 256
+    X, W, XS, WS = _mx_inputs(M, N, K, "var", "var", seed=7)
+    y_packed = _run_mx(X, W, XS, WS)
+    nsb = K // 32
+    wide = torch.zeros((M, nsb + 5), dtype=torch.uint8, device=DEV)
+    wide[:, :nsb] = dev_u8(XS)     # rows nsb + 5 bytes apart: not a multiple of 16
+    y_padded = run((dev_u8(X), wide[:, :nsb]), (dev_u8(W), dev_u8(WS))).cpu().numpy()
+    wide.zero_()
+    wide[:, 1:1 + nsb] = dev_u8(XS)  # base one byte past an aligned allocation
+    y_odd = run((dev_u8(X), wide[:, 1:1 + nsb]), (dev_u8(W), dev_u8(WS))).cpu().numpy()
+    assert y_packed.tobytes() == y_padded.tobytes()
+    assert y_packed.tobytes() == y_odd.tobytes()
+
+
+@pytest.mark.parametrize("K", [160, 1024])
+def test_mxfp8_nan_scale_stays_in_its_row(K):
+    """A NaN X scale (E8M0 0xFF) in one row poisons that row only."""
+    M, N = 48, 128
+    X, W, XS, WS = _mx_inputs(M, N, K, "var", "var", seed=3)
+    y0 = _run_mx(X, W, XS, WS)
+    XS2 = XS.copy()
+    XS2[5, :] = 255
+    y1 = _run_mx(X, W, XS2, WS)
+    others = np.arange(M) != 5
+    assert y1[others].tobytes() == y0[others].tobytes()
+    assert np.isnan(y1[5]).all()
+
+
 def test_mxfp8_large_sampled():
     M, N, K = 512, 4096, 4096
     X, W, XS, WS = _mx_inputs(M, N, K, "var", "var")
