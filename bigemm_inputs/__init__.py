@@ -76,6 +76,28 @@ def int_bf16(seed: int, shape, lo: int = -8, hi: int = 8) -> np.ndarray:
     return f32_to_bf16_bits(rng.integers(lo, hi + 1, size=shape).astype(np.float32))
 
 
+def normal_f16(seed: int, shape, sigma: float = 1.0) -> np.ndarray:
+    """N(0, sigma) drawn in float32 from ``default_rng(seed)``, rounded to IEEE binary16
+    (numpy's float32 -> float16 conversion, round to nearest even); returned as uint16 bits."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal(shape, dtype=np.float32)
+    if sigma != 1.0:
+        x = x * np.float32(sigma)
+    return x.astype(np.float16).view(np.uint16)
+
+
+def int_f16(seed: int, shape, lo: int = -8, hi: int = 8) -> np.ndarray:
+    """Uniform integers in [lo, hi] as binary16 bits (exact for |v| <= 2048)."""
+    rng = np.random.default_rng(seed)
+    return rng.integers(lo, hi + 1, size=shape).astype(np.float16).view(np.uint16)
+
+
+def int_i8(seed: int, shape, lo: int = -128, hi: int = 127) -> np.ndarray:
+    """Uniform int8 values in [lo, hi] (the full range by default)."""
+    rng = np.random.default_rng(seed)
+    return rng.integers(lo, hi + 1, size=shape).astype(np.int8)
+
+
 def linspace_bf16(lo: float, hi: float, n: int, shape=None) -> np.ndarray:
     """The blog's linspace operand, rounded to bf16 in two explicit steps.
 

@@ -29,7 +29,7 @@
 extern "C" {
 #endif
 
-#define BIGEMM_ABI_VERSION 1
+#define BIGEMM_ABI_VERSION 2
 
 /* Exported entry points (the library is built with hidden visibility by default). */
 #if defined(__GNUC__)
@@ -52,16 +52,30 @@ typedef enum {
   BIGEMM_BF16 = 1,  /* bfloat16: the top 16 bits of an IEEE binary32                            */
   BIGEMM_F32 = 2,   /* IEEE binary32                                                           */
   BIGEMM_E4M3 = 3,  /* OCP E4M3FN (bias 7, 3 mantissa bits, no infinities, S.1111.111 = NaN)    */
-  BIGEMM_E8M0 = 4   /* OCP E8M0 block scale, 2^(byte - 127), 0xFF = NaN                         */
+  BIGEMM_E8M0 = 4,  /* OCP E8M0 block scale, 2^(byte - 127), 0xFF = NaN                         */
+  BIGEMM_F16 = 5,   /* IEEE binary16                                                           */
+  BIGEMM_I8 = 6,    /* two's-complement signed 8-bit integer                                   */
+  BIGEMM_I32 = 7    /* two's-complement signed 32-bit integer                                  */
 } bigemm_dtype;
 
 /*
- * Operation descriptor. Two combinations are provided:
- *   bf16:  x_type = w_type = BIGEMM_BF16, y_type = BIGEMM_F32, scale_block = 0
- *   MXFP8: x_type = w_type = BIGEMM_E4M3, y_type = BIGEMM_F32, scale_block = 32
+ * Operation descriptor. The combinations provided:
+ *   bf16:  x_type = w_type = BIGEMM_BF16, y_type = BIGEMM_F32 or BIGEMM_BF16, scale_block = 0
+ *   fp16:  x_type = w_type = BIGEMM_F16,  y_type = BIGEMM_F32 or BIGEMM_BF16, scale_block = 0
+ *   MXFP8: x_type = w_type = BIGEMM_E4M3, y_type = BIGEMM_F32 or BIGEMM_BF16, scale_block = 32
  *          (one E8M0 scale per 32 consecutive K elements — the MXFP8 path with a
  *          K-varying scale named in the CANN issue's background and grid)
- * Fields are int32_t (holding bigemm_dtype values) to keep the struct layout fixed.
+ *   int8:  x_type = w_type = BIGEMM_I8,   y_type = BIGEMM_I32, scale_block = 0
+ *          (exact integer products and sums; integer addition is associative, so
+ *          the result does not depend on the order at all — barring overflow,
+ *          which cannot occur for K < 2^31 / 128^2 = 131072)
+ * Floating-point inputs accumulate in fp32 in the one fixed order. A BIGEMM_BF16
+ * output is that fp32 accumulator rounded once, to nearest even (a NaN becomes
+ * a quiet NaN of the same sign: the top 16 bits with bit 6 set); it is
+ * therefore exactly the rounding of the BIGEMM_F32 result of the same call.
+ * The BI, fixed-order and fail-closed rules the blog and the CANN issue state
+ * for the matmul hold for every combination. Fields are int32_t (holding
+ * bigemm_dtype values) to keep the struct layout fixed.
  */
 typedef struct {
   int32_t x_type;
@@ -74,7 +88,7 @@ typedef struct {
  * Create a handle for the current HIP device.
  * Takes no M, N or K: the configuration cannot depend on the problem shape.
  * Returns BIGEMM_ERR_UNSUPPORTED on any device other than gfx950 and for any
- * descriptor other than the two above — it never falls back to another path.
+ * descriptor other than those above — it never falls back to another path.
  * Ownership: the handle owns only immutable configuration; free it with
  * bigemm_destroy. *out is set to NULL on failure.
  */
@@ -85,9 +99,9 @@ BIGEMM_API bigemm_status bigemm_create(const bigemm_desc* desc, bigemm_t* out);
  * return without synchronising.
  *
  * Shapes and layouts (row-major, leading dimensions in ELEMENTS):
- *   X [M, K], leading dimension ldx >= K     (bf16 bits or E4M3 bytes)
- *   W [K, N], leading dimension ldw >= N     (bf16 bits or E4M3 bytes)
- *   Y [M, N], leading dimension ldy >= N     (float32, written, never read)
+ *   X [M, K], leading dimension ldx >= K     (bf16 / fp16 bits, E4M3 or int8 bytes)
+ *   W [K, N], leading dimension ldw >= N     (same type as X)
+ *   Y [M, N], leading dimension ldy >= N     (float32, bf16 or int32; written, never read)
  *   MXFP8 only:
  *   X_scale [M, K/32], leading dimension ldxs >= K/32   (E8M0 bytes)
  *   W_scale [K/32, N], leading dimension ldws >= N      (E8M0 bytes)
@@ -97,12 +111,14 @@ BIGEMM_API bigemm_status bigemm_create(const bigemm_desc* desc, bigemm_t* out);
  * Requirements (violations return BIGEMM_ERR_ARG synchronously; nothing is
  * launched and Y is untouched):
  *   M >= 0, N >= 1, K >= 1; M == 0 is a successful no-op;
- *   bf16:  K % 8 == 0, N % 8 == 0;  MXFP8: K % 32 == 0, N % 16 == 0;
+ *   bf16, fp16: K % 8 == 0, N % 8 == 0;  MXFP8: K % 32 == 0, N % 16 == 0;
+ *   int8: K % 16 == 0, N % 16 == 0;
  *   X, W, Y non-NULL when M > 0, 16-byte aligned; ldx, ldw, ldy such that
- *   every row starts 16-byte aligned (ldx*esize, ldw*esize, ldy*4 multiples of 16);
+ *   every row starts 16-byte aligned (ldx, ldw, ldy times the element size
+ *   multiples of 16);
  *   MXFP8: X_scale, W_scale non-NULL (no alignment requirement);
- *   bf16:  X_scale and W_scale NULL;
- *   128 * ldx * esize, 128 * ldw * esize, 128 * ldy * 4 below 2^31.
+ *   other types: X_scale and W_scale NULL;
+ *   128 * ldx, 128 * ldw, 128 * ldy times the element size below 2^31.
  * Y must not overlap X, W or the scales (not checked).
  *
  * Memory: all buffers are device memory owned by the caller. The library

@@ -33,6 +33,9 @@ BIGEMM_BF16 = 1
 BIGEMM_F32 = 2
 BIGEMM_E4M3 = 3
 BIGEMM_E8M0 = 4
+BIGEMM_F16 = 5
+BIGEMM_I8 = 6
+BIGEMM_I32 = 7
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libbigemm.so")
@@ -151,17 +154,20 @@ def bigemm_check_args(x_type: int, w_type: int, y_type: int, scale_block: int, M
 _handles = {}
 
 
-def _handle(kind: str, device_index: int) -> int:
+# input family -> (x/w dtype, scale block)
+_FAMILIES = {"bf16": (BIGEMM_BF16, 0), "f16": (BIGEMM_F16, 0), "mx": (BIGEMM_E4M3, 32), "i8": (BIGEMM_I8, 0)}
+
+
+def _handle(kind: str, device_index: int, y_type: int = BIGEMM_F32) -> int:
+    """One cached handle per (input family, output type, device)."""
     import torch
 
-    key = (kind, device_index)
+    key = (kind, y_type, device_index)
     h = _handles.get(key)
     if h is None:
+        t, sb = _FAMILIES[kind]
         with torch.cuda.device(device_index):
-            if kind == "bf16":
-                h = bigemm_create(BIGEMM_BF16, BIGEMM_BF16, BIGEMM_F32, 0)
-            else:
-                h = bigemm_create(BIGEMM_E4M3, BIGEMM_E4M3, BIGEMM_F32, 32)
+            h = bigemm_create(t, t, y_type, sb)
         _handles[key] = h
     return h
 
@@ -171,14 +177,17 @@ def _ld(t) -> int:
     return int(t.stride(0)) if t.shape[0] > 1 else int(t.shape[1])
 
 
-def mm(x, w, x_scale=None, w_scale=None, out=None, stream=None):
+def mm(x, w, x_scale=None, w_scale=None, out=None, stream=None, out_dtype=None):
     """Y = X W on the GPU through libbigemm.
 
     bf16: ``x`` [M, K] and ``w`` [K, N] are torch.bfloat16 (or int16/uint16 bit
-    patterns). MXFP8: ``x``/``w`` are torch.float8_e4m3fn (or uint8 codes) and
+    patterns). fp16: torch.float16. int8: torch.int8 (int32 output).
+    MXFP8: ``x``/``w`` are torch.float8_e4m3fn (or uint8 codes) and
     ``x_scale`` [M, K/32], ``w_scale`` [K/32, N] are uint8 E8M0 bytes. Rows
     must be contiguous; the leading dimension is taken from ``stride(0)``.
-    Returns ``out`` (float32 [M, N], allocated if None).
+    Output: ``out`` if given (its dtype selects the output type), else a new
+    [M, N] tensor of ``out_dtype`` (float32 or bfloat16 for floating inputs,
+    default float32; int32 for int8).
     """
     import torch
 
@@ -191,22 +200,38 @@ def mm(x, w, x_scale=None, w_scale=None, out=None, stream=None):
     for t in (x, w):
         if not t.is_cuda or (t.shape[1] > 1 and t.stride(1) != 1):
             raise ValueError("operands must be CUDA tensors with contiguous rows")
+    if x.dtype != w.dtype:
+        raise ValueError(f"x and w must have one dtype ({x.dtype} vs {w.dtype})")
     mx = x_scale is not None or w_scale is not None
     if mx:
-        if x.element_size() != 1 or w.element_size() != 1:
+        if x.element_size() != 1:
             raise ValueError("MXFP8 operands must be 1-byte E4M3 codes")
         if x_scale is None or w_scale is None:
             raise ValueError("MXFP8 needs both x_scale and w_scale")
-    elif x.element_size() != 2 or w.element_size() != 2:
-        raise ValueError("bf16 operands must be 2-byte bf16 bit patterns")
+        kind = "mx"
+    elif x.dtype == torch.float16:
+        kind = "f16"
+    elif x.dtype == torch.int8:
+        kind = "i8"
+    elif x.element_size() == 2:
+        kind = "bf16"
+    else:
+        raise ValueError(f"unsupported operand dtype {x.dtype}")
+    if out is not None:
+        out_dtype = out.dtype
+    elif out_dtype is None:
+        out_dtype = torch.int32 if kind == "i8" else torch.float32
+    ytypes = {torch.float32: BIGEMM_F32, torch.bfloat16: BIGEMM_BF16, torch.int32: BIGEMM_I32}
+    if out_dtype not in ytypes:
+        raise ValueError(f"unsupported output dtype {out_dtype}")
     dev = x.device.index if x.device.index is not None else torch.cuda.current_device()
     if out is None:
-        out = torch.empty((M, N), dtype=torch.float32, device=x.device)
-    if out.dtype != torch.float32 or tuple(out.shape) != (M, N) or (N > 1 and out.stride(1) != 1):
-        raise ValueError("out must be float32 [M, N] with contiguous rows")
+        out = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    if tuple(out.shape) != (M, N) or (N > 1 and out.stride(1) != 1):
+        raise ValueError("out must be [M, N] with contiguous rows")
     if stream is None:
         stream = torch.cuda.current_stream(x.device).cuda_stream
-    h = _handle("mx" if mx else "bf16", dev)
+    h = _handle(kind, dev, ytypes[out_dtype])  # raises BigemmError for a combination not provided
     if mx:
         for t in (x_scale, w_scale):
             if not t.is_cuda or t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):

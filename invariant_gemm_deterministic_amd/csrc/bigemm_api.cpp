@@ -4,7 +4,7 @@
 // configuration cannot be chosen per shape — the single-configuration rule of
 // the nondeterminism blog's batch-invariant matmul section, enforced by the
 // interface. Creation refuses every device but gfx950 and every descriptor
-// but the two provided, rather than falling back (the fail-closed entry-point
+// but those provided, rather than falling back (the fail-closed entry-point
 // discipline of the vLLM mHC batch-invariance PR, review follow-up).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -16,7 +16,7 @@
 #include "bigemm_kernels.h"
 
 struct bigemm_s {
-  int32_t kind;    // 1 = bf16, 2 = MXFP8
+  bigemm::Op op;
   int device;
 };
 
@@ -26,30 +26,38 @@ constexpr int64_t kOffsetLimit = (int64_t)1 << 31;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-int desc_kind(const bigemm_desc* d) {
-  if (!d) return 0;
-  if (d->x_type == BIGEMM_BF16 && d->w_type == BIGEMM_BF16 && d->y_type == BIGEMM_F32 && d->scale_block == 0)
-    return 1;
-  if (d->x_type == BIGEMM_E4M3 && d->w_type == BIGEMM_E4M3 && d->y_type == BIGEMM_F32 && d->scale_block == 32)
-    return 2;
-  return 0;
+// The descriptors provided (include/bigemm.h); in == 0 for anything else.
+bigemm::Op desc_op(const bigemm_desc* d) {
+  bigemm::Op op{0, 0};
+  if (!d || d->x_type != d->w_type) return op;
+  const bool fout = d->y_type == BIGEMM_F32 || d->y_type == BIGEMM_BF16;
+  if ((d->x_type == BIGEMM_BF16 || d->x_type == BIGEMM_F16) && fout && d->scale_block == 0)
+    op = {d->x_type == BIGEMM_BF16 ? bigemm::kInBf16 : bigemm::kInF16, d->y_type};
+  else if (d->x_type == BIGEMM_E4M3 && fout && d->scale_block == 32)
+    op = {bigemm::kInMx, d->y_type};
+  else if (d->x_type == BIGEMM_I8 && d->y_type == BIGEMM_I32 && d->scale_block == 0)
+    op = {bigemm::kInI8, d->y_type};
+  return op;
 }
 
-bigemm_status check(int kind, int64_t M, int64_t N, int64_t K, const void* X, int64_t ldx,
+bigemm_status check(bigemm::Op op, int64_t M, int64_t N, int64_t K, const void* X, int64_t ldx,
                     const void* W, int64_t ldw, const void* Y, int64_t ldy, const void* XS,
                     int64_t ldxs, const void* WS, int64_t ldws) {
-  if (kind == 0) return BIGEMM_ERR_UNSUPPORTED;
+  if (op.in == 0) return BIGEMM_ERR_UNSUPPORTED;
   if (M < 0 || N < 1 || K < 1) return BIGEMM_ERR_ARG;
   if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return BIGEMM_ERR_ARG;
   if (((M + 127) / 128) * ((N + 127) / 128) > INT32_MAX) return BIGEMM_ERR_ARG;  // grid size
-  const int64_t es = kind == 1 ? 2 : 1;
-  if (kind == 1 && (K % 8 != 0 || N % 8 != 0)) return BIGEMM_ERR_ARG;
-  if (kind == 2 && (K % 32 != 0 || N % 16 != 0)) return BIGEMM_ERR_ARG;
+  const bool mx = op.in == bigemm::kInMx;
+  const int64_t es = (op.in == bigemm::kInBf16 || op.in == bigemm::kInF16) ? 2 : 1;
+  const int64_t eo = op.out == BIGEMM_BF16 ? 2 : 4;
+  if (es == 2 && (K % 8 != 0 || N % 8 != 0)) return BIGEMM_ERR_ARG;
+  if (mx && (K % 32 != 0 || N % 16 != 0)) return BIGEMM_ERR_ARG;
+  if (op.in == bigemm::kInI8 && (K % 16 != 0 || N % 16 != 0)) return BIGEMM_ERR_ARG;
   if (ldx < K || ldw < N || ldy < N) return BIGEMM_ERR_ARG;
-  if ((ldx * es) % 16 != 0 || (ldw * es) % 16 != 0 || (ldy * 4) % 16 != 0) return BIGEMM_ERR_ARG;
-  if (128 * ldx * es >= kOffsetLimit || 128 * ldw * es >= kOffsetLimit || 128 * ldy * 4 >= kOffsetLimit)
+  if ((ldx * es) % 16 != 0 || (ldw * es) % 16 != 0 || (ldy * eo) % 16 != 0) return BIGEMM_ERR_ARG;
+  if (128 * ldx * es >= kOffsetLimit || 128 * ldw * es >= kOffsetLimit || 128 * ldy * eo >= kOffsetLimit)
     return BIGEMM_ERR_ARG;
-  if (kind == 1) {
+  if (!mx) {
     if (XS != nullptr || WS != nullptr) return BIGEMM_ERR_ARG;
   } else {
     if (ldxs < K / 32 || ldws < N) return BIGEMM_ERR_ARG;
@@ -58,7 +66,7 @@ bigemm_status check(int kind, int64_t M, int64_t N, int64_t K, const void* X, in
   if (M == 0) return BIGEMM_OK;
   if (!X || !W || !Y) return BIGEMM_ERR_ARG;
   if (!aligned16(X) || !aligned16(W) || !aligned16(Y)) return BIGEMM_ERR_ARG;
-  if (kind == 2 && (!XS || !WS)) return BIGEMM_ERR_ARG;
+  if (mx && (!XS || !WS)) return BIGEMM_ERR_ARG;
   return BIGEMM_OK;
 }
 
@@ -72,7 +80,7 @@ const char* bigemm_status_str(bigemm_status s) {
   switch (s) {
     case BIGEMM_OK: return "ok";
     case BIGEMM_ERR_ARG: return "invalid argument";
-    case BIGEMM_ERR_UNSUPPORTED: return "unsupported device or descriptor (gfx950 bf16 or MXFP8 only)";
+    case BIGEMM_ERR_UNSUPPORTED: return "unsupported device or descriptor (gfx950; bf16, fp16, MXFP8 or int8)";
     case BIGEMM_ERR_DEVICE: return "HIP device error";
     case BIGEMM_ERR_NOMEM: return "out of host memory";
   }
@@ -84,15 +92,15 @@ bigemm_status bigemm_check_args(const bigemm_desc* desc, int64_t M, int64_t N, i
                                 const void* Y, int64_t ldy, const void* X_scale, int64_t ldxs,
                                 const void* W_scale, int64_t ldws) {
   if (!desc) return BIGEMM_ERR_ARG;
-  return check(desc_kind(desc), M, N, K, X, ldx, W, ldw, Y, ldy, X_scale, ldxs, W_scale, ldws);
+  return check(desc_op(desc), M, N, K, X, ldx, W, ldw, Y, ldy, X_scale, ldxs, W_scale, ldws);
 }
 
 bigemm_status bigemm_create(const bigemm_desc* desc, bigemm_t* out) {
   if (!out) return BIGEMM_ERR_ARG;
   *out = nullptr;
   if (!desc) return BIGEMM_ERR_ARG;
-  const int kind = desc_kind(desc);
-  if (kind == 0) return BIGEMM_ERR_UNSUPPORTED;
+  const bigemm::Op op = desc_op(desc);
+  if (op.in == 0) return BIGEMM_ERR_UNSUPPORTED;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) {
     (void)hipGetLastError();
@@ -108,7 +116,7 @@ bigemm_status bigemm_create(const bigemm_desc* desc, bigemm_t* out) {
     return BIGEMM_ERR_UNSUPPORTED;
   bigemm_s* h = new (std::nothrow) bigemm_s;
   if (!h) return BIGEMM_ERR_NOMEM;
-  h->kind = kind;
+  h->op = op;
   h->device = dev;
   *out = h;
   return BIGEMM_OK;
@@ -123,7 +131,7 @@ bigemm_status bigemm_get_config(bigemm_t h, int32_t* bm, int32_t* bn, int32_t* b
   if (!h) return BIGEMM_ERR_ARG;
   if (bm) *bm = bigemm::kTileM;
   if (bn) *bn = bigemm::kTileN;
-  if (bk) *bk = h->kind == 1 ? bigemm::kTileKBf16 : bigemm::kTileKMx;
+  if (bk) *bk = (h->op.in == bigemm::kInBf16 || h->op.in == bigemm::kInF16) ? bigemm::kTileKBf16 : bigemm::kTileKMx;
   return BIGEMM_OK;
 }
 
@@ -131,14 +139,16 @@ bigemm_status bigemm_run(bigemm_t h, int64_t M, int64_t N, int64_t K, const void
                          const void* W, int64_t ldw, void* Y, int64_t ldy, const void* X_scale,
                          int64_t ldxs, const void* W_scale, int64_t ldws, void* stream) {
   if (!h) return BIGEMM_ERR_ARG;
-  const bigemm_status st = check(h->kind, M, N, K, X, ldx, W, ldw, Y, ldy, X_scale, ldxs, W_scale, ldws);
+  const bigemm_status st = check(h->op, M, N, K, X, ldx, W, ldw, Y, ldy, X_scale, ldxs, W_scale, ldws);
   if (st != BIGEMM_OK || M == 0) return st;
   hipError_t e;
-  if (h->kind == 1)
-    e = bigemm::launch_bf16(X, W, Y, M, N, K, ldx, ldw, ldy, (hipStream_t)stream);
-  else
-    e = bigemm::launch_mxfp8(X, W, Y, X_scale, W_scale, M, N, K, ldx, ldw, ldy, ldxs, ldws,
+  if (h->op.in == bigemm::kInMx)
+    e = bigemm::launch_mxfp8(h->op, X, W, Y, X_scale, W_scale, M, N, K, ldx, ldw, ldy, ldxs, ldws,
                              (hipStream_t)stream);
+  else if (h->op.in == bigemm::kInI8)
+    e = bigemm::launch_i8(X, W, Y, M, N, K, ldx, ldw, ldy, (hipStream_t)stream);
+  else
+    e = bigemm::launch_bf16(h->op, X, W, Y, M, N, K, ldx, ldw, ldy, (hipStream_t)stream);
   return e == hipSuccess ? BIGEMM_OK : BIGEMM_ERR_DEVICE;
 }
 

@@ -8,14 +8,24 @@ namespace bigemm {
 // The one tile configuration of each kernel.
 constexpr int kTileM = 128;
 constexpr int kTileN = 128;
-constexpr int kTileKBf16 = 64;
-constexpr int kTileKMx = 128;
+constexpr int kTileKBf16 = 64;   // bf16 and fp16 inputs
+constexpr int kTileKMx = 128;    // MXFP8 and int8 inputs
 
-hipError_t launch_bf16(const void* X, const void* W, void* Y, int64_t M, int64_t N, int64_t K,
+// Input families (the kernel that runs) and the output type (a bigemm_dtype value).
+enum { kInBf16 = 1, kInF16 = 2, kInMx = 3, kInI8 = 4 };
+struct Op {
+  int32_t in;
+  int32_t out;
+};
+
+hipError_t launch_bf16(Op op, const void* X, const void* W, void* Y, int64_t M, int64_t N, int64_t K,
                        int64_t ldx, int64_t ldw, int64_t ldy, hipStream_t stream);
 
-hipError_t launch_mxfp8(const void* X, const void* W, void* Y, const void* XS, const void* WS,
+hipError_t launch_mxfp8(Op op, const void* X, const void* W, void* Y, const void* XS, const void* WS,
                         int64_t M, int64_t N, int64_t K, int64_t ldx, int64_t ldw, int64_t ldy,
                         int64_t ldxs, int64_t ldws, hipStream_t stream);
+
+hipError_t launch_i8(const void* X, const void* W, void* Y, int64_t M, int64_t N, int64_t K,
+                     int64_t ldx, int64_t ldw, int64_t ldy, hipStream_t stream);
 
 }  // namespace bigemm

@@ -106,6 +106,38 @@ __device__ __forceinline__ int swz_w8(int k) { return k & 7; }
 #define BIGEMM_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
 #define BIGEMM_BARRIER() asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory")
 
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+// binary32 -> bfloat16, round to nearest, ties to even (add half an ulp of the
+// 16 dropped bits, plus one when the kept part is odd, then truncate). A NaN
+// keeps its sign and top payload bits and gets the quiet bit (bit 6) set.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(uint32_t u) {
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x0040u;
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Store one output element at element index e of the tile-relative buffer
+// (out-of-range e is the kOob sentinel and is dropped): the raw 32-bit
+// accumulator (fp32 or int32), or its bf16 rounding.
+template <bool kOutBf16>
+__device__ __forceinline__ void store_out(__amdgpu_buffer_rsrc_t ry, bool ok, uint32_t e, uint32_t bits) {
+  if (kOutBf16) {
+    const uint32_t o = ok ? e * 2 : kOob;
+    __builtin_amdgcn_raw_buffer_store_b16((unsigned short)f32_to_bf16_rne(bits), ry, o, 0, 0);
+  } else {
+    const uint32_t o = ok ? e * 4 : kOob;
+    __builtin_amdgcn_raw_buffer_store_b32(bits, ry, o, 0, 0);
+  }
+}
+
+// 32x32x16 MFMA on 16-bit inputs: bf16 or fp16 bit patterns (8 per lane).
+template <bool kF16>
+__device__ __forceinline__ f32x16 mfma_16bit(i32x4 a, i32x4 b, f32x16 c) {
+  if (kF16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
 // ------------------------------------------------------------------------ bf16
 //
 // K block 64, MFMA 32x32x16 bf16, fp32 accumulate. 512 threads: 8 waves in a
@@ -122,9 +154,10 @@ constexpr int kThreadsBf16 = 512;
 constexpr int kStagesBf16 = BIGEMM_BF16_STAGES;
 static_assert(kStagesBf16 >= 3 && kStagesBf16 <= 5, "LDS holds 3 to 5 stages of 32 KiB");
 
+template <bool kF16, bool kOutBf16>
 __global__ __launch_bounds__(kThreadsBf16, 1)
 void bigemm_bf16_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
-                        float* __restrict__ Y, int M, int N, int K,
+                        void* __restrict__ Y, int M, int N, int K,
                         int64_t ldx, int64_t ldw, int64_t ldy, int tiles_m, int tiles_n) {
   // One LDS array per pipeline stage: distinct objects let the compiler see
   // that reads of one stage do not depend on the loads in flight into another.
@@ -223,16 +256,15 @@ void bigemm_bf16_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
     issue(kb + kStagesBf16 - 1, refill);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      bf16x8 a[2];
+      i32x4 a[2];
 #pragma unroll
-      for (int f = 0; f < 2; ++f) a[f] = *LDS(const bf16x8, st + a_addr[f][kk]);
+      for (int f = 0; f < 2; ++f) a[f] = *LDS(const i32x4, st + a_addr[f][kk]);
       const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS(i16x4, st + b_addr[kk][0]));
       const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS(i16x4, st + b_addr[kk][1]));
       const i32x2 lo2 = __builtin_bit_cast(i32x2, lo), hi2 = __builtin_bit_cast(i32x2, hi);
-      const i32x4 v = {lo2[0], lo2[1], hi2[0], hi2[1]};
-      const bf16x8 b = __builtin_bit_cast(bf16x8, v);
+      const i32x4 b = {lo2[0], lo2[1], hi2[0], hi2[1]};
 #pragma unroll
-      for (int f = 0; f < 2; ++f) acc[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[f], b, acc[f], 0, 0, 0);
+      for (int f = 0; f < 2; ++f) acc[f] = mfma_16bit<kF16>(a[f], b, acc[f]);
     }
   };
 
@@ -261,19 +293,21 @@ void bigemm_bf16_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
   }
   BIGEMM_WAIT_VMCNT(0);  // no LDS-DMA load may outlive the workgroup
 
-  // Epilogue: plain fp32 stores, masked through the buffer range check.
-  const __amdgpu_buffer_rsrc_t ry = make_rsrc(Y + (int64_t)row0 * ldy + col0);
+  // Epilogue: plain stores (fp32, or its bf16 rounding), masked through the
+  // buffer range check.
+  const __amdgpu_buffer_rsrc_t ry =
+      make_rsrc((uint8_t*)Y + ((int64_t)row0 * ldy + col0) * (kOutBf16 ? 2 : 4));
 #pragma unroll
   for (int f = 0; f < 2; ++f)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int rl = wm * 64 + f * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
       const int cl = wn * 32 + (lane & 31);
-      const uint32_t o = (rl < rows_valid && cl < cols_valid) ? (uint32_t)((rl * ldy + cl) * 4) : kOob;
       // Copy the element out first: bit-casting an ext_vector element
       // expression directly reads element 0 with this compiler.
       const float v = acc[f][r];
-      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), ry, o, 0, 0);
+      store_out<kOutBf16>(ry, rl < rows_valid && cl < cols_valid, (uint32_t)(rl * ldy + cl),
+                          __builtin_bit_cast(uint32_t, v));
     }
 }
 
@@ -289,10 +323,10 @@ constexpr int kBkMx = 128;
 constexpr int kStagesMx = BIGEMM_MX_STAGES;
 static_assert(kStagesMx >= 3 && kStagesMx <= 4, "LDS holds 3 or 4 stages of 32 KiB");
 
-template <bool kVecXs>
+template <bool kVecXs, bool kOutBf16>
 __global__ __launch_bounds__(kThreads, 1)
 void bigemm_mxfp8_kernel(const uint8_t* __restrict__ X, const uint8_t* __restrict__ W,
-                         float* __restrict__ Y, const uint8_t* __restrict__ XS,
+                         void* __restrict__ Y, const uint8_t* __restrict__ XS,
                          const uint8_t* __restrict__ WS, int M, int N, int K,
                          int64_t ldx, int64_t ldw, int64_t ldy, int64_t ldxs, int64_t ldws,
                          int tiles_m, int tiles_n) {
@@ -538,6 +572,162 @@ void bigemm_mxfp8_kernel(const uint8_t* __restrict__ X, const uint8_t* __restric
   }
   BIGEMM_WAIT_VMCNT(0);  // no LDS-DMA load may outlive the workgroup
 
+  const __amdgpu_buffer_rsrc_t ry =
+      make_rsrc((uint8_t*)Y + ((int64_t)row0 * ldy + col0) * (kOutBf16 ? 2 : 4));
+#pragma unroll
+  for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < 2; ++fn)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int rl = wm * 64 + fm * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        const int cl = wn * 64 + fn * 32 + (lane & 31);
+        // Copy the element out first: bit-casting an ext_vector element
+        // expression directly reads element 0 with this compiler.
+        const float v = acc[fm][fn][r];
+        store_out<kOutBf16>(ry, rl < rows_valid && cl < cols_valid, (uint32_t)(rl * ldy + cl),
+                            __builtin_bit_cast(uint32_t, v));
+      }
+}
+
+// ------------------------------------------------------------------------ int8
+//
+// The MXFP8 skeleton without scales: K block 128, X tile 128 x 128 bytes and W
+// tile 128 x 128 bytes per stage, 4 waves of 64 x 64 outputs, three stages.
+// MFMA 32x32x32 int8 with int32 accumulate: lane l holds row (column) l%32 and
+// the 16 consecutive K values 16*(l/32) .. +15 of a 32-wide step (any K order
+// shared by both operands gives the same exact integer sum). Integer addition
+// is associative, so the result is independent of the summation order; the
+// kernel still walks K in one fixed order like the others.
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+constexpr int kBkI8 = 128;
+constexpr int kStagesI8 = 3;
+
+__global__ __launch_bounds__(kThreads, 1)
+void bigemm_i8_kernel(const uint8_t* __restrict__ X, const uint8_t* __restrict__ W,
+                      int32_t* __restrict__ Y, int M, int N, int K,
+                      int64_t ldx, int64_t ldw, int64_t ldy, int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(1024))) uint8_t stage0[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t stage1[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t stage2[kStageBytes];
+  uint8_t* const stg[3] = {stage0, stage1, stage2};
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  int tm, tn;
+  tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+  const int row0 = tm * 128;
+  const int col0 = tn * 128;
+  const int rows_valid = min(128, M - row0);
+  const int cols_valid = min(128, N - col0);
+  const int nkb = (K + kBkI8 - 1) / kBkI8;
+
+  // Load assignment as in the MXFP8 kernel: chunk p = i*256 + tid.
+  uint32_t xoff[4], woff[4];
+  int xk[4], wk[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int p = i * kThreads + tid;
+    const int r = p >> 3, s = p & 7, c = s ^ swz_x(r);
+    xoff[i] = (uint32_t)(r * ldx + c * 16);
+    xk[i] = r < rows_valid ? c * 16 : 0x7FFFFFFF;
+    const int kr = p >> 3, cw = s ^ swz_w8(kr);
+    woff[i] = (uint32_t)(kr * ldw + cw * 16);
+    wk[i] = cw * 16 < cols_valid ? kr : 0x7FFFFFFF;
+  }
+  const uint8_t* Xt = X + (int64_t)row0 * ldx;
+  const uint8_t* Wt = W + col0;
+
+  // The 8 LDS-DMA loads of K block kb (blocks past the end load zeros).
+  auto issue = [&](int kb, uint8_t* stage) {
+    const bool live = kb < nkb;
+    const int k0 = live ? kb * kBkI8 : 0;
+    const int kleft = live ? K - k0 : 0;
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(Xt + k0);
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(Wt + (int64_t)k0 * ldw);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t o = xk[i] < kleft ? xoff[i] : kOob;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, LDS(void, stage + i * 4096 + wave * 1024), 16, o, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t o = wk[i] < kleft ? woff[i] : kOob;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, LDS(void, stage + kTileBytes + i * 4096 + wave * 1024), 16, o,
+                                                0, 0, 0);
+    }
+  };
+
+  // Fragment addresses per 32-wide K step kk: A one 16-byte read, B two
+  // transposing 8-byte reads (K values 0..7 and 8..15 of the lane's 16).
+  const int wm = wave >> 1, wn = wave & 1;
+  int a_addr[2][4];      // [f][kk]
+  int b_addr[2][4][2];   // [f][kk][half]
+#pragma unroll
+  for (int f = 0; f < 2; ++f) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int r = wm * 64 + f * 32 + (lane & 31);
+      const int c = kk * 2 + (lane >> 5);
+      a_addr[f][kk] = r * 128 + ((c ^ swz_x(r)) << 4);
+      const int G = lane >> 4, j = lane & 15;
+      const int col = wn * 64 + f * 32 + (G & 1) * 16 + (j & 1) * 8;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int kr = kk * 32 + (G >> 1) * 16 + h * 8 + (j >> 1);
+        b_addr[f][kk][h] = kTileBytes + kr * 128 + (((col >> 4) ^ swz_w8(kr)) << 4) + (col & 15);
+      }
+    }
+  }
+
+  i32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = i32x16{};
+
+  // One K block: wait for this stage (the next block's 8 loads may stay in
+  // flight), refill the stage read in the previous block, MFMA chain kk ascending.
+  auto step = [&](int kb, const uint8_t* st, uint8_t* refill) {
+    BIGEMM_WAIT_VMCNT(8 * (kStagesI8 - 2));
+    BIGEMM_BARRIER();
+    issue(kb + kStagesI8 - 1, refill);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      i32x4 a[2], b[2];
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        a[f] = *LDS(const i32x4, st + a_addr[f][kk]);
+        const i32x2 lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32(LDS(i32x2, st + b_addr[f][kk][0]));
+        const i32x2 hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32(LDS(i32x2, st + b_addr[f][kk][1]));
+        b[f] = i32x4{lo[0], lo[1], hi[0], hi[1]};
+      }
+#pragma unroll
+      for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < 2; ++fn)
+          acc[fm][fn] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[fm], b[fn], acc[fm][fn], 0, 0, 0);
+    }
+  };
+
+  issue(nkb, stg[kStagesI8 - 1]);
+#pragma unroll
+  for (int s2 = 0; s2 < kStagesI8 - 1; ++s2) issue(s2, stg[s2]);
+  for (int kb = 0;;) {
+    bool done = false;
+#pragma unroll
+    for (int u = 0; u < 2 * kStagesI8; ++u) {
+      step(kb, stg[u % kStagesI8], stg[(u + kStagesI8 - 1) % kStagesI8]);
+      if (++kb == nkb) {
+        done = true;
+        break;
+      }
+    }
+    if (done) break;
+  }
+  BIGEMM_WAIT_VMCNT(0);  // no LDS-DMA load may outlive the workgroup
+
   const __amdgpu_buffer_rsrc_t ry = make_rsrc(Y + (int64_t)row0 * ldy + col0);
 #pragma unroll
   for (int fm = 0; fm < 2; ++fm)
@@ -547,27 +737,26 @@ void bigemm_mxfp8_kernel(const uint8_t* __restrict__ X, const uint8_t* __restric
       for (int r = 0; r < 16; ++r) {
         const int rl = wm * 64 + fm * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
         const int cl = wn * 64 + fn * 32 + (lane & 31);
-        const uint32_t o = (rl < rows_valid && cl < cols_valid) ? (uint32_t)((rl * ldy + cl) * 4) : kOob;
-        // Copy the element out first: bit-casting an ext_vector element
-        // expression directly reads element 0 with this compiler.
-        const float v = acc[fm][fn][r];
-        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), ry, o, 0, 0);
+        const int v = acc[fm][fn][r];
+        store_out<false>(ry, rl < rows_valid && cl < cols_valid, (uint32_t)(rl * ldy + cl), (uint32_t)v);
       }
 }
 
 // ------------------------------------------------------------------ launchers
 
-hipError_t launch_bf16(const void* X, const void* W, void* Y, int64_t M, int64_t N, int64_t K,
+hipError_t launch_bf16(Op op, const void* X, const void* W, void* Y, int64_t M, int64_t N, int64_t K,
                        int64_t ldx, int64_t ldw, int64_t ldy, hipStream_t stream) {
   const int tiles_m = (int)((M + 127) / 128);
   const int tiles_n = (int)((N + 127) / 128);
-  hipLaunchKernelGGL(bigemm_bf16_kernel, dim3(tiles_m * tiles_n), dim3(kThreadsBf16), 0, stream,
-                     (const uint16_t*)X, (const uint16_t*)W, (float*)Y, (int)M, (int)N, (int)K,
-                     ldx, ldw, ldy, tiles_m, tiles_n);
+  const bool f16 = op.in == kInF16, obf = op.out == 1 /* BIGEMM_BF16 */;
+  auto kern = f16 ? (obf ? bigemm_bf16_kernel<true, true> : bigemm_bf16_kernel<true, false>)
+                  : (obf ? bigemm_bf16_kernel<false, true> : bigemm_bf16_kernel<false, false>);
+  hipLaunchKernelGGL(kern, dim3(tiles_m * tiles_n), dim3(kThreadsBf16), 0, stream, (const uint16_t*)X,
+                     (const uint16_t*)W, Y, (int)M, (int)N, (int)K, ldx, ldw, ldy, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
-hipError_t launch_mxfp8(const void* X, const void* W, void* Y, const void* XS, const void* WS,
+hipError_t launch_mxfp8(Op op, const void* X, const void* W, void* Y, const void* XS, const void* WS,
                         int64_t M, int64_t N, int64_t K, int64_t ldx, int64_t ldw, int64_t ldy,
                         int64_t ldxs, int64_t ldws, hipStream_t stream) {
   const int tiles_m = (int)((M + 127) / 128);
@@ -575,11 +764,21 @@ hipError_t launch_mxfp8(const void* X, const void* W, void* Y, const void* XS, c
   // The X-scale load path depends on the scale layout and K only (never on M);
   // both paths read the same scale values.
   const bool vec_xs = K % 512 == 0 && ((uintptr_t)XS & 15) == 0 && ldxs % 16 == 0;
-  hipLaunchKernelGGL(vec_xs ? bigemm_mxfp8_kernel<true> : bigemm_mxfp8_kernel<false>, dim3(tiles_m * tiles_n),
-                     dim3(kThreads), 0, stream,
-                     (const uint8_t*)X, (const uint8_t*)W, (float*)Y, (const uint8_t*)XS,
-                     (const uint8_t*)WS, (int)M, (int)N, (int)K, ldx, ldw, ldy, ldxs, ldws,
-                     tiles_m, tiles_n);
+  const bool obf = op.out == 1 /* BIGEMM_BF16 */;
+  auto kern = vec_xs ? (obf ? bigemm_mxfp8_kernel<true, true> : bigemm_mxfp8_kernel<true, false>)
+                     : (obf ? bigemm_mxfp8_kernel<false, true> : bigemm_mxfp8_kernel<false, false>);
+  hipLaunchKernelGGL(kern, dim3(tiles_m * tiles_n), dim3(kThreads), 0, stream, (const uint8_t*)X,
+                     (const uint8_t*)W, Y, (const uint8_t*)XS, (const uint8_t*)WS, (int)M, (int)N, (int)K, ldx, ldw,
+                     ldy, ldxs, ldws, tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
+hipError_t launch_i8(const void* X, const void* W, void* Y, int64_t M, int64_t N, int64_t K, int64_t ldx,
+                     int64_t ldw, int64_t ldy, hipStream_t stream) {
+  const int tiles_m = (int)((M + 127) / 128);
+  const int tiles_n = (int)((N + 127) / 128);
+  hipLaunchKernelGGL(bigemm_i8_kernel, dim3(tiles_m * tiles_n), dim3(kThreads), 0, stream, (const uint8_t*)X,
+                     (const uint8_t*)W, (int32_t*)Y, (int)M, (int)N, (int)K, ldx, ldw, ldy, tiles_m, tiles_n);
   return hipGetLastError();
 }
 

@@ -9,9 +9,9 @@ sums for tiny shapes).
 What it computes (the nondeterminism blog, section on batch-invariant matrix
 multiplication: C_ij = sum_k A_ik B_kj) and how closely the GPU must agree:
 
-* ``gemm_bf16`` / ``gemm_mxfp8`` return the fp64-accumulated product of the
-  exactly decoded operands, summed with k ascending, and
-  S_ij = sum_k |x_ik w_kj|.
+* ``gemm_bf16`` / ``gemm_f16`` / ``gemm_mxfp8`` return the fp64-accumulated
+  product of the exactly decoded operands, summed with k ascending, and
+  S_ij = sum_k |x_ik w_kj|. ``gemm_i8`` returns the exact int64 product.
 * ``max_normalized_error`` is the parity metric: max_ij |y_gpu - y| / S_ij
   (elements with S_ij = 0 must be exactly 0). Any fp32 accumulation of the
   exact products, in any order, satisfies e <= gamma_{K-1}(fp32) by the blog's
@@ -31,6 +31,9 @@ SOURCE = os.path.join(_HERE, "oracle.c")
 LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
 PARITY_TOL = 2e-3  # max normalised error allowed for bf16/MXFP8 inputs with fp32 accumulation
+# bf16 output: the fp32 result is rounded once to 8 significant bits, adding at
+# most u_bf16 = 2^-8 of |y| <= S(1 + gamma) to the accumulation error.
+PARITY_TOL_BF16_OUT = PARITY_TOL + 2.0 ** -8 * (1 + PARITY_TOL)
 
 _i64 = ctypes.c_int64
 _p = ctypes.c_void_p
@@ -62,6 +65,12 @@ class Oracle:
         lib.oracle_decode_e4m3.argtypes = [ctypes.c_uint8]
         lib.oracle_decode_e8m0.restype = ctypes.c_double
         lib.oracle_decode_e8m0.argtypes = [ctypes.c_uint8]
+        lib.oracle_decode_f16.restype = ctypes.c_double
+        lib.oracle_decode_f16.argtypes = [ctypes.c_uint16]
+        lib.oracle_gemm_f16.restype = ctypes.c_int
+        lib.oracle_gemm_f16.argtypes = [_i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i64]
+        lib.oracle_gemm_i8.restype = ctypes.c_int
+        lib.oracle_gemm_i8.argtypes = [_i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64]
         lib.oracle_gemm_f64.restype = ctypes.c_int
         lib.oracle_gemm_f64.argtypes = [_i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i64]
         lib.oracle_gemm_bf16.restype = ctypes.c_int
@@ -92,6 +101,39 @@ class Oracle:
         c = np.asarray(codes, dtype=np.uint8)
         f = self.lib.oracle_decode_e8m0
         return np.array([f(int(v)) for v in c.ravel()], dtype=np.float64).reshape(c.shape)
+
+    def decode_f16(self, bits) -> np.ndarray:
+        b = np.asarray(bits, dtype=np.uint16)
+        f = self.lib.oracle_decode_f16
+        return np.array([f(int(v)) for v in b.ravel()], dtype=np.float64).reshape(b.shape)
+
+    def gemm_f16(self, X, W, want_s: bool = True):
+        """fp16 X[M,K] (uint16 bits) times fp16 W[K,N]; returns (Y, S) in fp64."""
+        X = np.ascontiguousarray(X, dtype=np.uint16)
+        W = np.ascontiguousarray(W, dtype=np.uint16)
+        M, K = X.shape
+        K2, N = W.shape
+        assert K == K2, (X.shape, W.shape)
+        Y = np.empty((M, N), dtype=np.float64)
+        S = np.empty((M, N), dtype=np.float64) if want_s else None
+        rc = self.lib.oracle_gemm_f16(M, N, K, _ptr(X), K, _ptr(W), N, _ptr(Y), N,
+                                      _ptr(S) if want_s else None, N)
+        if rc != 0:
+            raise RuntimeError(f"oracle_gemm_f16 failed rc={rc}")
+        return (Y, S) if want_s else Y
+
+    def gemm_i8(self, X, W) -> np.ndarray:
+        """int8 X[M,K] times int8 W[K,N], exact, as int64."""
+        X = np.ascontiguousarray(X, dtype=np.int8)
+        W = np.ascontiguousarray(W, dtype=np.int8)
+        M, K = X.shape
+        K2, N = W.shape
+        assert K == K2, (X.shape, W.shape)
+        Y = np.empty((M, N), dtype=np.int64)
+        rc = self.lib.oracle_gemm_i8(M, N, K, _ptr(X), K, _ptr(W), N, _ptr(Y), N)
+        if rc != 0:
+            raise RuntimeError(f"oracle_gemm_i8 failed rc={rc}")
+        return Y
 
     def gemm_f64(self, A, B, want_s: bool = True):
         """fp64 product of fp64 operands (the oracle's accumulation core)."""
@@ -171,6 +213,18 @@ def decode_e4m3(codes):
 
 def decode_e8m0(codes):
     return default().decode_e8m0(codes)
+
+
+def decode_f16(bits):
+    return default().decode_f16(bits)
+
+
+def gemm_f16(X, W, want_s: bool = True):
+    return default().gemm_f16(X, W, want_s)
+
+
+def gemm_i8(X, W):
+    return default().gemm_i8(X, W)
 
 
 def gemm_f64(A, B, want_s: bool = True):

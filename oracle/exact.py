@@ -41,6 +41,35 @@ def e8m0_value(code: int) -> float:
     return math.ldexp(1.0, code - 127)
 
 
+def f16_value(bits: int) -> float:
+    """IEEE binary16: sign, 5-bit exponent (bias 15), 10-bit mantissa; field 31 is inf / NaN."""
+    bits = int(bits) & 0xFFFF
+    sign = -1.0 if bits & 0x8000 else 1.0
+    e = (bits >> 10) & 0x1F
+    m = bits & 0x3FF
+    if e == 0x1F:
+        return float("nan") if m else sign * float("inf")
+    if e == 0:
+        return sign * (m / 1024.0) * 2.0 ** (-14)
+    return sign * (1.0 + m / 1024.0) * 2.0 ** (e - 15)
+
+
+def fsum_gemm_f16(X, W):
+    """Correctly rounded binary64 of the exact sums for fp16 bit patterns (products exact)."""
+    X = np.asarray(X)
+    W = np.asarray(W)
+    M, K = X.shape
+    N = W.shape[1]
+    Y = np.empty((M, N), dtype=np.float64)
+    S = np.empty((M, N), dtype=np.float64)
+    for i in range(M):
+        for j in range(N):
+            p = [f16_value(X[i, k]) * f16_value(W[k, j]) for k in range(K)]
+            Y[i, j] = math.fsum(p)
+            S[i, j] = math.fsum(abs(v) for v in p)
+    return Y, S
+
+
 def _products_bf16(X, W, i, j):
     K = X.shape[1]
     return [bf16_value(X[i, k]) * bf16_value(W[k, j]) for k in range(K)]  # exact in binary64

@@ -16,10 +16,14 @@
  *     path): 1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits, no
  *     infinities, S.1111.111 is NaN, exponent field 0 is subnormal m/8*2^-6;
  *   - E8M0 (the MXFP8 block scale, one per 32 consecutive K elements): the
- *     byte e encodes 2^(e-127), 0xFF is NaN.
+ *     byte e encodes 2^(e-127), 0xFF is NaN;
+ *   - IEEE binary16: 1 sign bit, 5 exponent bits with bias 15, 10 mantissa
+ *     bits, exponent field 0 subnormal m/1024*2^-14, field 31 infinity / NaN;
+ *   - int8 operands are exact integers; their GEMM is accumulated exactly in
+ *     int64 (integer addition is associative: no order question arises).
  *
  * Every product is exact in binary64 (bf16*bf16 has at most 16 significant
- * bits; a scaled E4M3*E4M3 product has at most 8). The only rounding is the
+ * bits, fp16*fp16 at most 22; a scaled E4M3*E4M3 product has at most 8). The only rounding is the
  * binary64 accumulation, bounded by the blog's sequential-sum bound
  * (section "unit roundoff"): |s_hat - s| <= gamma_{K-1} * sum_k |x_ik w_kj|,
  * gamma_n = n u / (1 - n u), u = 2^-53.
@@ -69,6 +73,18 @@ double oracle_decode_e4m3(uint8_t code) {
 double oracle_decode_e8m0(uint8_t code) {
   if (code == 0xFF) return NAN;
   return ldexp(1.0, (int)code - 127);
+}
+
+/* IEEE binary16 from its definition (exponent bias 15, 10 mantissa bits). */
+double oracle_decode_f16(uint16_t bits) {
+  int s = bits >> 15;
+  int e = (bits >> 10) & 31;
+  int m = bits & 1023;
+  double v;
+  if (e == 31) v = m ? NAN : INFINITY;
+  else if (e == 0) v = ldexp((double)m, -24);           /* m/1024 * 2^(1-15) */
+  else v = ldexp((double)(1024 + m), e - 25);          /* (1 + m/1024) * 2^(e-15) */
+  return s ? -v : v;
 }
 
 static double e4m3_table[256];
@@ -133,6 +149,51 @@ int oracle_gemm_bf16(int64_t M, int64_t N, int64_t K,
   free(A);
   free(B);
   return rc;
+}
+
+/* ------------------------------------------------------------------- fp16 */
+
+int oracle_gemm_f16(int64_t M, int64_t N, int64_t K,
+                    const uint16_t* X, int64_t ldx,
+                    const uint16_t* W, int64_t ldw,
+                    double* Y, int64_t ldy, double* S, int64_t lds) {
+  if (M < 0 || N < 0 || K < 0 || ldx < K || ldw < N || ldy < N) return 1;
+  if (M == 0 || N == 0) return 0;
+  double* A = (double*)malloc(sizeof(double) * (size_t)(M * K + 1));
+  double* B = (double*)malloc(sizeof(double) * (size_t)(K * N + 1));
+  if (!A || !B) { free(A); free(B); return 2; }
+  for (int64_t i = 0; i < M; ++i)
+    for (int64_t k = 0; k < K; ++k) A[i * K + k] = oracle_decode_f16(X[i * ldx + k]);
+  for (int64_t k = 0; k < K; ++k)
+    for (int64_t j = 0; j < N; ++j) B[k * N + j] = oracle_decode_f16(W[k * ldw + j]);
+  int rc = oracle_gemm_f64(M, N, K, A, K, B, N, Y, ldy, S, lds);
+  free(A);
+  free(B);
+  return rc;
+}
+
+/* ------------------------------------------------------------------- int8 */
+
+/* Y_ij = sum_k X_ik W_kj in int64, k ascending (exact). */
+int oracle_gemm_i8(int64_t M, int64_t N, int64_t K,
+                   const int8_t* X, int64_t ldx,
+                   const int8_t* W, int64_t ldw,
+                   int64_t* Y, int64_t ldy) {
+  if (M < 0 || N < 0 || K < 0 || ldx < K || ldw < N || ldy < N) return 1;
+  if (M == 0 || N == 0) return 0;
+  if (!X || !W || !Y) return 1;
+  int64_t i;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (i = 0; i < M; ++i) {
+    int64_t* acc = Y + i * ldy;
+    for (int64_t j = 0; j < N; ++j) acc[j] = 0;
+    for (int64_t k = 0; k < K; ++k) {
+      const int64_t a = X[i * ldx + k];
+      const int8_t* wrow = W + k * ldw;
+      for (int64_t j = 0; j < N; ++j) acc[j] += a * (int64_t)wrow[j];
+    }
+  }
+  return 0;
 }
 
 /* ------------------------------------------------------------------ MXFP8 */

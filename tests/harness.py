@@ -26,7 +26,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from bigemm_inputs import (SEED_A, SEED_B, SEED_C, SCALE_SEED_OFFSET, normal_bf16, normal_e4m3,
+from bigemm_inputs import (SEED_A, SEED_B, SEED_C, SCALE_SEED_OFFSET, normal_bf16, normal_e4m3, normal_f16, int_i8,
                            e8m0_scales, e8m0_kvar_scales, row_positions)
 
 
@@ -49,6 +49,19 @@ def byte_diff(a, b) -> int:
 def rows_bf16(K: int, sigma: float = 1.0):
     def make(seed: int, n: int):
         return (normal_bf16(seed, (n, K), sigma),)
+    return make
+
+
+def rows_f16(K: int, sigma: float = 1.0):
+    """fp16 rows (numpy float16, so the GPU adapter can tell them from bf16 bits)."""
+    def make(seed: int, n: int):
+        return (normal_f16(seed, (n, K), sigma).view(np.float16),)
+    return make
+
+
+def rows_i8(K: int):
+    def make(seed: int, n: int):
+        return (int_i8(seed, (n, K)),)
     return make
 
 

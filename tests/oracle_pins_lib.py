@@ -14,8 +14,9 @@ Sources of truth used here, none of which is the oracle itself:
     non-associativity), which fixes the summation order;
   * the row-separability identity [A; B] C = [A C; B C] (blog, section on
     batch invariance);
-  * torch's CPU float8_e4m3fn / float8_e8m0fnu / bfloat16 conversions
-    (library routines) for the decoders;
+  * torch's CPU float8_e4m3fn / float8_e8m0fnu / bfloat16 conversions and
+    numpy's float16 (library routines) for the decoders;
+  * numpy's int64 matrix product (a library routine) for the exact int8 GEMM;
   * invariances of power-of-two block scaling (exact in binary64).
 """
 from __future__ import annotations
@@ -30,7 +31,7 @@ import torch
 import oracle
 from oracle import exact
 from bigemm_inputs import (normal_bf16, int_bf16, linspace_bf16, normal_e4m3, int_e4m3,
-                           e8m0_scales, f32_to_bf16_bits)
+                           e8m0_scales, f32_to_bf16_bits, normal_f16, int_f16, int_i8)
 
 U64 = 2.0 ** -53
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
@@ -270,6 +271,59 @@ def check_degenerate(orc: oracle.Oracle):
     assert Y.shape == (4, 1)
 
 
+def check_decoder_f16(orc: oracle.Oracle):
+    """All 65536 binary16 codes against numpy's float16 widening and against the
+    pure-Python decoder written from the format definition (NaN where both say NaN)."""
+    codes = np.arange(65536, dtype=np.uint16)
+    got = orc.decode_f16(codes)
+    lib = codes.view(np.float16).astype(np.float64)
+    dfn = np.array([exact.f16_value(int(c)) for c in codes])
+    for ref, name in ((lib, "numpy"), (dfn, "definition")):
+        same = (got == ref) | (np.isnan(got) & np.isnan(ref))
+        assert same.all(), f"fp16 decoder vs {name}: {int((~same).sum())} codes differ"
+    assert np.signbit(got[0x8000]) and got[0x8000] == 0.0
+    assert got[0x7C00] == np.inf and got[0x0001] == 2.0 ** -24 and got[0x7BFF] == 65504.0
+
+
+def check_bruteforce_f16(orc: oracle.Oracle, trials: int = 10):
+    rng = np.random.default_rng(2468)
+    for t in range(trials):
+        M, N, K = int(rng.integers(1, 6)), int(rng.integers(1, 6)), int(rng.integers(1, 65))
+        X = normal_f16(1100 + t, (M, K))
+        W = normal_f16(1200 + t, (K, N))
+        Y, S = orc.gemm_f16(X, W)
+        Yf, Sf = exact.fsum_gemm_f16(X, W)
+        g = oracle.gamma(max(K - 1, 0), U64)
+        _close(Y, Yf, g * Sf, f"f16 brute force M={M} N={N} K={K}")
+        _close(S, Sf, g * Sf, f"f16 S brute force M={M} N={N} K={K}")
+
+
+def check_integer_f16(orc: oracle.Oracle):
+    """Integer binary16 operands: the oracle must equal int64 arithmetic exactly."""
+    for (M, K, N, s) in [(5, 40, 19, 0), (2, 300, 3, 1), (6, 1, 7, 2)]:
+        X = int_f16(1300 + s, (M, K), -64, 64)
+        W = int_f16(1400 + s, (K, N), -64, 64)
+        Xi = X.view(np.float16).astype(np.int64)
+        Wi = W.view(np.float16).astype(np.int64)
+        Y = orc.gemm_f16(X, W, want_s=False)
+        assert np.array_equal(Y, (Xi @ Wi).astype(np.float64)), f"integer f16 {M}x{K}x{N}"
+
+
+def check_i8(orc: oracle.Oracle):
+    """int8 over the full range (-128 included): equal to numpy's int64 product, and to a
+    plain Python triple loop on a tiny case; non-square shapes expose transposes."""
+    for (M, K, N, s) in [(7, 96, 5, 0), (1, 16, 33, 1), (40, 512, 24, 2), (3, 3, 2, 3)]:
+        X = int_i8(1500 + s, (M, K))
+        W = int_i8(1600 + s, (K, N))
+        Y = orc.gemm_i8(X, W)
+        assert np.array_equal(Y, X.astype(np.int64) @ W.astype(np.int64)), f"i8 {M}x{K}x{N}"
+    X = np.array([[-128, 127, -1], [5, -128, 0]], dtype=np.int8)
+    W = np.array([[-128, 2], [127, -128], [3, 4]], dtype=np.int8)
+    want = [[sum(int(X[i, k]) * int(W[k, j]) for k in range(3)) for j in range(2)] for i in range(2)]
+    assert orc.gemm_i8(X, W).tolist() == want
+
+
 ALL_CHECKS = [check_sum_order, check_bruteforce_bf16, check_bruteforce_mx, check_integer_bf16,
               check_integer_mx, check_decoders, check_linspace_closed_form, check_linspace_bf16_row0,
-              check_row_separability, check_mx_equals_prescaled_bf16, check_scale_shift, check_degenerate]
+              check_row_separability, check_mx_equals_prescaled_bf16, check_scale_shift, check_degenerate,
+              check_decoder_f16, check_bruteforce_f16, check_integer_f16, check_i8]

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert bg.bigemm_abi_version() == 1
+    assert bg.bigemm_abi_version() == 2
     for s in range(5):
         assert bg.bigemm_status_str(s)
     assert "unknown" in bg.bigemm_status_str(99)
@@ -91,5 +91,32 @@ def test_check_args_mxfp8():
 
 def test_check_args_rejects_unsupported_descriptors():
     assert chk((bg.BIGEMM_BF16, bg.BIGEMM_E4M3, bg.BIGEMM_F32, 0), 4, 64, 64) == bg.BIGEMM_ERR_UNSUPPORTED
-    assert chk((bg.BIGEMM_BF16, bg.BIGEMM_BF16, bg.BIGEMM_BF16, 0), 4, 64, 64) == bg.BIGEMM_ERR_UNSUPPORTED
+    assert chk((bg.BIGEMM_BF16, bg.BIGEMM_F16, bg.BIGEMM_F32, 0), 4, 64, 64) == bg.BIGEMM_ERR_UNSUPPORTED
+    assert chk((bg.BIGEMM_BF16, bg.BIGEMM_BF16, bg.BIGEMM_I32, 0), 4, 64, 64) == bg.BIGEMM_ERR_UNSUPPORTED
+    assert chk((bg.BIGEMM_BF16, bg.BIGEMM_BF16, bg.BIGEMM_F16, 0), 4, 64, 64) == bg.BIGEMM_ERR_UNSUPPORTED
     assert chk((bg.BIGEMM_E4M3, bg.BIGEMM_E4M3, bg.BIGEMM_F32, 16), 4, 64, 64) == bg.BIGEMM_ERR_UNSUPPORTED
+    assert chk((bg.BIGEMM_I8, bg.BIGEMM_I8, bg.BIGEMM_F32, 0), 4, 64, 64) == bg.BIGEMM_ERR_UNSUPPORTED
+    assert chk((bg.BIGEMM_I8, bg.BIGEMM_I8, bg.BIGEMM_I32, 32), 4, 64, 64) == bg.BIGEMM_ERR_UNSUPPORTED
+
+
+F16 = (bg.BIGEMM_F16, bg.BIGEMM_F16, bg.BIGEMM_F32, 0)
+BF_OUT_BF = (bg.BIGEMM_BF16, bg.BIGEMM_BF16, bg.BIGEMM_BF16, 0)
+I8 = (bg.BIGEMM_I8, bg.BIGEMM_I8, bg.BIGEMM_I32, 0)
+
+
+def test_check_args_other_types():
+    # fp16 inputs follow the bf16 rules
+    assert chk(F16, 16, 64, 64) == bg.BIGEMM_OK
+    assert chk(F16, 16, 64, 12) == bg.BIGEMM_ERR_ARG
+    # bf16 output: rows of ldy * 2 bytes must be 16-byte aligned
+    assert chk(BF_OUT_BF, 16, 64, 64) == bg.BIGEMM_OK
+    assert chk(BF_OUT_BF, 16, 8, 64, ldy=8) == bg.BIGEMM_OK
+    assert chk(BF_OUT_BF, 16, 8, 64, ldy=12) == bg.BIGEMM_ERR_ARG
+    assert chk((bg.BIGEMM_E4M3, bg.BIGEMM_E4M3, bg.BIGEMM_BF16, 32), 16, 64, 128,
+               XS=A, ldxs=4, WS=A, ldws=64) == bg.BIGEMM_OK
+    # int8: K and N multiples of 16, int32 rows 16-byte aligned, no scales
+    assert chk(I8, 16, 64, 64) == bg.BIGEMM_OK
+    assert chk(I8, 16, 64, 24) == bg.BIGEMM_ERR_ARG
+    assert chk(I8, 16, 40, 64) == bg.BIGEMM_ERR_ARG
+    assert chk(I8, 16, 64, 64, ldy=66) == bg.BIGEMM_ERR_ARG
+    assert chk(I8, 16, 64, 64, XS=A, ldxs=2) == bg.BIGEMM_ERR_ARG

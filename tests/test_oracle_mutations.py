@@ -26,6 +26,13 @@ MUTATIONS = [
     ("e8m0_bias", "return ldexp(1.0, (int)code - 127);", "return ldexp(1.0, (int)code - 126);"),
     ("x_scale_block", "oracle_decode_e8m0(XS[i * ldxs + k / 32])", "oracle_decode_e8m0(XS[i * ldxs + (k % 32) % ldxs])"),
     ("w_scale_column", "oracle_decode_e8m0(WS[(k / 32) * ldws + j])", "oracle_decode_e8m0(WS[(k / 32) * ldws + (N - 1 - j)])"),
+    ("f16_bias", "v = ldexp((double)(1024 + m), e - 25);", "v = ldexp((double)(1024 + m), e - 24);"),
+    ("f16_subnormal", "v = ldexp((double)m, -24);", "v = ldexp((double)m, -23);"),
+    ("f16_inf", "if (e == 31) v = m ? NAN : INFINITY;", "if (e == 31) v = m ? NAN : 65536.0;"),
+    ("i8_unsigned", "const int64_t a = X[i * ldx + k];", "const int64_t a = (uint8_t)X[i * ldx + k];"),
+    ("i8_w_columns", "acc[j] += a * (int64_t)wrow[j];", "acc[j] += a * (int64_t)wrow[N - 1 - j];"),
+    ("i8_drop_last_k", "for (int64_t k = 0; k < K; ++k) {\n      const int64_t a",
+     "for (int64_t k = 0; k < K - 1; ++k) {\n      const int64_t a"),
     ("x_scale_dropped", "A[i * K + k] = e4m3_table[X[i * ldx + k]] * oracle_decode_e8m0(XS[i * ldxs + k / 32]);",
      "A[i * K + k] = e4m3_table[X[i * ldx + k]];"),
 ]
