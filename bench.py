@@ -10,6 +10,8 @@ ABI with inputs resident in HBM. Also reported:
   last-level cache, so W is read from HBM), with achieved algorithmic HBM GB/s;
 * ``mxfp8_k4096_n4096``: the MXFP8 kernel (E4M3, K-varying E8M0 scales) at
   M = 1024 and 4096, against the dense FP8 MFMA peak (context, not the metric);
+* ``split_k_context``: the opt-in pinned-chunk split-K handle at small M (cold
+  LLC) and on the long-K workload, against the unsplit kernel (context);
 * ``invariance_byte_diffs``: every row of every sweep result compared with the
   same row of the M = 4096 result (must be 0);
 * ``roofline``: the kernel's algorithmic flops per launch over its average
@@ -165,6 +167,43 @@ def main():
             del Ws, Xs, Ys
             torch.cuda.empty_cache()
 
+    # ------------------------------------------------ opt-in split-K (context)
+    # The pinned-chunk split-K handle (not the measured kernel: it sums K in
+    # chunks of 512 then adds the chunk sums, so its bytes differ from the
+    # unsplit ones; still batch-invariant). Small M with cold-LLC rotation as
+    # in the sweep, and the long-K workload [1024,16384] . [16384,1024].
+    split = []
+    if not args.no_sweep:
+        kc = 512
+        for m in (1, 16, 64, 128, 256):
+            set_bytes = 2 * m * K + 2 * K * N + 4 * m * N
+            nsets = max(2, int(np.ceil(600e6 / set_bytes)))
+            Ws = [W] + [W.clone() for _ in range(nsets - 1)]
+            Ys = [torch.empty((m, N), dtype=torch.float32, device=dev) for _ in range(nsets)]
+            ws = torch.empty(bg.bigemm_workspace_size(bg._handle("bf16", 0, bg.BIGEMM_F32, kc), m, N, K),
+                             dtype=torch.uint8, device=dev)
+            for i in range(2 * nsets):
+                bg.mm(X[:m], Ws[i % nsets], out=Ys[i % nsets], k_chunk=kc, workspace=ws)
+            t = _events(torch, stream, lambda i: bg.mm(X[:m], Ws[i % nsets], out=Ys[i % nsets], k_chunk=kc,
+                                                       workspace=ws), max(20, 2 * nsets))
+            f = 2.0 * m * N * K
+            byts = 2 * m * K + 2 * K * N + 4 * m * N
+            split.append({"M": m, "K": K, "N": N, "k_chunk": kc, "us": round(t * 1e3, 2),
+                          "tflops": round(f / (t * 1e-3) / 1e12, 1),
+                          "hbm_gbs_algorithmic": round(byts / (t * 1e-3) / 1e9, 0), "cold_llc": True})
+            del Ws, Ys, ws
+        XL = torch.from_numpy(normal_bf16(SEED_X, (1024, 16384)).view(np.int16)).to(dev)
+        WL = torch.from_numpy(normal_bf16(SEED_W, (16384, 1024)).view(np.int16)).to(dev)
+        YL = torch.empty((1024, 1024), dtype=torch.float32, device=dev)
+        for kcl in (None, 2048):
+            for _ in range(3):
+                bg.mm(XL, WL, out=YL, k_chunk=kcl)
+            t = _events(torch, stream, lambda i: bg.mm(XL, WL, out=YL, k_chunk=kcl), 20)
+            split.append({"M": 1024, "K": 16384, "N": 1024, "k_chunk": kcl, "us": round(t * 1e3, 2),
+                          "tflops": round(2.0 * 1024 * 16384 * 1024 / (t * 1e-3) / 1e12, 1)})
+        del XL, WL, YL
+        torch.cuda.empty_cache()
+
     # ------------------------------------------------------- MXFP8 (context)
     mx = []
     if not args.no_sweep:
@@ -204,6 +243,7 @@ def main():
                      "traffic": measured_traffic() if M == 4096 else None},
         "m_sweep": sweep,
         "mxfp8_k4096_n4096": mx,
+        "split_k_context": split,
         "invariance_byte_diffs": diffs if sweep else None,
         "timed_wall_s": round(wall, 3),
     }

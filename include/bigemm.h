@@ -29,7 +29,7 @@
 extern "C" {
 #endif
 
-#define BIGEMM_ABI_VERSION 2
+#define BIGEMM_ABI_VERSION 3
 
 /* Exported entry points (the library is built with hidden visibility by default). */
 #if defined(__GNUC__)
@@ -122,7 +122,7 @@ BIGEMM_API bigemm_status bigemm_create(const bigemm_desc* desc, bigemm_t* out);
  * Y must not overlap X, W or the scales (not checked).
  *
  * Memory: all buffers are device memory owned by the caller. The library
- * allocates nothing per call (there is no split-K and hence no workspace).
+ * allocates nothing per call (this path has no split-K and hence no workspace).
  * Errors: BIGEMM_ERR_ARG as above; BIGEMM_ERR_DEVICE if the launch fails (the
  * HIP error is consumed). Concurrent calls on different streams are safe;
  * bigemm_destroy must not race with calls in flight.
@@ -134,6 +134,55 @@ BIGEMM_API bigemm_status bigemm_run(bigemm_t h, int64_t M, int64_t N, int64_t K,
                          const void* X_scale, int64_t ldxs,
                          const void* W_scale, int64_t ldws,
                          void* stream);
+
+/*
+ * Opt-in split-K handle (bf16 and fp16 inputs; fp32 or bf16 output): the
+ * pinned-split, ordered-merge deterministic split-K that the vLLM mHC pull
+ * request ("What") pins and that the nondeterminism blog (section on
+ * batch-invariant matmul) names as what breaks invariance when the split
+ * count follows the batch. Here the split count follows K only:
+ *   - the K range of every output tile is cut into ceil(K / k_chunk) chunks of
+ *     k_chunk values (k_chunk a positive multiple of 64, fixed per handle);
+ *   - one workgroup per (tile, chunk) accumulates its chunk in fp32 in the
+ *     same fixed order as bigemm_run and stores the chunk sum to the workspace;
+ *   - a second kernel adds the chunk sums in ascending chunk order (fp32),
+ *     then rounds once to bf16 for a bf16 output.
+ * Rows stay batch-invariant (nothing depends on M or on other rows), and the
+ * same call repeated gives the same bytes. The bytes differ from those of an
+ * unsplit handle whenever K > k_chunk (another fixed summation tree); with
+ * K <= k_chunk they are identical. The point is occupancy: at small M the
+ * unsplit kernel has ceil(M/128)*ceil(N/128) workgroups, this one that many
+ * times the chunk count.
+ * Returns BIGEMM_ERR_ARG for a bad k_chunk, BIGEMM_ERR_UNSUPPORTED for other
+ * descriptors or devices. Run it with bigemm_run_ws (bigemm_run returns
+ * BIGEMM_ERR_ARG on such a handle: it needs a workspace).
+ */
+BIGEMM_API bigemm_status bigemm_create_split_k(const bigemm_desc* desc, int32_t k_chunk, bigemm_t* out);
+
+/*
+ * Device workspace, in bytes, that bigemm_run_ws needs for this shape:
+ * ceil(K / k_chunk) * M * N * 4 for a split-K handle when K > k_chunk, 0
+ * otherwise (an unsplit handle, or a single chunk). Pure host function.
+ * BIGEMM_ERR_ARG for a NULL handle or output, or negative sizes.
+ */
+BIGEMM_API bigemm_status bigemm_workspace_size(bigemm_t h, int64_t M, int64_t N, int64_t K, uint64_t* bytes);
+
+/*
+ * bigemm_run with a caller-provided device workspace (16-byte aligned, at least
+ * bigemm_workspace_size bytes; it may be NULL when that size is 0). The
+ * library allocates nothing. The workspace is scratch for the duration of the
+ * call on `stream`: calls that share a workspace must be ordered (same stream)
+ * or they race. For a handle without split-K this is bigemm_run. Errors as
+ * bigemm_run, plus BIGEMM_ERR_ARG for a missing, misaligned or short workspace.
+ */
+BIGEMM_API bigemm_status bigemm_run_ws(bigemm_t h, int64_t M, int64_t N, int64_t K,
+                            const void* X, int64_t ldx,
+                            const void* W, int64_t ldw,
+                            void* Y, int64_t ldy,
+                            const void* X_scale, int64_t ldxs,
+                            const void* W_scale, int64_t ldws,
+                            void* workspace, uint64_t workspace_bytes,
+                            void* stream);
 
 /* Release a handle. NULL is accepted. */
 BIGEMM_API bigemm_status bigemm_destroy(bigemm_t h);

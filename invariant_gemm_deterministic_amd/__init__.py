@@ -83,6 +83,13 @@ def load():
                                           vp, i64, vp, i64, vp, i64]
         lib.bigemm_abi_version.restype = i32
         lib.bigemm_abi_version.argtypes = []
+        lib.bigemm_create_split_k.restype = ctypes.c_int
+        lib.bigemm_create_split_k.argtypes = [ctypes.POINTER(bigemm_desc), i32, ctypes.POINTER(vp)]
+        lib.bigemm_workspace_size.restype = ctypes.c_int
+        lib.bigemm_workspace_size.argtypes = [vp, i64, i64, i64, ctypes.POINTER(ctypes.c_uint64)]
+        lib.bigemm_run_ws.restype = ctypes.c_int
+        lib.bigemm_run_ws.argtypes = [vp, i64, i64, i64, vp, i64, vp, i64, vp, i64, vp, i64, vp, i64, vp,
+                                      ctypes.c_uint64, vp]
         _lib = lib
         return lib
 
@@ -114,6 +121,37 @@ def bigemm_create(x_type: int, w_type: int, y_type: int = BIGEMM_F32, scale_bloc
     if st != BIGEMM_OK:
         raise BigemmError(st, "bigemm_create")
     return int(h.value)
+
+
+def bigemm_create_split_k(x_type: int, w_type: int, y_type: int, k_chunk: int) -> int:
+    """Create an opt-in split-K handle (bf16 / fp16 inputs). Raises BigemmError."""
+    h = ctypes.c_void_p()
+    d = _desc(x_type, w_type, y_type, 0)
+    st = load().bigemm_create_split_k(ctypes.byref(d), int(k_chunk), ctypes.byref(h))
+    if st != BIGEMM_OK:
+        raise BigemmError(st, "bigemm_create_split_k")
+    return int(h.value)
+
+
+def bigemm_workspace_size(h: int, M: int, N: int, K: int) -> int:
+    n = ctypes.c_uint64()
+    st = load().bigemm_workspace_size(ctypes.c_void_p(h) if h else None, M, N, K, ctypes.byref(n))
+    if st != BIGEMM_OK:
+        raise BigemmError(st, "bigemm_workspace_size")
+    return int(n.value)
+
+
+def bigemm_run_ws(h: int, M: int, N: int, K: int, X: int, ldx: int, W: int, ldw: int, Y: int, ldy: int,
+                  X_scale: int = 0, ldxs: int = 0, W_scale: int = 0, ldws: int = 0, workspace: int = 0,
+                  workspace_bytes: int = 0, stream: int = 0, check: bool = True) -> int:
+    """bigemm_run with a caller-provided device workspace. Raises BigemmError unless check=False."""
+    st = load().bigemm_run_ws(ctypes.c_void_p(h) if h else None, M, N, K,
+                              X or None, ldx, W or None, ldw, Y or None, ldy,
+                              X_scale or None, ldxs, W_scale or None, ldws,
+                              workspace or None, int(workspace_bytes), stream or None)
+    if check and st != BIGEMM_OK:
+        raise BigemmError(st, "bigemm_run_ws")
+    return int(st)
 
 
 def bigemm_destroy(h: int) -> int:
@@ -158,16 +196,16 @@ _handles = {}
 _FAMILIES = {"bf16": (BIGEMM_BF16, 0), "f16": (BIGEMM_F16, 0), "mx": (BIGEMM_E4M3, 32), "i8": (BIGEMM_I8, 0)}
 
 
-def _handle(kind: str, device_index: int, y_type: int = BIGEMM_F32) -> int:
-    """One cached handle per (input family, output type, device)."""
+def _handle(kind: str, device_index: int, y_type: int = BIGEMM_F32, k_chunk: int = 0) -> int:
+    """One cached handle per (input family, output type, split-K chunk, device)."""
     import torch
 
-    key = (kind, y_type, device_index)
+    key = (kind, y_type, k_chunk, device_index)
     h = _handles.get(key)
     if h is None:
         t, sb = _FAMILIES[kind]
         with torch.cuda.device(device_index):
-            h = bigemm_create(t, t, y_type, sb)
+            h = bigemm_create_split_k(t, t, y_type, k_chunk) if k_chunk else bigemm_create(t, t, y_type, sb)
         _handles[key] = h
     return h
 
@@ -177,7 +215,8 @@ def _ld(t) -> int:
     return int(t.stride(0)) if t.shape[0] > 1 else int(t.shape[1])
 
 
-def mm(x, w, x_scale=None, w_scale=None, out=None, stream=None, out_dtype=None):
+def mm(x, w, x_scale=None, w_scale=None, out=None, stream=None, out_dtype=None, k_chunk=None,
+       workspace=None):
     """Y = X W on the GPU through libbigemm.
 
     bf16: ``x`` [M, K] and ``w`` [K, N] are torch.bfloat16 (or int16/uint16 bit
@@ -188,6 +227,9 @@ def mm(x, w, x_scale=None, w_scale=None, out=None, stream=None, out_dtype=None):
     Output: ``out`` if given (its dtype selects the output type), else a new
     [M, N] tensor of ``out_dtype`` (float32 or bfloat16 for floating inputs,
     default float32; int32 for int8).
+    ``k_chunk`` (bf16 / fp16 only) selects the opt-in split-K handle with that
+    K chunk; its workspace is ``workspace`` (a CUDA tensor of at least
+    ``bigemm_workspace_size`` bytes) or a fresh torch allocation.
     """
     import torch
 
@@ -231,6 +273,17 @@ def mm(x, w, x_scale=None, w_scale=None, out=None, stream=None, out_dtype=None):
         raise ValueError("out must be [M, N] with contiguous rows")
     if stream is None:
         stream = torch.cuda.current_stream(x.device).cuda_stream
+    if k_chunk:
+        if kind not in ("bf16", "f16"):
+            raise ValueError("split-K is provided for bf16 and fp16 inputs")
+        h = _handle(kind, dev, ytypes[out_dtype], int(k_chunk))
+        need = bigemm_workspace_size(h, M, N, K)
+        if workspace is None:
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+        ws_bytes = workspace.numel() * workspace.element_size()
+        bigemm_run_ws(h, M, N, K, x.data_ptr(), _ld(x), w.data_ptr(), _ld(w), out.data_ptr(), _ld(out),
+                      0, 0, 0, 0, workspace.data_ptr(), ws_bytes, stream)
+        return out
     h = _handle(kind, dev, ytypes[out_dtype])  # raises BigemmError for a combination not provided
     if mx:
         for t in (x_scale, w_scale):

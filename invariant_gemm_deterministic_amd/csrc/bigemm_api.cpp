@@ -18,6 +18,7 @@
 struct bigemm_s {
   bigemm::Op op;
   int device;
+  int32_t k_chunk;  // 0: no split-K
 };
 
 namespace {
@@ -70,6 +71,16 @@ bigemm_status check(bigemm::Op op, int64_t M, int64_t N, int64_t K, const void* 
   return BIGEMM_OK;
 }
 
+// The one fixed kernel of the handle's input family (no split).
+hipError_t launch_unsplit(bigemm::Op op, int64_t M, int64_t N, int64_t K, const void* X, int64_t ldx, const void* W,
+                          int64_t ldw, void* Y, int64_t ldy, const void* XS, int64_t ldxs, const void* WS,
+                          int64_t ldws, hipStream_t stream) {
+  if (op.in == bigemm::kInMx)
+    return bigemm::launch_mxfp8(op, X, W, Y, XS, WS, M, N, K, ldx, ldw, ldy, ldxs, ldws, stream);
+  if (op.in == bigemm::kInI8) return bigemm::launch_i8(X, W, Y, M, N, K, ldx, ldw, ldy, stream);
+  return bigemm::launch_bf16(op, X, W, Y, M, N, K, ldx, ldw, ldy, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -118,8 +129,54 @@ bigemm_status bigemm_create(const bigemm_desc* desc, bigemm_t* out) {
   if (!h) return BIGEMM_ERR_NOMEM;
   h->op = op;
   h->device = dev;
+  h->k_chunk = 0;
   *out = h;
   return BIGEMM_OK;
+}
+
+bigemm_status bigemm_create_split_k(const bigemm_desc* desc, int32_t k_chunk, bigemm_t* out) {
+  if (!out) return BIGEMM_ERR_ARG;
+  *out = nullptr;
+  if (!desc) return BIGEMM_ERR_ARG;
+  const bigemm::Op op = desc_op(desc);
+  if (op.in != bigemm::kInBf16 && op.in != bigemm::kInF16) return BIGEMM_ERR_UNSUPPORTED;
+  if (k_chunk < bigemm::kTileKBf16 || k_chunk % bigemm::kTileKBf16 != 0) return BIGEMM_ERR_ARG;
+  const bigemm_status st = bigemm_create(desc, out);
+  if (st != BIGEMM_OK) return st;
+  (*out)->k_chunk = k_chunk;
+  return BIGEMM_OK;
+}
+
+bigemm_status bigemm_workspace_size(bigemm_t h, int64_t M, int64_t N, int64_t K, uint64_t* bytes) {
+  if (!h || !bytes || M < 0 || N < 0 || K < 0) return BIGEMM_ERR_ARG;
+  *bytes = 0;
+  if (h->k_chunk > 0 && K > h->k_chunk) {
+    const uint64_t nsplit = (uint64_t)((K + h->k_chunk - 1) / h->k_chunk);
+    *bytes = nsplit * (uint64_t)M * (uint64_t)N * 4u;
+  }
+  return BIGEMM_OK;
+}
+
+bigemm_status bigemm_run_ws(bigemm_t h, int64_t M, int64_t N, int64_t K, const void* X, int64_t ldx,
+                            const void* W, int64_t ldw, void* Y, int64_t ldy, const void* X_scale,
+                            int64_t ldxs, const void* W_scale, int64_t ldws, void* workspace,
+                            uint64_t workspace_bytes, void* stream) {
+  if (!h) return BIGEMM_ERR_ARG;
+  const bigemm_status st = check(h->op, M, N, K, X, ldx, W, ldw, Y, ldy, X_scale, ldxs, W_scale, ldws);
+  if (st != BIGEMM_OK || M == 0) return st;
+  uint64_t need = 0;
+  bigemm_workspace_size(h, M, N, K, &need);
+  if (need == 0) {  // unsplit handle, or a single chunk: the one fixed kernel
+    const hipError_t e = launch_unsplit(h->op, M, N, K, X, ldx, W, ldw, Y, ldy, X_scale, ldxs, W_scale, ldws,
+                                        (hipStream_t)stream);
+    return e == hipSuccess ? BIGEMM_OK : BIGEMM_ERR_DEVICE;
+  }
+  if (!workspace || !aligned16(workspace) || workspace_bytes < need) return BIGEMM_ERR_ARG;
+  if ((K + h->k_chunk - 1) / h->k_chunk * ((M + 127) / 128) * ((N + 127) / 128) > INT32_MAX) return BIGEMM_ERR_ARG;
+  if (M * N > (int64_t)INT32_MAX * 4) return BIGEMM_ERR_ARG;  // merge grid
+  const hipError_t e = bigemm::launch_bf16_split(h->op, h->k_chunk, X, W, Y, workspace, M, N, K, ldx, ldw, ldy,
+                                                 (hipStream_t)stream);
+  return e == hipSuccess ? BIGEMM_OK : BIGEMM_ERR_DEVICE;
 }
 
 bigemm_status bigemm_destroy(bigemm_t h) {
@@ -139,16 +196,11 @@ bigemm_status bigemm_run(bigemm_t h, int64_t M, int64_t N, int64_t K, const void
                          const void* W, int64_t ldw, void* Y, int64_t ldy, const void* X_scale,
                          int64_t ldxs, const void* W_scale, int64_t ldws, void* stream) {
   if (!h) return BIGEMM_ERR_ARG;
+  if (h->k_chunk > 0) return BIGEMM_ERR_ARG;  // a split-K handle needs bigemm_run_ws
   const bigemm_status st = check(h->op, M, N, K, X, ldx, W, ldw, Y, ldy, X_scale, ldxs, W_scale, ldws);
   if (st != BIGEMM_OK || M == 0) return st;
-  hipError_t e;
-  if (h->op.in == bigemm::kInMx)
-    e = bigemm::launch_mxfp8(h->op, X, W, Y, X_scale, W_scale, M, N, K, ldx, ldw, ldy, ldxs, ldws,
-                             (hipStream_t)stream);
-  else if (h->op.in == bigemm::kInI8)
-    e = bigemm::launch_i8(X, W, Y, M, N, K, ldx, ldw, ldy, (hipStream_t)stream);
-  else
-    e = bigemm::launch_bf16(h->op, X, W, Y, M, N, K, ldx, ldw, ldy, (hipStream_t)stream);
+  const hipError_t e = launch_unsplit(h->op, M, N, K, X, ldx, W, ldw, Y, ldy, X_scale, ldxs, W_scale, ldws,
+                                      (hipStream_t)stream);
   return e == hipSuccess ? BIGEMM_OK : BIGEMM_ERR_DEVICE;
 }
 

@@ -75,16 +75,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
 // land on one XCD (its L2 then serves the shared X and W tiles), and walk the
 // tiles in groups of kGroupM tile-rows so that the XCD's concurrent tiles form
 // a compact block.
-__device__ __forceinline__ void tile_of(int bid, int nblocks, int tiles_m, int tiles_n, int& tm, int& tn) {
-  int t = bid;
+__device__ __forceinline__ int xcd_order(int bid, int nblocks) {
   const int per = nblocks / kXcds;
-  if (bid < per * kXcds) t = (bid % kXcds) * per + bid / kXcds;
+  return bid < per * kXcds ? (bid % kXcds) * per + bid / kXcds : bid;
+}
+__device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int& tm, int& tn) {
   const int group = t / (kGroupM * tiles_n);
   const int first_m = group * kGroupM;
   const int gm = min(tiles_m - first_m, kGroupM);
   const int in = t - group * kGroupM * tiles_n;
   tm = first_m + in % gm;
   tn = in / gm;
+}
+__device__ __forceinline__ void tile_of(int bid, int nblocks, int tiles_m, int tiles_n, int& tm, int& tn) {
+  tile_coords(xcd_order(bid, nblocks), tiles_m, tiles_n, tm, tn);
 }
 
 // 16-byte-chunk swizzle of a 128-byte-row operand tile (X tiles, and the MXFP8
@@ -154,11 +158,16 @@ constexpr int kThreadsBf16 = 512;
 constexpr int kStagesBf16 = BIGEMM_BF16_STAGES;
 static_assert(kStagesBf16 >= 3 && kStagesBf16 <= 5, "LDS holds 3 to 5 stages of 32 KiB");
 
-template <bool kF16, bool kOutBf16>
+// kSplit: the opt-in split-K variant. The grid is (chunk, tile) pairs; the
+// workgroup runs the same chain over the K blocks of its chunk only
+// (kb_per_split blocks) and stores the fp32 chunk sum at Y + chunk * split_stride.
+template <bool kF16, bool kOutBf16, bool kSplit>
 __global__ __launch_bounds__(kThreadsBf16, 1)
 void bigemm_bf16_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
                         void* __restrict__ Y, int M, int N, int K,
-                        int64_t ldx, int64_t ldw, int64_t ldy, int tiles_m, int tiles_n) {
+                        int64_t ldx, int64_t ldw, int64_t ldy, int tiles_m, int tiles_n,
+                        int kb_per_split, int64_t split_stride) {
+  static_assert(!(kSplit && kOutBf16), "chunk sums are stored in fp32");
   // One LDS array per pipeline stage: distinct objects let the compiler see
   // that reads of one stage do not depend on the loads in flight into another.
   __shared__ __attribute__((aligned(1024))) uint8_t stage0[kStageBytes];
@@ -172,12 +181,23 @@ void bigemm_bf16_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
   const int lane = tid & 63;
   const int wave = tid >> 6;
   int tm, tn;
-  tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+  int kb_first = 0;                               // first K block of this workgroup
+  int nkb = (K + kBkBf16 - 1) / kBkBf16;          // K blocks this workgroup accumulates
+  if (kSplit) {
+    const int ntiles = tiles_m * tiles_n;
+    const int t = xcd_order(blockIdx.x, gridDim.x);
+    const int chunk = t / ntiles;
+    tile_coords(t - chunk * ntiles, tiles_m, tiles_n, tm, tn);
+    kb_first = chunk * kb_per_split;
+    nkb = min(nkb - kb_first, kb_per_split);
+    Y = (float*)Y + chunk * split_stride;
+  } else {
+    tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+  }
   const int row0 = tm * 128;
   const int col0 = tn * 128;
   const int rows_valid = min(128, M - row0);
   const int cols_valid = min(128, N - col0);
-  const int nkb = (K + kBkBf16 - 1) / kBkBf16;
 
   // Load assignment: chunk p = i*512 + tid of each tile (i = 0, 1). With
   // buffer_load ... lds a wave's 64 lanes fill 1 KiB of LDS contiguously, so
@@ -197,8 +217,9 @@ void bigemm_bf16_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
     woff[i] = (uint32_t)((kr * ldw + cw * 8) * 2);
     wk[i] = cw * 8 < cols_valid ? kr : 0x7FFFFFFF;
   }
-  const uint16_t* Xt = X + (int64_t)row0 * ldx;
-  const uint16_t* Wt = W + col0;
+  const uint16_t* Xt = X + (int64_t)row0 * ldx + (int64_t)kb_first * kBkBf16;
+  const uint16_t* Wt = W + col0 + (int64_t)kb_first * kBkBf16 * ldw;
+  const int Kr = K - kb_first * kBkBf16;           // K remaining from this workgroup's first block
 
   // Issue the 4 LDS-DMA loads of K block kb into `stage`. A block past the
   // end (kb >= nkb) is still issued, entirely out of range: it loads zeros
@@ -207,7 +228,7 @@ void bigemm_bf16_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
   auto issue = [&](int kb, uint8_t* stage) {
     const bool live = kb < nkb;
     const int k0 = live ? kb * kBkBf16 : 0;
-    const int kleft = live ? K - k0 : 0;
+    const int kleft = live ? Kr - k0 : 0;
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(Xt + k0);
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(Wt + (int64_t)k0 * ldw);
 #pragma unroll
@@ -742,6 +763,43 @@ void bigemm_i8_kernel(const uint8_t* __restrict__ X, const uint8_t* __restrict__
       }
 }
 
+// ------------------------------------------------------------- split-K merge
+//
+// Y[i, j] = P[0][i, j] + P[1][i, j] + ... + P[S-1][i, j], added in ascending
+// chunk order in fp32 (then rounded once to bf16 for a bf16 output). One
+// thread per four consecutive outputs of a row; P is [S][M][N] fp32.
+template <bool kOutBf16>
+__global__ __launch_bounds__(256)
+void bigemm_split_merge_kernel(const float* __restrict__ P, void* __restrict__ Y, int M, int N, int64_t ldy,
+                               int nsplit, int64_t split_stride) {
+  const int nq = N / 4;
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (q >= (int64_t)M * nq) return;
+  const int i = (int)(q / nq);
+  const int j = (int)(q - (int64_t)i * nq) * 4;
+  const float* p = P + (int64_t)i * N + j;
+  float4 acc = *(const float4*)p;
+  for (int s = 1; s < nsplit; ++s) {
+    const float4 v = *(const float4*)(p + s * split_stride);
+    acc.x += v.x;
+    acc.y += v.y;
+    acc.z += v.z;
+    acc.w += v.w;
+  }
+  if (kOutBf16) {
+    const uint32_t b0 = f32_to_bf16_rne(__builtin_bit_cast(uint32_t, acc.x));
+    const uint32_t b1 = f32_to_bf16_rne(__builtin_bit_cast(uint32_t, acc.y));
+    const uint32_t b2 = f32_to_bf16_rne(__builtin_bit_cast(uint32_t, acc.z));
+    const uint32_t b3 = f32_to_bf16_rne(__builtin_bit_cast(uint32_t, acc.w));
+    uint2 packed;
+    packed.x = b0 | (b1 << 16);
+    packed.y = b2 | (b3 << 16);
+    *(uint2*)((uint16_t*)Y + (int64_t)i * ldy + j) = packed;
+  } else {
+    *(float4*)((float*)Y + (int64_t)i * ldy + j) = acc;
+  }
+}
+
 // ------------------------------------------------------------------ launchers
 
 hipError_t launch_bf16(Op op, const void* X, const void* W, void* Y, int64_t M, int64_t N, int64_t K,
@@ -749,10 +807,30 @@ hipError_t launch_bf16(Op op, const void* X, const void* W, void* Y, int64_t M, 
   const int tiles_m = (int)((M + 127) / 128);
   const int tiles_n = (int)((N + 127) / 128);
   const bool f16 = op.in == kInF16, obf = op.out == 1 /* BIGEMM_BF16 */;
-  auto kern = f16 ? (obf ? bigemm_bf16_kernel<true, true> : bigemm_bf16_kernel<true, false>)
-                  : (obf ? bigemm_bf16_kernel<false, true> : bigemm_bf16_kernel<false, false>);
+  auto kern = f16 ? (obf ? bigemm_bf16_kernel<true, true, false> : bigemm_bf16_kernel<true, false, false>)
+                  : (obf ? bigemm_bf16_kernel<false, true, false> : bigemm_bf16_kernel<false, false, false>);
   hipLaunchKernelGGL(kern, dim3(tiles_m * tiles_n), dim3(kThreadsBf16), 0, stream, (const uint16_t*)X,
-                     (const uint16_t*)W, Y, (int)M, (int)N, (int)K, ldx, ldw, ldy, tiles_m, tiles_n);
+                     (const uint16_t*)W, Y, (int)M, (int)N, (int)K, ldx, ldw, ldy, tiles_m, tiles_n, 0, (int64_t)0);
+  return hipGetLastError();
+}
+
+hipError_t launch_bf16_split(Op op, int32_t k_chunk, const void* X, const void* W, void* Y, void* P, int64_t M,
+                             int64_t N, int64_t K, int64_t ldx, int64_t ldw, int64_t ldy, hipStream_t stream) {
+  const int tiles_m = (int)((M + 127) / 128);
+  const int tiles_n = (int)((N + 127) / 128);
+  const int nsplit = (int)((K + k_chunk - 1) / k_chunk);
+  const int64_t stride = M * N;
+  const bool f16 = op.in == kInF16, obf = op.out == 1 /* BIGEMM_BF16 */;
+  auto kern = f16 ? bigemm_bf16_kernel<true, false, true> : bigemm_bf16_kernel<false, false, true>;
+  hipLaunchKernelGGL(kern, dim3(tiles_m * tiles_n * nsplit), dim3(kThreadsBf16), 0, stream, (const uint16_t*)X,
+                     (const uint16_t*)W, P, (int)M, (int)N, (int)K, ldx, ldw, N, tiles_m, tiles_n,
+                     k_chunk / kBkBf16, stride);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t threads = M * (N / 4);
+  const int blocks = (int)((threads + 255) / 256);
+  hipLaunchKernelGGL(obf ? bigemm_split_merge_kernel<true> : bigemm_split_merge_kernel<false>, dim3(blocks),
+                     dim3(256), 0, stream, (const float*)P, Y, (int)M, (int)N, ldy, nsplit, stride);
   return hipGetLastError();
 }
 

@@ -22,7 +22,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     fns = declared_functions()
     for name in ("bigemm_create", "bigemm_run", "bigemm_destroy", "bigemm_status_str",
-                 "bigemm_get_config", "bigemm_check_args", "bigemm_abi_version"):
+                 "bigemm_get_config", "bigemm_check_args", "bigemm_abi_version",
+                 "bigemm_create_split_k", "bigemm_workspace_size", "bigemm_run_ws"):
         assert name in fns
 
 
@@ -33,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert bg.bigemm_abi_version() == 2
+    assert bg.bigemm_abi_version() == 3
     for s in range(5):
         assert bg.bigemm_status_str(s)
     assert "unknown" in bg.bigemm_status_str(99)
@@ -45,6 +46,10 @@ def test_null_handle_paths():
     assert bg.bigemm_run(0, 1, 8, 8, A, 8, A, 8, A, 8, check=False) == bg.BIGEMM_ERR_ARG
     assert lib.bigemm_get_config(None, None, None, None) == bg.BIGEMM_ERR_ARG
     assert lib.bigemm_create(None, None) == bg.BIGEMM_ERR_ARG
+    assert lib.bigemm_create_split_k(None, 512, None) == bg.BIGEMM_ERR_ARG
+    assert bg.bigemm_run_ws(0, 1, 8, 8, A, 8, A, 8, A, 8, check=False) == bg.BIGEMM_ERR_ARG
+    n = ctypes.c_uint64()
+    assert lib.bigemm_workspace_size(None, 1, 8, 8, ctypes.byref(n)) == bg.BIGEMM_ERR_ARG
 
 
 BF = (bg.BIGEMM_BF16, bg.BIGEMM_BF16, bg.BIGEMM_F32, 0)
