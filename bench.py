@@ -12,6 +12,8 @@ ABI with inputs resident in HBM. Also reported:
   M = 1024 and 4096, against the dense FP8 MFMA peak (context, not the metric);
 * ``split_k_context``: the opt-in pinned-chunk split-K handle at small M (cold
   LLC) and on the long-K workload, against the unsplit kernel (context);
+* ``rmsnorm_bf16_context``: the batch-invariant RMSNorm (bf16, D = 4096) against
+  the HBM peak (context);
 * ``invariance_byte_diffs``: every row of every sweep result compared with the
   same row of the M = 4096 result (must be 0);
 * ``roofline``: the kernel's algorithmic flops per launch over its average
@@ -204,6 +206,24 @@ def main():
         del XL, WL, YL
         torch.cuda.empty_cache()
 
+    # ------------------------------------------------ RMSNorm (context)
+    # The batch-invariant RMSNorm (one workgroup per row), bf16, D = 4096;
+    # algorithmic bytes 2*M*D read + 2*M*D written + 2*D, against 8 TB/s HBM.
+    norm = []
+    if not args.no_sweep:
+        D = 4096
+        G = torch.from_numpy(normal_bf16(SEED_W, (D,)).view(np.int16)).to(dev)
+        for m in (1, 128, 4096, 16384):
+            XN = torch.from_numpy(normal_bf16(SEED_X + 1, (m, D)).view(np.int16)).to(dev)
+            YN = torch.empty_like(XN)
+            for _ in range(3):
+                bg.rmsnorm(XN, G, 1e-6, out=YN)
+            t = _events(torch, stream, lambda i: bg.rmsnorm(XN, G, 1e-6, out=YN), 50)
+            byts = 4 * m * D + 2 * D
+            norm.append({"M": m, "D": D, "us": round(t * 1e3, 2), "gbs_algorithmic": round(byts / (t * 1e-3) / 1e9, 0),
+                         "pct_hbm_peak": round(100 * byts / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 1)})
+            del XN, YN
+
     # ------------------------------------------------------- MXFP8 (context)
     mx = []
     if not args.no_sweep:
@@ -244,6 +264,7 @@ def main():
         "m_sweep": sweep,
         "mxfp8_k4096_n4096": mx,
         "split_k_context": split,
+        "rmsnorm_bf16_context": norm,
         "invariance_byte_diffs": diffs if sweep else None,
         "timed_wall_s": round(wall, 3),
     }

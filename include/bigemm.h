@@ -29,7 +29,7 @@
 extern "C" {
 #endif
 
-#define BIGEMM_ABI_VERSION 3
+#define BIGEMM_ABI_VERSION 4
 
 /* Exported entry points (the library is built with hidden visibility by default). */
 #if defined(__GNUC__)
@@ -183,6 +183,33 @@ BIGEMM_API bigemm_status bigemm_run_ws(bigemm_t h, int64_t M, int64_t N, int64_t
                             const void* W_scale, int64_t ldws,
                             void* workspace, uint64_t workspace_bytes,
                             void* stream);
+
+/*
+ * Batch-invariant RMSNorm, the blog's section "batch-invariant RMSNorm":
+ *   Y[i, j] = X[i, j] / sqrt((1/D) * sum_k X[i, k]^2 + eps) * gamma[j]
+ * with the data-parallel strategy it recommends and no small-batch switch: one
+ * workgroup per row at every M, the row's sum of squares accumulated in fp32 in
+ * an order fixed by D alone, then rounded once to the output type. Each output
+ * row depends only on its input row, gamma, D and eps.
+ *   dtype: BIGEMM_BF16 (X, gamma, Y bf16) or BIGEMM_F32 (all fp32)
+ *   X [M, D] (ldx >= D), gamma [D], Y [M, D] (ldy >= D), row-major, elements.
+ * Requirements (else BIGEMM_ERR_ARG, nothing launched): M >= 0 (M == 0 is a
+ * no-op), 8 <= D <= 65536, D % 8 == 0; X, gamma, Y non-NULL and 16-byte aligned
+ * with every row 16-byte aligned; M <= 2^31 - 1. Y may equal X (in place) but
+ * must not otherwise overlap X or gamma. BIGEMM_ERR_UNSUPPORTED on a device
+ * other than gfx950 (checked once per device, never a fallback). Enqueued on
+ * `stream` without synchronising; allocates nothing.
+ */
+BIGEMM_API bigemm_status bigemm_rmsnorm(int32_t dtype, int64_t M, int64_t D,
+                             const void* X, int64_t ldx,
+                             const void* gamma,
+                             void* Y, int64_t ldy,
+                             float eps, void* stream);
+
+/* The argument checks of bigemm_rmsnorm as a pure host function (no HIP call). */
+BIGEMM_API bigemm_status bigemm_rmsnorm_check_args(int32_t dtype, int64_t M, int64_t D,
+                                        const void* X, int64_t ldx, const void* gamma,
+                                        const void* Y, int64_t ldy);
 
 /* Release a handle. NULL is accepted. */
 BIGEMM_API bigemm_status bigemm_destroy(bigemm_t h);

@@ -83,6 +83,10 @@ def load():
                                           vp, i64, vp, i64, vp, i64]
         lib.bigemm_abi_version.restype = i32
         lib.bigemm_abi_version.argtypes = []
+        lib.bigemm_rmsnorm.restype = ctypes.c_int
+        lib.bigemm_rmsnorm.argtypes = [i32, i64, i64, vp, i64, vp, vp, i64, ctypes.c_float, vp]
+        lib.bigemm_rmsnorm_check_args.restype = ctypes.c_int
+        lib.bigemm_rmsnorm_check_args.argtypes = [i32, i64, i64, vp, i64, vp, vp, i64]
         lib.bigemm_create_split_k.restype = ctypes.c_int
         lib.bigemm_create_split_k.argtypes = [ctypes.POINTER(bigemm_desc), i32, ctypes.POINTER(vp)]
         lib.bigemm_workspace_size.restype = ctypes.c_int
@@ -294,4 +298,48 @@ def mm(x, w, x_scale=None, w_scale=None, out=None, stream=None, out_dtype=None, 
     else:
         bigemm_run(h, M, N, K, x.data_ptr(), _ld(x), w.data_ptr(), _ld(w), out.data_ptr(), _ld(out),
                    0, 0, 0, 0, stream)
+    return out
+
+
+def bigemm_rmsnorm(dtype: int, M: int, D: int, X: int, ldx: int, gamma: int, Y: int, ldy: int, eps: float,
+                   stream: int = 0, check: bool = True) -> int:
+    """Enqueue the batch-invariant RMSNorm (device pointers as integers)."""
+    st = load().bigemm_rmsnorm(int(dtype), M, D, X or None, ldx, gamma or None, Y or None, ldy, float(eps),
+                               stream or None)
+    if check and st != BIGEMM_OK:
+        raise BigemmError(st, "bigemm_rmsnorm")
+    return int(st)
+
+
+def bigemm_rmsnorm_check_args(dtype: int, M: int, D: int, X: int, ldx: int, gamma: int, Y: int, ldy: int) -> int:
+    return int(load().bigemm_rmsnorm_check_args(int(dtype), M, D, X or None, ldx, gamma or None, Y or None, ldy))
+
+
+def rmsnorm(x, gamma, eps: float = 1e-6, out=None, stream=None):
+    """Batch-invariant RMSNorm of each row of ``x`` [M, D] with ``gamma`` [D]: bf16 (or
+    int16/uint16 bf16 bit patterns) or float32, output of the same type. ``out`` may be
+    ``x`` itself (in place)."""
+    import torch
+
+    if x.dim() != 2 or gamma.dim() != 1 or gamma.shape[0] != x.shape[1]:
+        raise ValueError("x must be [M, D] and gamma [D]")
+    if x.dtype != gamma.dtype or not x.is_cuda or not gamma.is_cuda:
+        raise ValueError("x and gamma must be CUDA tensors of one dtype")
+    if x.element_size() == 2:
+        dtype = BIGEMM_BF16
+    elif x.dtype == torch.float32:
+        dtype = BIGEMM_F32
+    else:
+        raise ValueError(f"unsupported dtype {x.dtype}")
+    M, D = x.shape
+    if (D > 1 and x.stride(1) != 1) or not gamma.is_contiguous():
+        raise ValueError("rows must be contiguous")
+    if out is None:
+        out = torch.empty_like(x)
+    if out.shape != x.shape or out.dtype != x.dtype or (D > 1 and out.stride(1) != 1):
+        raise ValueError("out must match x")
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    with torch.cuda.device(x.device):
+        bigemm_rmsnorm(dtype, M, D, x.data_ptr(), _ld(x), gamma.data_ptr(), out.data_ptr(), _ld(out), eps, stream)
     return out

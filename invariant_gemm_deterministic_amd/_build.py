@@ -8,7 +8,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libbigemm.so")
-SOURCES = [os.path.join(CSRC, "bigemm_kernels.hip"), os.path.join(CSRC, "bigemm_api.cpp")]
+SOURCES = [os.path.join(CSRC, "bigemm_kernels.hip"), os.path.join(CSRC, "bigemm_rmsnorm.hip"),
+           os.path.join(CSRC, "bigemm_api.cpp")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed fp32 ops are disabled for every HIP translation unit.

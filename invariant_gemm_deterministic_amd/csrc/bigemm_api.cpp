@@ -12,8 +12,11 @@
 
 #include <new>
 
+#include <atomic>
+
 #include "../../include/bigemm.h"
 #include "bigemm_kernels.h"
+#include "bigemm_rmsnorm.h"
 
 struct bigemm_s {
   bigemm::Op op;
@@ -69,6 +72,41 @@ bigemm_status check(bigemm::Op op, int64_t M, int64_t N, int64_t K, const void* 
   if (!aligned16(X) || !aligned16(W) || !aligned16(Y)) return BIGEMM_ERR_ARG;
   if (mx && (!XS || !WS)) return BIGEMM_ERR_ARG;
   return BIGEMM_OK;
+}
+
+bigemm_status rmsnorm_check(int32_t dtype, int64_t M, int64_t D, const void* X, int64_t ldx, const void* G,
+                            const void* Y, int64_t ldy) {
+  if (dtype != BIGEMM_BF16 && dtype != BIGEMM_F32) return BIGEMM_ERR_UNSUPPORTED;
+  if (M < 0 || M > INT32_MAX || D < 8 || D > 65536 || D % 8 != 0) return BIGEMM_ERR_ARG;
+  const int64_t es = dtype == BIGEMM_BF16 ? 2 : 4;
+  if (ldx < D || ldy < D || (ldx * es) % 16 != 0 || (ldy * es) % 16 != 0) return BIGEMM_ERR_ARG;
+  if (M == 0) return BIGEMM_OK;
+  if (!X || !G || !Y || !aligned16(X) || !aligned16(G) || !aligned16(Y)) return BIGEMM_ERR_ARG;
+  return BIGEMM_OK;
+}
+
+// gfx950 check for the current device, done once per device (0 unknown, 1 yes, 2 no).
+std::atomic<int> g_arch_ok[64];
+
+bigemm_status current_device_supported() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return BIGEMM_ERR_DEVICE;
+  }
+  int state = dev >= 0 && dev < 64 ? g_arch_ok[dev].load(std::memory_order_relaxed) : 0;
+  if (state == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return BIGEMM_ERR_DEVICE;
+    }
+    const bool ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0 &&
+                    (prop.gcnArchName[6] == '\0' || prop.gcnArchName[6] == ':');
+    state = ok ? 1 : 2;
+    if (dev >= 0 && dev < 64) g_arch_ok[dev].store(state, std::memory_order_relaxed);
+  }
+  return state == 1 ? BIGEMM_OK : BIGEMM_ERR_UNSUPPORTED;
 }
 
 // The one fixed kernel of the handle's input family (no split).
@@ -176,6 +214,22 @@ bigemm_status bigemm_run_ws(bigemm_t h, int64_t M, int64_t N, int64_t K, const v
   if (M * N > (int64_t)INT32_MAX * 4) return BIGEMM_ERR_ARG;  // merge grid
   const hipError_t e = bigemm::launch_bf16_split(h->op, h->k_chunk, X, W, Y, workspace, M, N, K, ldx, ldw, ldy,
                                                  (hipStream_t)stream);
+  return e == hipSuccess ? BIGEMM_OK : BIGEMM_ERR_DEVICE;
+}
+
+bigemm_status bigemm_rmsnorm_check_args(int32_t dtype, int64_t M, int64_t D, const void* X, int64_t ldx,
+                                        const void* gamma, const void* Y, int64_t ldy) {
+  return rmsnorm_check(dtype, M, D, X, ldx, gamma, Y, ldy);
+}
+
+bigemm_status bigemm_rmsnorm(int32_t dtype, int64_t M, int64_t D, const void* X, int64_t ldx, const void* gamma,
+                             void* Y, int64_t ldy, float eps, void* stream) {
+  const bigemm_status st = rmsnorm_check(dtype, M, D, X, ldx, gamma, Y, ldy);
+  if (st != BIGEMM_OK || M == 0) return st;
+  const bigemm_status dv = current_device_supported();
+  if (dv != BIGEMM_OK) return dv;
+  const hipError_t e = bigemm::launch_rmsnorm(dtype == BIGEMM_BF16, X, ldx, gamma, Y, ldy, M, D, eps,
+                                              (hipStream_t)stream);
   return e == hipSuccess ? BIGEMM_OK : BIGEMM_ERR_DEVICE;
 }
 

@@ -69,6 +69,10 @@ class Oracle:
         lib.oracle_decode_f16.argtypes = [ctypes.c_uint16]
         lib.oracle_gemm_f16.restype = ctypes.c_int
         lib.oracle_gemm_f16.argtypes = [_i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i64]
+        lib.oracle_rmsnorm_bf16.restype = ctypes.c_int
+        lib.oracle_rmsnorm_bf16.argtypes = [_i64, _i64, _p, _i64, _p, ctypes.c_double, _p, _i64]
+        lib.oracle_rmsnorm_f32.restype = ctypes.c_int
+        lib.oracle_rmsnorm_f32.argtypes = [_i64, _i64, _p, _i64, _p, ctypes.c_double, _p, _i64]
         lib.oracle_gemm_i8.restype = ctypes.c_int
         lib.oracle_gemm_i8.argtypes = [_i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64]
         lib.oracle_gemm_f64.restype = ctypes.c_int
@@ -133,6 +137,22 @@ class Oracle:
         rc = self.lib.oracle_gemm_i8(M, N, K, _ptr(X), K, _ptr(W), N, _ptr(Y), N)
         if rc != 0:
             raise RuntimeError(f"oracle_gemm_i8 failed rc={rc}")
+        return Y
+
+    def rmsnorm(self, X, gamma, eps: float) -> np.ndarray:
+        """RMSNorm of each row of X (uint16 bf16 bits or float32) with gamma, in fp64."""
+        X = np.asarray(X)
+        bf16 = X.dtype == np.uint16
+        dt = np.uint16 if bf16 else np.float32
+        X = np.ascontiguousarray(X, dtype=dt)
+        G = np.ascontiguousarray(gamma, dtype=dt)
+        M, D = X.shape
+        assert G.shape == (D,), (G.shape, D)
+        Y = np.empty((M, D), dtype=np.float64)
+        f = self.lib.oracle_rmsnorm_bf16 if bf16 else self.lib.oracle_rmsnorm_f32
+        rc = f(M, D, _ptr(X), D, _ptr(G), float(eps), _ptr(Y), D)
+        if rc != 0:
+            raise RuntimeError(f"oracle rmsnorm failed rc={rc}")
         return Y
 
     def gemm_f64(self, A, B, want_s: bool = True):
@@ -225,6 +245,19 @@ def gemm_f16(X, W, want_s: bool = True):
 
 def gemm_i8(X, W):
     return default().gemm_i8(X, W)
+
+
+def rmsnorm(X, gamma, eps: float):
+    return default().rmsnorm(X, gamma, eps)
+
+
+def rmsnorm_tol(D: int, bf16_out: bool) -> float:
+    """Relative error bound of the fp32 RMSNorm against the exact value: the sum of D
+    squares (relative error at most gamma_{D-1}(fp32), halved by the square root) plus
+    a few binary32 roundings (division, eps, square root, reciprocal, two products),
+    and one bf16 rounding (u = 2^-8) for a bf16 output."""
+    u32 = unit_roundoff(24)
+    return gamma(D - 1, u32) / 2 + 8 * u32 + (unit_roundoff(8) if bf16_out else 0.0)
 
 
 def gemm_f64(A, B, want_s: bool = True):

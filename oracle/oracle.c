@@ -22,6 +22,9 @@
  *   - int8 operands are exact integers; their GEMM is accumulated exactly in
  *     int64 (integer addition is associative: no order question arises).
  *
+ * It also holds the blog's RMSNorm in binary64 (section "batch-invariant
+ * RMSNorm"), for the batch-invariant RMSNorm kernel.
+ *
  * Every product is exact in binary64 (bf16*bf16 has at most 16 significant
  * bits, fp16*fp16 at most 22; a scaled E4M3*E4M3 product has at most 8). The only rounding is the
  * binary64 accumulation, bounded by the blog's sequential-sum bound
@@ -227,6 +230,60 @@ int oracle_gemm_mxfp8(int64_t M, int64_t N, int64_t K,
   free(A);
   free(B);
   return rc;
+}
+
+/* --------------------------------------------------------------- RMSNorm */
+
+/*
+ * The blog's batch-invariant RMSNorm section defines
+ *   RMSNorm(x_i) = x_i / sqrt((1/d) sum_j x_ij^2 + eps) (.) gamma.
+ * Here in binary64: s = sum_j x_ij^2 with j ascending, then
+ * y_ij = x_ij / sqrt(s / d + eps) * gamma_j. Operands are decoded exactly
+ * (bf16 bits, or binary32 values widened).
+ */
+static void rmsnorm_rows(int64_t M, int64_t D, const double* X, const double* G, double eps, double* Y,
+                         int64_t ldy) {
+  int64_t i;
+#pragma omp parallel for schedule(static)
+  for (i = 0; i < M; ++i) {
+    const double* x = X + i * D;
+    double s = 0.0;
+    for (int64_t j = 0; j < D; ++j) s += x[j] * x[j];
+    const double den = sqrt(s / (double)D + eps);
+    for (int64_t j = 0; j < D; ++j) Y[i * ldy + j] = x[j] / den * G[j];
+  }
+}
+
+int oracle_rmsnorm_bf16(int64_t M, int64_t D, const uint16_t* X, int64_t ldx, const uint16_t* gamma, double eps,
+                        double* Y, int64_t ldy) {
+  if (M < 0 || D < 1 || ldx < D || ldy < D) return 1;
+  if (M == 0) return 0;
+  double* A = (double*)malloc(sizeof(double) * (size_t)(M * D));
+  double* G = (double*)malloc(sizeof(double) * (size_t)D);
+  if (!A || !G) { free(A); free(G); return 2; }
+  for (int64_t i = 0; i < M; ++i)
+    for (int64_t j = 0; j < D; ++j) A[i * D + j] = oracle_decode_bf16(X[i * ldx + j]);
+  for (int64_t j = 0; j < D; ++j) G[j] = oracle_decode_bf16(gamma[j]);
+  rmsnorm_rows(M, D, A, G, eps, Y, ldy);
+  free(A);
+  free(G);
+  return 0;
+}
+
+int oracle_rmsnorm_f32(int64_t M, int64_t D, const float* X, int64_t ldx, const float* gamma, double eps,
+                       double* Y, int64_t ldy) {
+  if (M < 0 || D < 1 || ldx < D || ldy < D) return 1;
+  if (M == 0) return 0;
+  double* A = (double*)malloc(sizeof(double) * (size_t)(M * D));
+  double* G = (double*)malloc(sizeof(double) * (size_t)D);
+  if (!A || !G) { free(A); free(G); return 2; }
+  for (int64_t i = 0; i < M; ++i)
+    for (int64_t j = 0; j < D; ++j) A[i * D + j] = (double)X[i * ldx + j];
+  for (int64_t j = 0; j < D; ++j) G[j] = (double)gamma[j];
+  rmsnorm_rows(M, D, A, G, eps, Y, ldy);
+  free(A);
+  free(G);
+  return 0;
 }
 
 /* ------------------------------------------------------------------ misc */

@@ -323,7 +323,60 @@ def check_i8(orc: oracle.Oracle):
     assert orc.gemm_i8(X, W).tolist() == want
 
 
+def _py_rmsnorm(x, g, eps):
+    """RMSNorm of one row in Python floats: fsum of the (exact) squares, one sqrt."""
+    s = math.fsum(float(v) * float(v) for v in x)
+    den = math.sqrt(s / len(x) + eps)
+    return [float(v) / den * float(w) for v, w in zip(x, g)]
+
+
+def check_rmsnorm_fsum(orc: oracle.Oracle):
+    """Random bf16 and fp32 rows (eps 0.5 and 1e-6) against a Python evaluation of the
+    blog's RMSNorm formula with a correctly rounded sum of squares."""
+    rng = np.random.default_rng(97)
+    for t, (D, eps) in enumerate([(8, 0.5), (24, 1e-6), (96, 1e-6), (40, 0.5)]):
+        X = normal_bf16(1700 + t, (3, D))
+        G = normal_bf16(1800 + t, (D,))
+        Y = orc.rmsnorm(X, G, eps)
+        xf, gf = t_bf16(X), t_bf16(G)
+        for i in range(3):
+            ref = np.array(_py_rmsnorm(xf[i], gf, eps))
+            _close(Y[i], ref, 8 * U64 * np.abs(ref) + 1e-300, f"rmsnorm bf16 D={D}")
+        Xf = rng.standard_normal((2, D)).astype(np.float32)
+        Gf = rng.standard_normal(D).astype(np.float32)
+        Yf = orc.rmsnorm(Xf, Gf, eps)
+        for i in range(2):
+            ref = np.array(_py_rmsnorm(Xf[i].astype(np.float64), Gf.astype(np.float64), eps))
+            _close(Yf[i], ref, 8 * U64 * np.abs(ref) + 1e-300, f"rmsnorm f32 D={D}")
+
+
+def check_rmsnorm_closed_forms(orc: oracle.Oracle):
+    """eps = 0: a constant row c gives sign(c) * gamma exactly; scaling a row by 2^k
+    leaves it bit-identical; a one-hot row a*e_p gives sign(a) * sqrt(D) * gamma_p at p
+    and 0 elsewhere; rows are separable ([A; B] row by row)."""
+    D = 64
+    G = normal_bf16(1900, (D,))
+    g = t_bf16(G)
+    for c in (1.5, -0.375, 96.0):
+        X = f32_to_bf16_bits(np.full((1, D), c, np.float32))
+        assert np.array_equal(orc.rmsnorm(X, G, 0.0)[0], np.sign(c) * g), c
+    X = normal_bf16(1901, (4, D))
+    Y = orc.rmsnorm(X, G, 0.0)
+    for k in (-3, 5):
+        Xk = f32_to_bf16_bits(t_bf16(X).astype(np.float32) * np.float32(2.0 ** k))
+        assert np.array_equal(orc.rmsnorm(Xk, G, 0.0), Y), k
+    X = np.zeros((1, D), np.uint16)
+    X[0, 9] = f32_to_bf16_bits(np.array([-2.5], np.float32))[0]
+    Y1 = orc.rmsnorm(X, G, 0.0)[0]
+    assert np.count_nonzero(Y1) == 1
+    _close([Y1[9]], [-math.sqrt(D) * g[9]], 4 * U64 * abs(math.sqrt(D) * g[9]), "rmsnorm one-hot")
+    A, B = normal_bf16(1902, (3, D)), normal_bf16(1903, (5, D))
+    assert np.array_equal(orc.rmsnorm(np.vstack([A, B]), G, 1e-6),
+                          np.vstack([orc.rmsnorm(A, G, 1e-6), orc.rmsnorm(B, G, 1e-6)]))
+
+
 ALL_CHECKS = [check_sum_order, check_bruteforce_bf16, check_bruteforce_mx, check_integer_bf16,
               check_integer_mx, check_decoders, check_linspace_closed_form, check_linspace_bf16_row0,
               check_row_separability, check_mx_equals_prescaled_bf16, check_scale_shift, check_degenerate,
-              check_decoder_f16, check_bruteforce_f16, check_integer_f16, check_i8]
+              check_decoder_f16, check_bruteforce_f16, check_integer_f16, check_i8,
+              check_rmsnorm_fsum, check_rmsnorm_closed_forms]

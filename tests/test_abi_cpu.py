@@ -23,7 +23,8 @@ def test_header_declares_the_boundary():
     fns = declared_functions()
     for name in ("bigemm_create", "bigemm_run", "bigemm_destroy", "bigemm_status_str",
                  "bigemm_get_config", "bigemm_check_args", "bigemm_abi_version",
-                 "bigemm_create_split_k", "bigemm_workspace_size", "bigemm_run_ws"):
+                 "bigemm_create_split_k", "bigemm_workspace_size", "bigemm_run_ws",
+                 "bigemm_rmsnorm", "bigemm_rmsnorm_check_args"):
         assert name in fns
 
 
@@ -34,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert bg.bigemm_abi_version() == 3
+    assert bg.bigemm_abi_version() == 4
     for s in range(5):
         assert bg.bigemm_status_str(s)
     assert "unknown" in bg.bigemm_status_str(99)
@@ -125,3 +126,17 @@ def test_check_args_other_types():
     assert chk(I8, 16, 40, 64) == bg.BIGEMM_ERR_ARG
     assert chk(I8, 16, 64, 64, ldy=66) == bg.BIGEMM_ERR_ARG
     assert chk(I8, 16, 64, 64, XS=A, ldxs=2) == bg.BIGEMM_ERR_ARG
+
+
+def test_rmsnorm_check_args():
+    ok = bg.bigemm_rmsnorm_check_args
+    assert ok(bg.BIGEMM_BF16, 16, 4096, A, 4096, A, A, 4096) == bg.BIGEMM_OK
+    assert ok(bg.BIGEMM_F32, 16, 8, A, 8, A, A, 12) == bg.BIGEMM_OK          # padded fp32 rows
+    assert ok(bg.BIGEMM_BF16, 0, 64, 0, 64, 0, 0, 64) == bg.BIGEMM_OK        # M = 0 is a no-op
+    assert ok(bg.BIGEMM_BF16, 16, 12, A, 16, A, A, 16) == bg.BIGEMM_ERR_ARG  # D % 8
+    assert ok(bg.BIGEMM_BF16, 16, 65544, A, 65544, A, A, 65544) == bg.BIGEMM_ERR_ARG  # D > 65536
+    assert ok(bg.BIGEMM_BF16, 16, 64, A, 60, A, A, 64) == bg.BIGEMM_ERR_ARG  # ldx < D
+    assert ok(bg.BIGEMM_BF16, 16, 64, A, 68, A, A, 64) == bg.BIGEMM_ERR_ARG  # row not 16-byte aligned
+    assert ok(bg.BIGEMM_BF16, 16, 64, A + 2, 64, A, A, 64) == bg.BIGEMM_ERR_ARG
+    assert ok(bg.BIGEMM_BF16, 16, 64, A, 64, 0, A, 64) == bg.BIGEMM_ERR_ARG
+    assert ok(bg.BIGEMM_E4M3, 16, 64, A, 64, A, A, 64) == bg.BIGEMM_ERR_UNSUPPORTED

@@ -33,6 +33,13 @@ MUTATIONS = [
     ("i8_w_columns", "acc[j] += a * (int64_t)wrow[j];", "acc[j] += a * (int64_t)wrow[N - 1 - j];"),
     ("i8_drop_last_k", "for (int64_t k = 0; k < K; ++k) {\n      const int64_t a",
      "for (int64_t k = 0; k < K - 1; ++k) {\n      const int64_t a"),
+    ("rms_not_squared", "for (int64_t j = 0; j < D; ++j) s += x[j] * x[j];", "for (int64_t j = 0; j < D; ++j) s += fabs(x[j]);"),
+    ("rms_drop_last", "for (int64_t j = 0; j < D; ++j) s += x[j] * x[j];", "for (int64_t j = 0; j < D - 1; ++j) s += x[j] * x[j];"),
+    ("rms_mean_d_minus_1", "sqrt(s / (double)D + eps)", "sqrt(s / (double)(D > 1 ? D - 1 : 1) + eps)"),
+    ("rms_no_eps", "sqrt(s / (double)D + eps)", "sqrt(s / (double)D)"),
+    ("rms_gamma_reversed", "Y[i * ldy + j] = x[j] / den * G[j];", "Y[i * ldy + j] = x[j] / den * G[D - 1 - j];"),
+    ("rms_gamma_ignored", "for (int64_t j = 0; j < D; ++j) G[j] = oracle_decode_bf16(gamma[j]);",
+     "for (int64_t j = 0; j < D; ++j) G[j] = 1.0;"),
     ("x_scale_dropped", "A[i * K + k] = e4m3_table[X[i * ldx + k]] * oracle_decode_e8m0(XS[i * ldxs + k / 32]);",
      "A[i * K + k] = e4m3_table[X[i * ldx + k]];"),
 ]
