@@ -8,8 +8,9 @@ ABI with inputs resident in HBM. Also reported:
 * ``m_sweep``: TFLOP/s and % of the bf16 MFMA peak for M = 1 ... 4096 at
   K = N = 4096 (small M rotates among buffer sets larger than the 256 MB
   last-level cache, so W is read from HBM), with achieved algorithmic HBM GB/s;
-* ``mxfp8_k4096_n4096``: the MXFP8 kernel (E4M3, K-varying E8M0 scales) at
-  M = 1024 and 4096, against the dense FP8 MFMA peak (context, not the metric);
+* ``other_types_k4096_n4096``: the MXFP8 kernel (E4M3, K-varying E8M0 scales),
+  fp16 inputs, bf16 output and int8 inputs at M = 1024 and 4096, each against
+  its dense MFMA peak (context, not the metric);
 * ``split_k_context``: the opt-in pinned-chunk split-K handle at small M (cold
   LLC) and on the long-K workload, against the unsplit kernel (context);
 * ``rmsnorm_bf16_context``: the batch-invariant RMSNorm (bf16, D = 4096) against
@@ -38,6 +39,7 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PEAK_FP8_TFLOPS = 5033.2    # MI355X dense FP8 / MXFP8 MFMA
+PEAK_I8_TOPS = 5033.2       # MI355X dense int8 MFMA (TOP/s)
 M_SWEEP = [1, 16, 64, 128, 256, 512, 1024, 2048, 4096]
 K = N = 4096
 
@@ -237,9 +239,28 @@ def main():
                 bg.mm(Xm[:m], Wm, XS[:m], WS, out=Y[:m])
             t = _events(torch, stream, lambda i: bg.mm(Xm[:m], Wm, XS[:m], WS, out=Y[:m]), 20)
             f = 2.0 * m * N * K
-            mx.append({"M": m, "us": round(t * 1e3, 2), "tflops": round(f / (t * 1e-3) / 1e12, 1),
-                       "pct_fp8_peak": round(100 * f / (t * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 1)})
+            mx.append({"kind": "mxfp8", "M": m, "us": round(t * 1e3, 2), "tflops": round(f / (t * 1e-3) / 1e12, 1),
+                       "pct_peak": round(100 * f / (t * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 1)})
         del Xm, Wm, XS, WS
+        # fp16 inputs and int8 inputs on the same tile skeleton, and bf16 output (context)
+        from bigemm_inputs import int_i8, normal_f16
+        Xh = torch.from_numpy(normal_f16(SEED_X, (4096, K))).view(torch.float16).to(dev)
+        Wh = torch.from_numpy(normal_f16(SEED_W, (K, N), 0.02)).view(torch.float16).to(dev)
+        Xi = torch.from_numpy(int_i8(SEED_X, (4096, K))).to(dev)
+        Wi = torch.from_numpy(int_i8(SEED_W, (K, N))).to(dev)
+        Yi = torch.empty((4096, N), dtype=torch.int32, device=dev)
+        Yb = torch.empty((4096, N), dtype=torch.bfloat16, device=dev)
+        for name, fn, peak in (("f16", lambda m: bg.mm(Xh[:m], Wh, out=Y[:m]), PEAK_BF16_TFLOPS),
+                               ("bf16_out", lambda m: bg.mm(X[:m], W, out=Yb[:m]), PEAK_BF16_TFLOPS),
+                               ("i8", lambda m: bg.mm(Xi[:m], Wi, out=Yi[:m]), PEAK_I8_TOPS)):
+            for m in (1024, 4096):
+                for _ in range(5):
+                    fn(m)
+                t = _events(torch, stream, lambda i: fn(m), 20)
+                f = 2.0 * m * N * K
+                mx.append({"kind": name, "M": m, "us": round(t * 1e3, 2), "tflops": round(f / (t * 1e-3) / 1e12, 1),
+                           "pct_peak": round(100 * f / (t * 1e-3) / 1e12 / peak, 1)})
+        del Xh, Wh, Xi, Wi, Yi, Yb
 
     line = {
         "metric": "TFLOP/s vs M (1-4096) at K=N=4096, % MFMA peak; invariance byte-diffs=0",
@@ -262,7 +283,7 @@ def main():
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic() if M == 4096 else None},
         "m_sweep": sweep,
-        "mxfp8_k4096_n4096": mx,
+        "other_types_k4096_n4096": mx,
         "split_k_context": split,
         "rmsnorm_bf16_context": norm,
         "invariance_byte_diffs": diffs if sweep else None,
