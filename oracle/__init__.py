@@ -12,6 +12,10 @@ multiplication: C_ij = sum_k A_ik B_kj) and how closely the GPU must agree:
 * ``gemm_bf16`` / ``gemm_f16`` / ``gemm_mxfp8`` return the fp64-accumulated
   product of the exactly decoded operands, summed with k ascending, and
   S_ij = sum_k |x_ik w_kj|. ``gemm_i8`` returns the exact int64 product.
+* ``attention`` is causal softmax attention of query tokens over the keys
+  and values of their sequences (section on batch-invariant attention), in
+  fp64; ``attention_tol`` bounds the fp32 evaluation's error for each
+  (token, head) relative to S = sum_j w_j |v_j| / sum_j w_j.
 * ``max_normalized_error`` is the parity metric: max_ij |y_gpu - y| / S_ij
   (elements with S_ij = 0 must be exactly 0). Any fp32 accumulation of the
   exact products, in any order, satisfies e <= gamma_{K-1}(fp32) by the blog's
@@ -82,6 +86,9 @@ class Oracle:
         lib.oracle_gemm_mxfp8.restype = ctypes.c_int
         lib.oracle_gemm_mxfp8.argtypes = [_i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i64,
                                           _p, _i64, _p, _i64]
+        lib.oracle_attention.restype = ctypes.c_int
+        lib.oracle_attention.argtypes = [_i64, _i64, _i64, _i64, _i64, _i64, _p, _p, _p, _p, _p, ctypes.c_double,
+                                         _p, _p, _p]
         lib.oracle_set_threads.restype = ctypes.c_int
         lib.oracle_set_threads.argtypes = [ctypes.c_int]
         self.lib = lib
@@ -154,6 +161,29 @@ class Oracle:
         if rc != 0:
             raise RuntimeError(f"oracle rmsnorm failed rc={rc}")
         return Y
+
+    def attention(self, Q, K, V, seq, pos, scale: float):
+        """Causal softmax attention of query tokens over per-sequence keys/values, in fp64.
+
+        Q [T, H, D] and K, V [nseq, maxlen, Hkv, D] are bf16 bit patterns (uint16);
+        seq, pos [T] give each token's sequence and position. Returns (O, S, stats):
+        O and S are [T, H, D]; stats [T, H, 3] holds (A, Mabs, R) for attention_tol."""
+        Q = np.ascontiguousarray(Q, dtype=np.uint16)
+        K = np.ascontiguousarray(K, dtype=np.uint16)
+        V = np.ascontiguousarray(V, dtype=np.uint16)
+        seq = np.ascontiguousarray(seq, dtype=np.int32)
+        pos = np.ascontiguousarray(pos, dtype=np.int32)
+        T, H, D = Q.shape
+        nseq, maxlen, Hkv, D2 = K.shape
+        assert D == D2 and V.shape == K.shape and seq.shape == (T,) and pos.shape == (T,)
+        O = np.empty((T, H, D), dtype=np.float64)
+        S = np.empty((T, H, D), dtype=np.float64)
+        st = np.empty((T, H, 3), dtype=np.float64)
+        rc = self.lib.oracle_attention(T, H, Hkv, D, nseq, maxlen, _ptr(Q), _ptr(K), _ptr(V), _ptr(seq), _ptr(pos),
+                                       float(scale), _ptr(O), _ptr(S), _ptr(st))
+        if rc != 0:
+            raise RuntimeError(f"oracle_attention failed rc={rc}")
+        return O, S, st
 
     def gemm_f64(self, A, B, want_s: bool = True):
         """fp64 product of fp64 operands (the oracle's accumulation core)."""
@@ -262,6 +292,37 @@ def rmsnorm_tol(D: int, bf16_out: bool) -> float:
 
 def gemm_f64(A, B, want_s: bool = True):
     return default().gemm_f64(A, B, want_s)
+
+
+def attention(Q, K, V, seq, pos, scale: float):
+    return default().attention(Q, K, V, seq, pos, scale)
+
+
+def attention_tol(stats, L, D: int, bf16_out: bool) -> np.ndarray:
+    """Bound on |o_gpu - o| / S for each (token, head), for any fp32 evaluation that
+    forms the scores with at most two roundings per product pair, subtracts a running
+    or final maximum, exponentiates in single precision (allowing 4 ulp) and adds the
+    weighted values in any order, possibly as partial sums rescaled by exp(m_s - m).
+
+    stats = (A, Mabs, R) from ``attention``; L = context length (pos + 1), broadcast
+    against stats[..., 0]. Score error: delta = gamma_{2D} A + 2u Mabs. A weight's
+    relative error: eps_w = 2 delta + 2 e_exp + 2u R + 3u (its score and the maximum
+    both err, two exponentials with their argument roundings, one product). Weights
+    with relative errors <= eps_w move o by at most 2 eps_w (1 + eps_w) S, and the two
+    sums (numerator, denominator) add gamma_{2L+4} S each; one division adds u."""
+    u = unit_roundoff(24)
+    st = np.asarray(stats, dtype=np.float64)
+    A, Mabs, R = st[..., 0], st[..., 1], st[..., 2]
+    L = np.broadcast_to(np.asarray(L, dtype=np.float64), A.shape)
+    e_exp = 8 * u
+    delta = gamma(2 * D, u) * A + 2 * u * Mabs
+    eps_w = 2 * delta + 2 * e_exp + 2 * u * R + 3 * u
+    nu = (2 * L + 4) * u
+    g_sum = nu / (1 - nu)
+    tol = 2 * eps_w * (1 + eps_w) + 2 * g_sum + u
+    if bf16_out:
+        tol = tol + unit_roundoff(8) * (1 + tol)
+    return tol
 
 
 def gemm_bf16(X, W, want_s: bool = True):

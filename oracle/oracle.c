@@ -286,6 +286,96 @@ int oracle_rmsnorm_f32(int64_t M, int64_t D, const float* X, int64_t ldx, const 
   return 0;
 }
 
+/* ------------------------------------------------------------- attention */
+
+/*
+ * The blog's batch-invariant attention section: the query at position i of a
+ * sequence attends to that sequence's keys and values at positions j <= i
+ * (the causal mask),
+ *   o = sum_{j <= i} softmax_j(scale * q . k_j) v_j,
+ * where the section's formula has scale = 1/sqrt(d); it is an argument here so
+ * that the caller's rounded value is the one used. Decode is a query at the
+ * last position of its sequence.
+ * Inputs, bf16 bit patterns, row-major:
+ *   Q [T][H][D]       query token t, head h;
+ *   K, V [nseq][maxlen][Hkv][D]   keys and values of each sequence by logical
+ *                     position (what the KV cache holds, in order);
+ *   seq[t], pos[t]    the token's sequence and position (pos < maxlen).
+ * Query head h reads key/value head h / (H / Hkv) (grouped-query attention).
+ * Per (t, h), in binary64 with j ascending:
+ *   s_j = scale * sum_e q_e k_je (e ascending), m = max_j s_j,
+ *   w_j = exp(s_j - m), O = sum_j w_j v_j / sum_j w_j,
+ *   S = sum_j w_j |v_j| / sum_j w_j (the scale of the error metric),
+ *   stats = (A, Mabs, R): A = max_j scale * sum_e |q_e k_je|,
+ *   Mabs = max_j |s_j|, R = m - min_j s_j (inputs of the error bound).
+ * Returns 1 for bad sizes or a token whose seq/pos is out of range.
+ */
+int oracle_attention(int64_t T, int64_t H, int64_t Hkv, int64_t D, int64_t nseq, int64_t maxlen,
+                     const uint16_t* Q, const uint16_t* K, const uint16_t* V, const int32_t* seq,
+                     const int32_t* pos, double scale, double* O, double* S, double* stats) {
+  if (T < 0 || H < 1 || Hkv < 1 || H % Hkv != 0 || D < 1 || nseq < 1 || maxlen < 1) return 1;
+  for (int64_t t = 0; t < T; ++t)
+    if (seq[t] < 0 || seq[t] >= nseq || pos[t] < 0 || pos[t] >= maxlen) return 1;
+  int bad = 0;
+  int64_t th;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+  for (th = 0; th < T * H; ++th) {
+    const int64_t t = th / H, h = th % H;
+    const int64_t sq = seq[t];
+    const int64_t p = pos[t];
+    const int64_t L = p + 1; /* keys j = 0 .. p */
+    const int64_t g = h / (H / Hkv);
+    double* q = (double*)malloc(sizeof(double) * (size_t)D);
+    double* s = (double*)malloc(sizeof(double) * (size_t)(p + 1));
+    double* w = (double*)malloc(sizeof(double) * (size_t)(p + 1));
+    if (!q || !s || !w) {
+      bad = 1;
+      free(q); free(s); free(w);
+      continue;
+    }
+    for (int64_t e = 0; e < D; ++e) q[e] = oracle_decode_bf16(Q[(t * H + h) * D + e]);
+    double a_max = 0.0, s_abs = 0.0, m = -INFINITY, s_min = INFINITY;
+    for (int64_t j = 0; j < L; ++j) {
+      const uint16_t* k = K + ((sq * maxlen + j) * Hkv + g) * D;
+      double d = 0.0, da = 0.0;
+      for (int64_t e = 0; e < D; ++e) {
+        const double prod = q[e] * oracle_decode_bf16(k[e]);
+        d += prod;
+        da += fabs(prod);
+      }
+      s[j] = scale * d;
+      if (scale * da > a_max) a_max = scale * da;
+      if (fabs(s[j]) > s_abs) s_abs = fabs(s[j]);
+      if (s[j] > m) m = s[j];
+      if (s[j] < s_min) s_min = s[j];
+    }
+    double den = 0.0;
+    for (int64_t j = 0; j < L; ++j) {
+      w[j] = exp(s[j] - m);
+      den += w[j];
+    }
+    for (int64_t e = 0; e < D; ++e) {
+      double num = 0.0, nabs = 0.0;
+      for (int64_t j = 0; j < L; ++j) {
+        const double v = oracle_decode_bf16(V[((sq * maxlen + j) * Hkv + g) * D + e]);
+        num += w[j] * v;
+        nabs += w[j] * fabs(v);
+      }
+      O[(t * H + h) * D + e] = num / den;
+      if (S) S[(t * H + h) * D + e] = nabs / den;
+    }
+    if (stats) {
+      stats[(t * H + h) * 3 + 0] = a_max;
+      stats[(t * H + h) * 3 + 1] = s_abs;
+      stats[(t * H + h) * 3 + 2] = m - s_min;
+    }
+    free(q);
+    free(s);
+    free(w);
+  }
+  return bad ? 2 : 0;
+}
+
 /* ------------------------------------------------------------------ misc */
 
 int oracle_set_threads(int n) {

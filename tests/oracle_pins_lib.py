@@ -17,7 +17,12 @@ Sources of truth used here, none of which is the oracle itself:
   * torch's CPU float8_e4m3fn / float8_e8m0fnu / bfloat16 conversions and
     numpy's float16 (library routines) for the decoders;
   * numpy's int64 matrix product (a library routine) for the exact int8 GEMM;
-  * invariances of power-of-two block scaling (exact in binary64).
+  * invariances of power-of-two block scaling (exact in binary64);
+  * torch's CPU scaled_dot_product_attention in float64 with the causal mask
+    (a library routine) for the attention formula of the blog's section on
+    batch-invariant attention, plus its closed forms: uniform weights when
+    q = 0, a single key when the position is 0, one key when its score
+    dominates by hundreds, and invariance under reordering the keys.
 """
 from __future__ import annotations
 
@@ -375,8 +380,109 @@ def check_rmsnorm_closed_forms(orc: oracle.Oracle):
                           np.vstack([orc.rmsnorm(A, G, 1e-6), orc.rmsnorm(B, G, 1e-6)]))
 
 
+# ------------------------------------------------------------------ attention
+def _attn_case(seed, lens, H, Hkv, D, maxlen=None):
+    """Keys/values of len(lens) sequences and one query per position of each."""
+    maxlen = maxlen or max(lens)
+    K = normal_bf16(seed, (len(lens), maxlen, Hkv, D))
+    V = normal_bf16(seed + 1, (len(lens), maxlen, Hkv, D))
+    seq = np.concatenate([np.full(L, s) for s, L in enumerate(lens)]).astype(np.int32)
+    pos = np.concatenate([np.arange(L) for L in lens]).astype(np.int32)
+    Q = normal_bf16(seed + 2, (len(seq), H, D))
+    return Q, K, V, seq, pos
+
+
+def check_attention_sdpa(orc: oracle.Oracle):
+    """Every position of three sequences as a query (grouped heads, H = 6 over Hkv = 2 and
+    H = Hkv = 3): equal to torch's float64 scaled_dot_product_attention with the causal
+    mask, keys and values repeated over each group's query heads, within 1e-12."""
+    import torch.nn.functional as F
+    for (H, Hkv, D, lens, seed) in [(6, 2, 24, [37, 50, 1], 2000), (3, 3, 16, [9, 20, 5], 2010)]:
+        Q, K, V, seq, pos = _attn_case(seed, lens, H, Hkv, D)
+        scale = float(np.float32(1.0 / math.sqrt(D)))
+        O, S, _ = orc.attention(Q, K, V, seq, pos, scale)
+        off = 0
+        for s_i, L in enumerate(lens):
+            q = torch.from_numpy(t_bf16(Q[off:off + L])).permute(1, 0, 2)[None]
+            k = torch.from_numpy(t_bf16(K[s_i, :L])).permute(1, 0, 2).repeat_interleave(H // Hkv, dim=0)[None]
+            v = torch.from_numpy(t_bf16(V[s_i, :L])).permute(1, 0, 2).repeat_interleave(H // Hkv, dim=0)[None]
+            ref = F.scaled_dot_product_attention(q, k, v, is_causal=True, scale=scale)[0].permute(1, 0, 2).numpy()
+            _close(O[off:off + L], ref, 1e-12 * (1 + np.abs(ref)), f"attention vs sdpa H={H} L={L}")
+            absref = F.scaled_dot_product_attention(q, k, v.abs(), is_causal=True, scale=scale)[0]
+            _close(S[off:off + L], absref.permute(1, 0, 2).numpy(), 1e-12 * (1 + np.abs(absref.numpy().max())),
+                   "attention S vs sdpa of |v|")
+            off += L
+
+
+def check_attention_closed_forms(orc: oracle.Oracle):
+    """q = 0: the weights are uniform, so o is the exact mean of v_0..v_p and S the mean of
+    |v|, with A = Mabs = R = 0. Position 0: o = v_0. One key scoring 896 above all others
+    at a score of 1024: o is that key's value exactly (exp(-896) underflows) and
+    (A, Mabs, R) = (1024, 1024, 896)."""
+    H, Hkv, D = 4, 2, 16
+    _, K, V, _, _ = _attn_case(2100, [40], H, Hkv, D)
+    pos = np.array([0, 1, 17, 39], np.int32)
+    seq = np.zeros(4, np.int32)
+    Q = np.zeros((4, H, D), np.uint16)
+    O, S, st = orc.attention(Q, K, V, seq, pos, 0.25)
+    vf = t_bf16(V[0])
+    for t, p in enumerate(pos):
+        for h in range(H):
+            g = h // (H // Hkv)
+            for e in (0, 7, 15):
+                col = [Fraction(float(x)) for x in vf[:p + 1, g, e]]
+                want = float(sum(col, Fraction(0)) / (p + 1))
+                wabs = float(sum((abs(c) for c in col), Fraction(0)) / (p + 1))
+                _close([O[t, h, e]], [want], 4 * U64 * (abs(want) + 1e-300), "mean of v")
+                _close([S[t, h, e]], [wabs], 4 * U64 * wabs, "mean of |v|")
+    assert not st.any(), "stats of q = 0"
+    Q1 = normal_bf16(2103, (1, H, D))
+    O1, S1, _ = orc.attention(Q1, K, V, np.zeros(1, np.int32), np.zeros(1, np.int32), 0.25)
+    for h in range(H):
+        assert np.array_equal(O1[0, h], vf[0, h // 2]) and np.array_equal(S1[0, h], np.abs(vf[0, h // 2]))
+    # dominant key: q = 64 e_0, k_j = 8 e_0 except k_5 = 64 e_0; scale 1/4 gives scores 128 and 1024
+    Kd = np.zeros((1, 12, Hkv, D), np.uint16)
+    Kd[0, :, :, 0] = f32_to_bf16_bits(np.array([8.0], np.float32))[0]
+    Kd[0, 5, :, 0] = f32_to_bf16_bits(np.array([64.0], np.float32))[0]
+    Qd = np.zeros((1, H, D), np.uint16)
+    Qd[0, :, 0] = f32_to_bf16_bits(np.array([64.0], np.float32))[0]
+    Od, _, std = orc.attention(Qd, Kd, V[:, :12], np.zeros(1, np.int32), np.array([11], np.int32), 0.25)
+    for h in range(H):
+        assert np.array_equal(Od[0, h], vf[5, h // 2]), "dominant key"
+    assert np.array_equal(std[0], np.tile([1024.0, 1024.0, 896.0], (H, 1))), std[0]
+
+
+def check_attention_invariances(orc: oracle.Oracle):
+    """Reordering the keys of a context (the same permutation on K and V) leaves the last
+    position's output unchanged up to rounding; the outputs of a token do not depend on the
+    other tokens or on their order (row by row); negating q negates every score, so A,
+    Mabs and R are unchanged exactly; equal query heads of one group give equal outputs."""
+    H, Hkv, D = 4, 2, 16
+    Q, K, V, seq, pos = _attn_case(2200, [30, 30], H, Hkv, D)
+    O, S, st = orc.attention(Q, K, V, seq, pos, 0.25)
+    perm = np.random.default_rng(5).permutation(30)
+    Kp, Vp = K.copy(), V.copy()
+    Kp[0] = K[0, perm]
+    Vp[0] = V[0, perm]
+    last = np.array([29], np.int32)
+    Op, _, _ = orc.attention(Q[29:30], Kp, Vp, np.zeros(1, np.int32), last, 0.25)
+    _close(Op[0], O[29], 64 * U64 * S[29], "keys reordered")
+    order = np.random.default_rng(6).permutation(len(seq))
+    O2, S2, st2 = orc.attention(Q[order], K, V, seq[order], pos[order], 0.25)
+    assert np.array_equal(O2, O[order]) and np.array_equal(S2, S[order]) and np.array_equal(st2, st[order])
+    Qn = Q ^ np.uint16(0x8000)
+    On, _, stn = orc.attention(Qn, K, V, seq, pos, 0.25)
+    assert np.array_equal(stn, st), "stats under q -> -q"
+    assert not np.allclose(On[pos > 3], O[pos > 3]), "negating q changes the weights"
+    Qg = Q.copy()
+    Qg[:, 1] = Qg[:, 0]
+    Og, _, _ = orc.attention(Qg, K, V, seq, pos, 0.25)
+    assert np.array_equal(Og[:, 0], Og[:, 1]) and np.array_equal(Og[:, 2:], O[:, 2:])
+
+
 ALL_CHECKS = [check_sum_order, check_bruteforce_bf16, check_bruteforce_mx, check_integer_bf16,
               check_integer_mx, check_decoders, check_linspace_closed_form, check_linspace_bf16_row0,
               check_row_separability, check_mx_equals_prescaled_bf16, check_scale_shift, check_degenerate,
               check_decoder_f16, check_bruteforce_f16, check_integer_f16, check_i8,
-              check_rmsnorm_fsum, check_rmsnorm_closed_forms]
+              check_rmsnorm_fsum, check_rmsnorm_closed_forms,
+              check_attention_sdpa, check_attention_closed_forms, check_attention_invariances]

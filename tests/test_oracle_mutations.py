@@ -42,6 +42,19 @@ MUTATIONS = [
      "for (int64_t j = 0; j < D; ++j) G[j] = 1.0;"),
     ("x_scale_dropped", "A[i * K + k] = e4m3_table[X[i * ldx + k]] * oracle_decode_e8m0(XS[i * ldxs + k / 32]);",
      "A[i * K + k] = e4m3_table[X[i * ldx + k]];"),
+    ("attn_causal_exclusive", "const int64_t L = p + 1; /* keys j = 0 .. p */", "const int64_t L = p;"),
+    ("attn_no_scale", "s[j] = scale * d;", "s[j] = d;"),
+    ("attn_gqa_modulo", "const int64_t g = h / (H / Hkv);", "const int64_t g = h % Hkv;"),
+    ("attn_no_max_shift", "w[j] = exp(s[j] - m);", "w[j] = exp(s[j]);"),
+    ("attn_unnormalised", "O[(t * H + h) * D + e] = num / den;", "O[(t * H + h) * D + e] = num;"),
+    ("attn_v_next_position", "V[((sq * maxlen + j) * Hkv + g) * D + e]",
+     "V[((sq * maxlen + (j + 1 < L ? j + 1 : j)) * Hkv + g) * D + e]"),
+    ("attn_seq_ignored", "const int64_t sq = seq[t];", "const int64_t sq = 0;"),
+    ("attn_k_reversed", "q[e] * oracle_decode_bf16(k[e])", "q[e] * oracle_decode_bf16(k[D - 1 - e])"),
+    ("attn_q_first_head_of_group", "Q[(t * H + h) * D + e]", "Q[(t * H + g * (H / Hkv)) * D + e]"),
+    ("attn_s_signed", "nabs += w[j] * fabs(v);", "nabs += w[j] * v;"),
+    ("attn_a_signed", "da += fabs(prod);", "da += prod;"),
+    ("attn_range_from_zero", "stats[(t * H + h) * 3 + 2] = m - s_min;", "stats[(t * H + h) * 3 + 2] = m;"),
 ]
 
 
