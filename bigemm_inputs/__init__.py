@@ -27,7 +27,7 @@ __all__ = [
     "SEED_W", "SEED_C", "SEED_A", "SEED_B", "SEED_X", "SCALE_SEED_OFFSET",
     "f32_to_bf16_bits", "bf16_bits_to_f32", "normal_bf16", "int_bf16", "linspace_bf16",
     "f32_to_e4m3_codes", "normal_e4m3", "int_e4m3", "e8m0_scales", "e8m0_kvar_scales",
-    "row_positions", "ab_cell_rows", "position_cell_rows",
+    "row_positions", "ab_cell_rows", "position_cell_rows", "block_table", "seq_kv_bf16", "kv_bf16",
 ]
 
 # Seed roles (the pages give none; these are fixed here once).
@@ -46,13 +46,17 @@ def f32_to_bf16_bits(a) -> np.ndarray:
     NaN stays NaN (quiet). The inputs built here are always finite.
     """
     a = np.ascontiguousarray(np.asarray(a, dtype=np.float32))
-    u = a.view(np.uint32).astype(np.uint64)
-    lsb = (u >> np.uint64(16)) & np.uint64(1)
-    r = ((u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)).astype(np.uint16)
-    nan = np.isnan(a)
+    u = a.view(np.uint32).reshape(-1)
+    r = np.empty(u.shape, np.uint16)
+    # uint32 arithmetic in chunks: for every non-NaN pattern u + 0x8000 < 2^32
+    step = 1 << 22
+    for i in range(0, u.size, step):
+        v = u[i:i + step]
+        r[i:i + step] = ((v + (np.uint32(0x7FFF) + ((v >> np.uint32(16)) & np.uint32(1)))) >> np.uint32(16))
+    nan = np.isnan(a).reshape(-1)
     if nan.any():
-        r[nan] = ((u[nan] >> np.uint64(16)).astype(np.uint16) | np.uint16(0x0040))
-    return r
+        r[nan] = ((u[nan] >> np.uint32(16)).astype(np.uint16) | np.uint16(0x0040))
+    return r.reshape(a.shape)
 
 
 def bf16_bits_to_f32(b) -> np.ndarray:
@@ -207,3 +211,47 @@ def position_cell_rows(make_rows, M: int, row: int, seed_C: int = SEED_C, seed_f
     X = make_rows(seed_fill, M).copy()
     X[row] = C[0]
     return X, C
+
+
+# ------------------------------------------------------------------ paged KV cache
+def block_table(seed: int, lens, block_size: int, spare: int = 0, max_blocks: int = 0):
+    """A page table for sequences of lengths ``lens``: sequence s owns ceil(lens[s] /
+    block_size) physical blocks, drawn without repetition from a shuffled pool of all the
+    blocks needed plus ``spare`` unused ones. Returns (table [len(lens), max_blocks] int32,
+    padded with -1, and the pool size num_blocks). Layout only: no attention arithmetic."""
+    need = [-(-int(L) // block_size) for L in lens]
+    num_blocks = sum(need) + spare
+    pool = np.random.default_rng(seed).permutation(num_blocks).astype(np.int32)
+    width = max(max(need), max_blocks, 1)
+    table = np.full((len(lens), width), -1, np.int32)
+    off = 0
+    for s, n in enumerate(need):
+        table[s, :n] = pool[off:off + n]
+        off += n
+    return table, num_blocks
+
+
+def seq_kv_bf16(seed: int, s: int, L: int, Hkv: int, D: int):
+    """Keys and values of sequence s, N(0, 1) rounded to bf16, each [L, Hkv, D], drawn in
+    float32 from default_rng((seed, s)) — one stream per sequence, so sequences can be
+    made independently and in parallel."""
+    x = np.random.default_rng((seed, s)).standard_normal((2, L, Hkv, D), dtype=np.float32)
+    b = f32_to_bf16_bits(x)
+    return b[0], b[1]
+
+
+def kv_bf16(seed: int, lens, Hkv: int, D: int, threads: int = 8):
+    """Keys and values of every sequence, [len(lens), max(lens), Hkv, D] each (positions
+    past a sequence's length are zero), from seq_kv_bf16."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    lens = [int(L) for L in lens]
+    K = np.zeros((len(lens), max(lens), Hkv, D), np.uint16)
+    V = np.zeros_like(K)
+
+    def fill(s):
+        K[s, :lens[s]], V[s, :lens[s]] = seq_kv_bf16(seed, s, lens[s], Hkv, D)
+
+    with ThreadPoolExecutor(max(1, threads)) as ex:
+        list(ex.map(fill, range(len(lens))))
+    return K, V

@@ -29,7 +29,7 @@
 extern "C" {
 #endif
 
-#define BIGEMM_ABI_VERSION 4
+#define BIGEMM_ABI_VERSION 5
 
 /* Exported entry points (the library is built with hidden visibility by default). */
 #if defined(__GNUC__)
@@ -210,6 +210,119 @@ BIGEMM_API bigemm_status bigemm_rmsnorm(int32_t dtype, int64_t M, int64_t D,
 BIGEMM_API bigemm_status bigemm_rmsnorm_check_args(int32_t dtype, int64_t M, int64_t D,
                                         const void* X, int64_t ldx, const void* gamma,
                                         const void* Y, int64_t ldy);
+
+/*
+ * ---------------------------------------------------------------------------
+ * Batch-invariant paged attention (the nondeterminism blog, section
+ * "batch-invariant attention").
+ *
+ * A query token t of sequence seq_ids[t] at position positions[t] = i attends
+ * to the keys and values of that sequence at positions 0..i (the causal mask):
+ *   O[t, h] = sum_{j <= i} softmax_j(scale * Q[t, h] . K_j) V_j,
+ * with query head h reading key/value head h / (num_heads / num_kv_heads)
+ * (grouped-query attention). Decode is one token per sequence at its last
+ * position; a chunk of prefill is several tokens of one sequence at consecutive
+ * positions. The section's two rules are the interface:
+ *   - the KV cache and the page table are updated BEFORE attention:
+ *     bigemm_kv_cache_write puts the new tokens' keys and values into the
+ *     cache, then bigemm_paged_attention reads every position 0..i from the
+ *     cache in the same layout, whether it was cached by an earlier call or
+ *     written just now — so splitting a sequence into chunks, or processing
+ *     it all at once, does not change a token's result;
+ *   - the KV range is cut into splits of a FIXED SIZE, BIGEMM_ATTN_SPLIT
+ *     positions (never a fixed number of splits). Each split is reduced by one
+ *     workgroup in a fixed order (fp32), and the splits are merged in
+ *     ascending order; the merge is rounded once to the output type.
+ * So the bytes of O[t, :, :] depend only on Q[t], on the keys and values of
+ * positions 0..i of its sequence, on i and on scale — not on T, on the other
+ * tokens, on the token's index t, on which physical blocks hold the positions,
+ * on max_context or on the workspace. Repeated calls give identical bytes.
+ */
+#define BIGEMM_ATTN_SPLIT 256
+
+/*
+ * The paged KV cache. K and V are separate device arrays of bf16, each
+ *   [num_blocks][num_kv_heads][block_size][head_dim], row-major,
+ * and the block table is a device array of int32 [num_seqs][max_blocks]:
+ * position j of sequence s lives in block block_table[s][j / block_size] at
+ * row j % block_size. The caller owns the cache, assigns the blocks (the page
+ * table) and keeps each table row's entries for positions 0..i valid.
+ */
+typedef struct {
+  int32_t num_kv_heads;  /* >= 1                                          */
+  int32_t head_dim;      /* 64 or 128                                     */
+  int32_t block_size;    /* positions per block: a power of two, 1..4096  */
+  int32_t num_blocks;    /* blocks in each of K and V, >= 1               */
+  int32_t num_seqs;      /* rows of the block table, >= 1                 */
+  int32_t max_blocks;    /* entries per block-table row, >= 1             */
+} bigemm_kv_layout;
+
+/*
+ * Write the keys and values of T new tokens into the cache:
+ *   K_cache[slot(t, kvh)] = K_new[t, kvh, :], same for V, for every KV head,
+ * where slot is the row of position positions[t] of sequence seq_ids[t].
+ *   K_new, V_new [T][num_kv_heads][head_dim] bf16; seq_ids, positions [T] int32.
+ * A token whose sequence, position (< max_blocks * block_size) or block id
+ * (< num_blocks) is out of range is skipped; nothing outside the caches is
+ * written. Two tokens with the same slot race (the caller's error).
+ * Requirements (else BIGEMM_ERR_ARG, nothing launched): the layout as above,
+ * T >= 0 (0 is a no-op), T * num_kv_heads * head_dim / 8 < 2^31; pointers
+ * non-NULL when T > 0, the bf16 arrays 16-byte aligned, the int32 arrays
+ * 4-byte aligned. BIGEMM_ERR_UNSUPPORTED on a device other than gfx950.
+ * Enqueued on `stream`; allocates nothing.
+ */
+BIGEMM_API bigemm_status bigemm_kv_cache_write(const bigemm_kv_layout* kv, int64_t T,
+                                    const void* K_new, const void* V_new,
+                                    const int32_t* seq_ids, const int32_t* positions,
+                                    const int32_t* block_table,
+                                    void* K_cache, void* V_cache, void* stream);
+
+/*
+ * Device workspace, in bytes, for bigemm_paged_attention:
+ *   T * num_heads * ceil(max_context / BIGEMM_ATTN_SPLIT) * (head_dim + 2) * 4.
+ * Pure host function; BIGEMM_ERR_ARG for arguments bigemm_paged_attention
+ * would reject (other than pointers).
+ */
+BIGEMM_API bigemm_status bigemm_attn_workspace_size(const bigemm_kv_layout* kv, int64_t T, int32_t num_heads,
+                                         int32_t max_context, uint64_t* bytes);
+
+/*
+ * Enqueue the attention of T query tokens over the cache on `stream`.
+ *   Q [T][num_heads][head_dim] bf16; O [T][num_heads][head_dim], out_dtype
+ *   BIGEMM_F32 or BIGEMM_BF16; seq_ids, positions [T] int32 (device);
+ *   max_context: an upper bound on positions[t] + 1, at most
+ *   max_blocks * block_size (it sizes the grid and the workspace only);
+ *   scale: the score scale, normally 1/sqrt(head_dim) rounded to float.
+ * num_heads must be num_kv_heads times 1, 2, 4 or 8.
+ * Data-dependent cases, handled on the device without faulting: a token whose
+ * sequence or position is out of range (position >= max_context included)
+ * gets an all-NaN output; a block-table entry outside [0, num_blocks) reached
+ * by a token's positions makes that token's output NaN. Scores beyond the fp32
+ * range give inf or NaN.
+ * Requirements (else BIGEMM_ERR_ARG, nothing launched): the layout as above;
+ * T >= 0 (0 is a no-op); 1 <= max_context <= max_blocks * block_size; the
+ * grids T * num_kv_heads * splits and T * num_heads below 2^31; pointers
+ * non-NULL when T > 0, Q, the caches, O and the workspace 16-byte aligned, the
+ * int32 arrays 4-byte aligned; workspace_bytes >= bigemm_attn_workspace_size.
+ * O must not overlap the inputs or the workspace. The workspace is scratch for
+ * the call: calls sharing one must be ordered on one stream.
+ * BIGEMM_ERR_UNSUPPORTED on a device other than gfx950. Allocates nothing.
+ */
+BIGEMM_API bigemm_status bigemm_paged_attention(const bigemm_kv_layout* kv, int64_t T, int32_t num_heads,
+                                     int32_t max_context, float scale, int32_t out_dtype,
+                                     const void* Q, const void* K_cache, const void* V_cache,
+                                     const int32_t* seq_ids, const int32_t* positions,
+                                     const int32_t* block_table, void* O,
+                                     void* workspace, uint64_t workspace_bytes, void* stream);
+
+/* The argument checks of bigemm_paged_attention as a pure host function (no HIP call). */
+BIGEMM_API bigemm_status bigemm_paged_attention_check_args(const bigemm_kv_layout* kv, int64_t T,
+                                                int32_t num_heads, int32_t max_context,
+                                                int32_t out_dtype, const void* Q,
+                                                const void* K_cache, const void* V_cache,
+                                                const int32_t* seq_ids, const int32_t* positions,
+                                                const int32_t* block_table, const void* O,
+                                                const void* workspace, uint64_t workspace_bytes);
 
 /* Release a handle. NULL is accepted. */
 BIGEMM_API bigemm_status bigemm_destroy(bigemm_t h);

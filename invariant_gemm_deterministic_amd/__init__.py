@@ -21,6 +21,8 @@ __all__ = [
     "BigemmError", "bigemm_desc", "library_path", "load",
     "bigemm_create", "bigemm_run", "bigemm_destroy", "bigemm_status_str", "bigemm_get_config",
     "bigemm_check_args", "bigemm_abi_version", "mm",
+    "bigemm_kv_layout", "bigemm_kv_cache_write", "bigemm_attn_workspace_size", "bigemm_paged_attention",
+    "bigemm_paged_attention_check_args", "kv_cache_write", "paged_attention", "ATTN_SPLIT",
 ]
 
 BIGEMM_OK = 0
@@ -37,6 +39,8 @@ BIGEMM_F16 = 5
 BIGEMM_I8 = 6
 BIGEMM_I32 = 7
 
+ATTN_SPLIT = 256  # BIGEMM_ATTN_SPLIT: KV positions per split of the paged attention
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libbigemm.so")
 _lib = None
@@ -52,6 +56,11 @@ class BigemmError(RuntimeError):
 class bigemm_desc(ctypes.Structure):
     _fields_ = [("x_type", ctypes.c_int32), ("w_type", ctypes.c_int32),
                 ("y_type", ctypes.c_int32), ("scale_block", ctypes.c_int32)]
+
+
+class bigemm_kv_layout(ctypes.Structure):
+    _fields_ = [("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("num_blocks", ctypes.c_int32), ("num_seqs", ctypes.c_int32), ("max_blocks", ctypes.c_int32)]
 
 
 def library_path() -> str:
@@ -94,6 +103,17 @@ def load():
         lib.bigemm_run_ws.restype = ctypes.c_int
         lib.bigemm_run_ws.argtypes = [vp, i64, i64, i64, vp, i64, vp, i64, vp, i64, vp, i64, vp, i64, vp,
                                       ctypes.c_uint64, vp]
+        kvp = ctypes.POINTER(bigemm_kv_layout)
+        lib.bigemm_kv_cache_write.restype = ctypes.c_int
+        lib.bigemm_kv_cache_write.argtypes = [kvp, i64, vp, vp, vp, vp, vp, vp, vp, vp]
+        lib.bigemm_attn_workspace_size.restype = ctypes.c_int
+        lib.bigemm_attn_workspace_size.argtypes = [kvp, i64, i32, i32, ctypes.POINTER(ctypes.c_uint64)]
+        lib.bigemm_paged_attention.restype = ctypes.c_int
+        lib.bigemm_paged_attention.argtypes = [kvp, i64, i32, i32, ctypes.c_float, i32, vp, vp, vp, vp, vp, vp, vp,
+                                               vp, ctypes.c_uint64, vp]
+        lib.bigemm_paged_attention_check_args.restype = ctypes.c_int
+        lib.bigemm_paged_attention_check_args.argtypes = [kvp, i64, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp,
+                                                          ctypes.c_uint64]
         _lib = lib
         return lib
 
@@ -342,4 +362,137 @@ def rmsnorm(x, gamma, eps: float = 1e-6, out=None, stream=None):
         stream = torch.cuda.current_stream(x.device).cuda_stream
     with torch.cuda.device(x.device):
         bigemm_rmsnorm(dtype, M, D, x.data_ptr(), _ld(x), gamma.data_ptr(), out.data_ptr(), _ld(out), eps, stream)
+    return out
+
+
+# ------------------------------------------------------------------ paged attention
+def bigemm_kv_cache_write(kv: bigemm_kv_layout, T: int, K_new: int, V_new: int, seq_ids: int, positions: int,
+                          block_table: int, K_cache: int, V_cache: int, stream: int = 0, check: bool = True) -> int:
+    """Enqueue the KV-cache write of T tokens (device pointers as integers)."""
+    st = load().bigemm_kv_cache_write(ctypes.byref(kv), T, K_new or None, V_new or None, seq_ids or None,
+                                      positions or None, block_table or None, K_cache or None, V_cache or None,
+                                      stream or None)
+    if check and st != BIGEMM_OK:
+        raise BigemmError(st, "bigemm_kv_cache_write")
+    return int(st)
+
+
+def bigemm_attn_workspace_size(kv: bigemm_kv_layout, T: int, num_heads: int, max_context: int) -> int:
+    n = ctypes.c_uint64()
+    st = load().bigemm_attn_workspace_size(ctypes.byref(kv), T, num_heads, max_context, ctypes.byref(n))
+    if st != BIGEMM_OK:
+        raise BigemmError(st, "bigemm_attn_workspace_size")
+    return int(n.value)
+
+
+def bigemm_paged_attention(kv: bigemm_kv_layout, T: int, num_heads: int, max_context: int, scale: float,
+                           out_dtype: int, Q: int, K_cache: int, V_cache: int, seq_ids: int, positions: int,
+                           block_table: int, O: int, workspace: int, workspace_bytes: int, stream: int = 0,
+                           check: bool = True) -> int:
+    """Enqueue the batch-invariant paged attention (device pointers as integers)."""
+    st = load().bigemm_paged_attention(ctypes.byref(kv), T, num_heads, max_context, float(scale), int(out_dtype),
+                                       Q or None, K_cache or None, V_cache or None, seq_ids or None,
+                                       positions or None, block_table or None, O or None, workspace or None,
+                                       int(workspace_bytes), stream or None)
+    if check and st != BIGEMM_OK:
+        raise BigemmError(st, "bigemm_paged_attention")
+    return int(st)
+
+
+def bigemm_paged_attention_check_args(kv: bigemm_kv_layout, T: int, num_heads: int, max_context: int,
+                                      out_dtype: int, Q: int, K_cache: int, V_cache: int, seq_ids: int,
+                                      positions: int, block_table: int, O: int, workspace: int,
+                                      workspace_bytes: int) -> int:
+    return int(load().bigemm_paged_attention_check_args(
+        ctypes.byref(kv), T, num_heads, max_context, int(out_dtype), Q or None, K_cache or None, V_cache or None,
+        seq_ids or None, positions or None, block_table or None, O or None, workspace or None,
+        int(workspace_bytes)))
+
+
+def _kv_layout(k_cache, block_table):
+    """Layout of a cache tensor [num_blocks, num_kv_heads, block_size, head_dim] and its table."""
+    if k_cache.dim() != 4 or block_table.dim() != 2:
+        raise ValueError("k_cache must be [num_blocks, num_kv_heads, block_size, head_dim], block_table 2-D")
+    nb, hkv, bs, d = (int(v) for v in k_cache.shape)
+    return bigemm_kv_layout(hkv, d, bs, nb, int(block_table.shape[0]), int(block_table.shape[1]))
+
+
+def _check_cache_args(k_cache, v_cache, block_table, seq_ids, positions):
+    import torch
+
+    for t in (k_cache, v_cache, block_table, seq_ids, positions):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("cache, table and token arrays must be contiguous CUDA tensors")
+    if k_cache.shape != v_cache.shape or k_cache.dtype != v_cache.dtype or k_cache.element_size() != 2:
+        raise ValueError("k_cache and v_cache must be bf16 tensors of one shape")
+    for t in (block_table, seq_ids, positions):
+        if t.dtype != torch.int32:
+            raise ValueError("block_table, seq_ids and positions must be int32")
+
+
+def kv_cache_write(k_new, v_new, k_cache, v_cache, block_table, seq_ids, positions, stream=None):
+    """Write the keys/values of T new tokens (``k_new``, ``v_new`` [T, num_kv_heads, head_dim]
+    bf16) into the paged caches at the slots of (``seq_ids[t]``, ``positions[t]``)."""
+    import torch
+
+    _check_cache_args(k_cache, v_cache, block_table, seq_ids, positions)
+    kv = _kv_layout(k_cache, block_table)
+    T = int(seq_ids.shape[0])
+    want = (T, kv.num_kv_heads, kv.head_dim)
+    for t in (k_new, v_new):
+        if tuple(t.shape) != want or t.element_size() != 2 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"k_new and v_new must be contiguous bf16 CUDA tensors of shape {want}")
+    if stream is None:
+        stream = torch.cuda.current_stream(k_cache.device).cuda_stream
+    with torch.cuda.device(k_cache.device):
+        bigemm_kv_cache_write(kv, T, k_new.data_ptr(), v_new.data_ptr(), seq_ids.data_ptr(), positions.data_ptr(),
+                              block_table.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), stream)
+
+
+def paged_attention(q, k_cache, v_cache, block_table, seq_ids, positions, max_context=None, scale=None,
+                    out=None, out_dtype=None, workspace=None, stream=None):
+    """Batch-invariant attention of query tokens ``q`` [T, num_heads, head_dim] (bf16) over the
+    paged caches: token t attends to positions 0..positions[t] of sequence seq_ids[t].
+    ``max_context`` defaults to the table's capacity (max_blocks * block_size) — it sizes
+    the grid and the workspace, never the result; ``scale`` defaults to 1/sqrt(head_dim)
+    rounded to float32. Output ``out`` or a new [T, num_heads, head_dim] tensor of
+    ``out_dtype`` (float32 default, or bfloat16)."""
+    import math
+
+    import torch
+
+    _check_cache_args(k_cache, v_cache, block_table, seq_ids, positions)
+    kv = _kv_layout(k_cache, block_table)
+    if q.dim() != 3 or q.shape[2] != kv.head_dim or q.element_size() != 2 or not q.is_cuda \
+            or not q.is_contiguous():
+        raise ValueError("q must be a contiguous bf16 CUDA tensor [T, num_heads, head_dim]")
+    T, H = int(q.shape[0]), int(q.shape[1])
+    if int(seq_ids.shape[0]) != T or int(positions.shape[0]) != T:
+        raise ValueError("seq_ids and positions must have one entry per query token")
+    if max_context is None:
+        max_context = kv.max_blocks * kv.block_size
+    if scale is None:
+        import numpy as np
+        scale = float(np.float32(1.0 / math.sqrt(kv.head_dim)))
+    if out is not None:
+        out_dtype = out.dtype
+    elif out_dtype is None:
+        out_dtype = torch.float32
+    otypes = {torch.float32: BIGEMM_F32, torch.bfloat16: BIGEMM_BF16}
+    if out_dtype not in otypes:
+        raise ValueError(f"unsupported output dtype {out_dtype}")
+    if out is None:
+        out = torch.empty((T, H, kv.head_dim), dtype=out_dtype, device=q.device)
+    if tuple(out.shape) != (T, H, kv.head_dim) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [T, num_heads, head_dim] tensor")
+    need = bigemm_attn_workspace_size(kv, T, H, int(max_context))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    with torch.cuda.device(q.device):
+        bigemm_paged_attention(kv, T, H, int(max_context), scale, otypes[out_dtype], q.data_ptr(),
+                               k_cache.data_ptr(), v_cache.data_ptr(), seq_ids.data_ptr(), positions.data_ptr(),
+                               block_table.data_ptr(), out.data_ptr(), workspace.data_ptr(), ws_bytes, stream)
     return out

@@ -9,6 +9,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libbigemm.so")
 SOURCES = [os.path.join(CSRC, "bigemm_kernels.hip"), os.path.join(CSRC, "bigemm_rmsnorm.hip"),
+           os.path.join(CSRC, "bigemm_attention.hip"),
            os.path.join(CSRC, "bigemm_api.cpp")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -16,6 +16,7 @@
 
 #include "../../include/bigemm.h"
 #include "bigemm_kernels.h"
+#include "bigemm_attention.h"
 #include "bigemm_rmsnorm.h"
 
 struct bigemm_s {
@@ -119,7 +120,145 @@ hipError_t launch_unsplit(bigemm::Op op, int64_t M, int64_t N, int64_t K, const 
   return bigemm::launch_bf16(op, X, W, Y, M, N, K, ldx, ldw, ldy, stream);
 }
 
+// ------------------------------------------------------------------ attention
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
+int log2_exact(int32_t v) {
+  if (v < 1 || (v & (v - 1)) != 0) return -1;
+  int k = 0;
+  while ((1 << k) != v) ++k;
+  return k;
+}
+
+bigemm_status kv_layout_check(const bigemm_kv_layout* kv) {
+  if (!kv) return BIGEMM_ERR_ARG;
+  if (kv->num_kv_heads < 1 || (kv->head_dim != 64 && kv->head_dim != 128)) return BIGEMM_ERR_ARG;
+  if (kv->block_size > 4096 || log2_exact(kv->block_size) < 0) return BIGEMM_ERR_ARG;
+  if (kv->num_blocks < 1 || kv->num_seqs < 1 || kv->max_blocks < 1) return BIGEMM_ERR_ARG;
+  return BIGEMM_OK;
+}
+
+// Sizes of a paged-attention call; fills nsplit and the workspace bytes.
+bigemm_status attn_sizes(const bigemm_kv_layout* kv, int64_t T, int32_t H, int32_t max_context, int32_t* nsplit,
+                         uint64_t* need) {
+  const bigemm_status st = kv_layout_check(kv);
+  if (st != BIGEMM_OK) return st;
+  if (T < 0 || H < 1 || H % kv->num_kv_heads != 0) return BIGEMM_ERR_ARG;
+  const int32_t G = H / kv->num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return BIGEMM_ERR_ARG;
+  if (max_context < 1 || (int64_t)max_context > (int64_t)kv->max_blocks * kv->block_size) return BIGEMM_ERR_ARG;
+  const int64_t ns = ((int64_t)max_context + bigemm::kAttnSplit - 1) / bigemm::kAttnSplit;
+  if (T * kv->num_kv_heads * ns > INT32_MAX || T * H > INT32_MAX) return BIGEMM_ERR_ARG;
+  *nsplit = (int32_t)ns;
+  *need = (uint64_t)T * (uint64_t)H * (uint64_t)ns * (uint64_t)(kv->head_dim + 2) * 4u;
+  return BIGEMM_OK;
+}
+
+bigemm_status attn_check(const bigemm_kv_layout* kv, int64_t T, int32_t H, int32_t max_context, int32_t out_dtype,
+                         const void* Q, const void* Kc, const void* Vc, const int32_t* seq, const int32_t* pos,
+                         const int32_t* bt, const void* O, const void* ws, uint64_t ws_bytes, int32_t* nsplit) {
+  if (out_dtype != BIGEMM_F32 && out_dtype != BIGEMM_BF16) return BIGEMM_ERR_UNSUPPORTED;
+  uint64_t need = 0;
+  const bigemm_status st = attn_sizes(kv, T, H, max_context, nsplit, &need);
+  if (st != BIGEMM_OK || T == 0) return st;
+  if (!Q || !Kc || !Vc || !seq || !pos || !bt || !O || !ws) return BIGEMM_ERR_ARG;
+  if (!aligned16(Q) || !aligned16(Kc) || !aligned16(Vc) || !aligned16(O) || !aligned16(ws)) return BIGEMM_ERR_ARG;
+  if (!aligned4(seq) || !aligned4(pos) || !aligned4(bt)) return BIGEMM_ERR_ARG;
+  if (ws_bytes < need) return BIGEMM_ERR_ARG;
+  return BIGEMM_OK;
+}
+
 }  // namespace
+
+bigemm_status bigemm_kv_cache_write(const bigemm_kv_layout* kv, int64_t T, const void* K_new, const void* V_new,
+                                    const int32_t* seq_ids, const int32_t* positions, const int32_t* block_table,
+                                    void* K_cache, void* V_cache, void* stream) {
+  const bigemm_status st = kv_layout_check(kv);
+  if (st != BIGEMM_OK) return st;
+  if (T < 0 || T * kv->num_kv_heads * (kv->head_dim / 8) >= (int64_t)INT32_MAX) return BIGEMM_ERR_ARG;
+  if (T == 0) return BIGEMM_OK;
+  if (!K_new || !V_new || !seq_ids || !positions || !block_table || !K_cache || !V_cache) return BIGEMM_ERR_ARG;
+  if (!aligned16(K_new) || !aligned16(V_new) || !aligned16(K_cache) || !aligned16(V_cache)) return BIGEMM_ERR_ARG;
+  if (!aligned4(seq_ids) || !aligned4(positions) || !aligned4(block_table)) return BIGEMM_ERR_ARG;
+  const bigemm_status dv = current_device_supported();
+  if (dv != BIGEMM_OK) return dv;
+  bigemm::KvWriteParams p;
+  p.K_new = (const uint16_t*)K_new;
+  p.V_new = (const uint16_t*)V_new;
+  p.seq_ids = seq_ids;
+  p.positions = positions;
+  p.block_table = block_table;
+  p.K = (uint16_t*)K_cache;
+  p.V = (uint16_t*)V_cache;
+  p.T = (int32_t)T;
+  p.Hkv = kv->num_kv_heads;
+  p.D = kv->head_dim;
+  p.bs_log2 = log2_exact(kv->block_size);
+  p.num_blocks = kv->num_blocks;
+  p.num_seqs = kv->num_seqs;
+  p.max_blocks = kv->max_blocks;
+  const hipError_t e = bigemm::launch_kv_write(p, (hipStream_t)stream);
+  return e == hipSuccess ? BIGEMM_OK : BIGEMM_ERR_DEVICE;
+}
+
+bigemm_status bigemm_attn_workspace_size(const bigemm_kv_layout* kv, int64_t T, int32_t num_heads,
+                                         int32_t max_context, uint64_t* bytes) {
+  if (!bytes) return BIGEMM_ERR_ARG;
+  int32_t ns = 0;
+  uint64_t need = 0;
+  const bigemm_status st = attn_sizes(kv, T, num_heads, max_context, &ns, &need);
+  if (st != BIGEMM_OK) return st;
+  *bytes = need;
+  return BIGEMM_OK;
+}
+
+bigemm_status bigemm_paged_attention_check_args(const bigemm_kv_layout* kv, int64_t T, int32_t num_heads,
+                                                int32_t max_context, int32_t out_dtype, const void* Q,
+                                                const void* K_cache, const void* V_cache, const int32_t* seq_ids,
+                                                const int32_t* positions, const int32_t* block_table,
+                                                const void* O, const void* workspace, uint64_t workspace_bytes) {
+  int32_t ns = 0;
+  return attn_check(kv, T, num_heads, max_context, out_dtype, Q, K_cache, V_cache, seq_ids, positions,
+                    block_table, O, workspace, workspace_bytes, &ns);
+}
+
+bigemm_status bigemm_paged_attention(const bigemm_kv_layout* kv, int64_t T, int32_t num_heads, int32_t max_context,
+                                     float scale, int32_t out_dtype, const void* Q, const void* K_cache,
+                                     const void* V_cache, const int32_t* seq_ids, const int32_t* positions,
+                                     const int32_t* block_table, void* O, void* workspace,
+                                     uint64_t workspace_bytes, void* stream) {
+  int32_t ns = 0;
+  const bigemm_status st = attn_check(kv, T, num_heads, max_context, out_dtype, Q, K_cache, V_cache, seq_ids,
+                                      positions, block_table, O, workspace, workspace_bytes, &ns);
+  if (st != BIGEMM_OK || T == 0) return st;
+  const bigemm_status dv = current_device_supported();
+  if (dv != BIGEMM_OK) return dv;
+  bigemm::AttnParams p;
+  p.Q = (const uint16_t*)Q;
+  p.K = (const uint16_t*)K_cache;
+  p.V = (const uint16_t*)V_cache;
+  p.seq_ids = seq_ids;
+  p.positions = positions;
+  p.block_table = block_table;
+  p.O = O;
+  p.ws_acc = (float*)workspace;
+  p.ws_ml = (float*)workspace + (int64_t)T * num_heads * ns * kv->head_dim;
+  p.T = (int32_t)T;
+  p.H = num_heads;
+  p.Hkv = kv->num_kv_heads;
+  p.D = kv->head_dim;
+  p.bs_log2 = log2_exact(kv->block_size);
+  p.num_blocks = kv->num_blocks;
+  p.num_seqs = kv->num_seqs;
+  p.max_blocks = kv->max_blocks;
+  p.max_context = max_context;
+  p.nsplit = ns;
+  p.scale = scale;
+  p.out_bf16 = out_dtype == BIGEMM_BF16;
+  const hipError_t e = bigemm::launch_paged_attention(p, (hipStream_t)stream);
+  return e == hipSuccess ? BIGEMM_OK : BIGEMM_ERR_DEVICE;
+}
+
 
 extern "C" {
 

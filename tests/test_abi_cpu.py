@@ -24,7 +24,8 @@ def test_header_declares_the_boundary():
     for name in ("bigemm_create", "bigemm_run", "bigemm_destroy", "bigemm_status_str",
                  "bigemm_get_config", "bigemm_check_args", "bigemm_abi_version",
                  "bigemm_create_split_k", "bigemm_workspace_size", "bigemm_run_ws",
-                 "bigemm_rmsnorm", "bigemm_rmsnorm_check_args"):
+                 "bigemm_rmsnorm", "bigemm_rmsnorm_check_args", "bigemm_kv_cache_write",
+                 "bigemm_attn_workspace_size", "bigemm_paged_attention", "bigemm_paged_attention_check_args"):
         assert name in fns
 
 
@@ -35,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert bg.bigemm_abi_version() == 4
+    assert bg.bigemm_abi_version() == 5
     for s in range(5):
         assert bg.bigemm_status_str(s)
     assert "unknown" in bg.bigemm_status_str(99)
@@ -140,3 +141,44 @@ def test_rmsnorm_check_args():
     assert ok(bg.BIGEMM_BF16, 16, 64, A + 2, 64, A, A, 64) == bg.BIGEMM_ERR_ARG
     assert ok(bg.BIGEMM_BF16, 16, 64, A, 64, 0, A, 64) == bg.BIGEMM_ERR_ARG
     assert ok(bg.BIGEMM_E4M3, 16, 64, A, 64, A, A, 64) == bg.BIGEMM_ERR_UNSUPPORTED
+
+
+def _kv(**kw):
+    f = dict(num_kv_heads=2, head_dim=128, block_size=32, num_blocks=10, num_seqs=2, max_blocks=4)
+    f.update(kw)
+    return bg.bigemm_kv_layout(*(f[k] for k in ("num_kv_heads", "head_dim", "block_size", "num_blocks", "num_seqs",
+                                                "max_blocks")))
+
+
+def achk(kv=None, T=3, H=4, mc=128, odt=bg.BIGEMM_F32, Q=A, K=A, V=A, s=A, p=A, bt=A, O=A, ws=A, wsb=1 << 30):
+    return bg.bigemm_paged_attention_check_args(kv or _kv(), T, H, mc, odt, Q, K, V, s, p, bt, O, ws, wsb)
+
+
+def test_paged_attention_check_args():
+    OK, ARG = bg.BIGEMM_OK, bg.BIGEMM_ERR_ARG
+    assert achk() == OK
+    assert achk(odt=bg.BIGEMM_BF16) == OK
+    assert achk(T=0, Q=0, K=0, V=0, s=0, p=0, bt=0, O=0, ws=0, wsb=0) == OK
+    for H in (2, 8, 16):
+        assert achk(H=H) == OK, H
+    for H in (0, 3, 6, 32):  # not a multiple of 2 KV heads, or a group of 3 or 16
+        assert achk(H=H) == ARG, H
+    assert achk(kv=_kv(head_dim=64)) == OK and achk(kv=_kv(head_dim=96)) == ARG
+    for bs, ok in ((1, OK), (4096, OK), (24, ARG), (0, ARG), (8192, ARG)):
+        assert achk(kv=_kv(block_size=bs), mc=1) == ok, bs
+    for f in ("num_kv_heads", "num_blocks", "num_seqs", "max_blocks"):
+        assert achk(kv=_kv(**{f: 0})) == ARG, f
+    assert achk(mc=0) == ARG and achk(mc=129) == ARG and achk(mc=1) == OK  # capacity 4 * 32
+    assert achk(T=-1) == ARG
+    assert achk(odt=bg.BIGEMM_I32) == bg.BIGEMM_ERR_UNSUPPORTED
+    for name in ("Q", "K", "V", "O", "ws"):
+        assert achk(**{name: A + 4}) == ARG, name
+        assert achk(**{name: 0}) == ARG, name
+    for name in ("s", "p", "bt"):
+        assert achk(**{name: A + 4}) == OK and achk(**{name: A + 2}) == ARG and achk(**{name: 0}) == ARG, name
+    need = bg.bigemm_attn_workspace_size(_kv(), 3, 4, 128)
+    assert need == 3 * 4 * 1 * 130 * 4
+    assert achk(wsb=need) == OK and achk(wsb=need - 1) == ARG
+    assert bg.bigemm_attn_workspace_size(_kv(max_blocks=40), 5, 8, 1280) == 5 * 8 * 5 * 130 * 4
+    assert bg.bigemm_attn_workspace_size(_kv(max_blocks=41), 5, 8, 1281) == 5 * 8 * 6 * 130 * 4
+    assert bg.load().bigemm_kv_cache_write(None, 1, None, None, None, None, None, None, None, None) == ARG
