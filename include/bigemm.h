@@ -231,8 +231,9 @@ BIGEMM_API bigemm_status bigemm_rmsnorm_check_args(int32_t dtype, int64_t M, int
  *     it all at once, does not change a token's result;
  *   - the KV range is cut into splits of a FIXED SIZE, BIGEMM_ATTN_SPLIT
  *     positions (never a fixed number of splits). Each split is reduced by one
- *     workgroup in a fixed order (fp32), and the splits are merged in
- *     ascending order; the merge is rounded once to the output type.
+ *     workgroup in a fixed order (fp32), and the splits are merged in a
+ *     fixed tree that depends only on their number; the merge is rounded once
+ *     to the output type.
  * So the bytes of O[t, :, :] depend only on Q[t], on the keys and values of
  * positions 0..i of its sequence, on i and on scale — not on T, on the other
  * tokens, on the token's index t, on which physical blocks hold the positions,
@@ -301,7 +302,7 @@ BIGEMM_API bigemm_status bigemm_attn_workspace_size(const bigemm_kv_layout* kv, 
  * range give inf or NaN.
  * Requirements (else BIGEMM_ERR_ARG, nothing launched): the layout as above;
  * T >= 0 (0 is a no-op); 1 <= max_context <= max_blocks * block_size; the
- * grids T * num_kv_heads * splits and T * num_heads below 2^31; pointers
+ * grids T * num_kv_heads * splits and T * num_heads * head_dim / 32 below 2^31; pointers
  * non-NULL when T > 0, Q, the caches, O and the workspace 16-byte aligned, the
  * int32 arrays 4-byte aligned; workspace_bytes >= bigemm_attn_workspace_size.
  * O must not overlap the inputs or the workspace. The workspace is scratch for

@@ -148,7 +148,7 @@ bigemm_status attn_sizes(const bigemm_kv_layout* kv, int64_t T, int32_t H, int32
   if (G != 1 && G != 2 && G != 4 && G != 8) return BIGEMM_ERR_ARG;
   if (max_context < 1 || (int64_t)max_context > (int64_t)kv->max_blocks * kv->block_size) return BIGEMM_ERR_ARG;
   const int64_t ns = ((int64_t)max_context + bigemm::kAttnSplit - 1) / bigemm::kAttnSplit;
-  if (T * kv->num_kv_heads * ns > INT32_MAX || T * H > INT32_MAX) return BIGEMM_ERR_ARG;
+  if (T * kv->num_kv_heads * ns > INT32_MAX || T * H * (kv->head_dim / 32) > INT32_MAX) return BIGEMM_ERR_ARG;
   *nsplit = (int32_t)ns;
   *need = (uint64_t)T * (uint64_t)H * (uint64_t)ns * (uint64_t)(kv->head_dim + 2) * 4u;
   return BIGEMM_OK;

@@ -29,8 +29,9 @@
 // Every butterfly step adds two partial sums of fixed, disjoint position sets,
 // so each split result is a fixed function of that split's inputs.
 // Merge kernel: per (token, query head), the splits' (m_s, l_s, acc_s) are
-// combined in ascending split order: m = max_s m_s, w_s = exp(m_s - m),
-// o = (sum_s w_s acc_s) / (sum_s w_s l_s), rounded once to the output type.
+// combined as m = max_s m_s, w_s = exp(m_s - m),
+// o = (sum_s w_s acc_s) / (sum_s w_s l_s), the sums in a fixed tree that depends
+// on the number of splits only, rounded once to the output type.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -64,22 +65,72 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(uint32_t u) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-// v[0..N) of every lane of an aligned group of N lanes (lane bits below N) are
-// partial sums over disjoint sets; afterwards v[0] of lane i holds the total of
-// index i. Step `half` pairs lanes that differ in that bit: each keeps the half
-// its bit selects and adds the partner's copy of it.
+// Cross-lane moves. DPP: row_mirror pairs lane i of a 16-lane row with 15 - i,
+// row_half_mirror pairs i with 7 - i inside each half row, the two quad
+// permutations swap neighbours at distance 2 and 1, row_ror:8 pairs i with i ^ 8.
+constexpr int kDppRowMirror = 0x140, kDppHalfMirror = 0x141, kDppQuadXor2 = 0x4E, kDppQuadXor1 = 0xB1,
+              kDppRor8 = 0x128;
+
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xF, 0xF, false));
+}
+
+// One reduce-scatter step between partner lanes (partner differs in the bit
+// `hi` tests and agrees on the bits already reduced): lanes with hi clear keep
+// index k (own a + partner's a), lanes with hi set keep index k + half (own b +
+// partner's b). Each kept sum is formed by exactly one lane.
+template <int kCtrl>
+__device__ __forceinline__ float rs_pair(float a, float b, bool hi) {
+  const float sa = a + dpp<kCtrl>(a);
+  const float sb = b + dpp<kCtrl>(b);
+  return hi ? sb : sa;
+}
+
+// v[0..N) of every lane of an aligned group of N lanes (N = 16 or 8, a row or
+// half row) are partial sums over disjoint sets; afterwards v[0] of lane i
+// holds the total of index i (the lane keeps, at each step, the half its own
+// bit selects).
 template <int N>
 __device__ __forceinline__ void reduce_scatter(float (&v)[N], int lane) {
+  static_assert(N == 16 || N == 8, "a row or half row of lanes");
+  if constexpr (N == 16) {
 #pragma unroll
-  for (int half = N / 2; half >= 1; half /= 2) {
-    const bool hi = (lane & half) != 0;
-#pragma unroll
-    for (int k = 0; k < half; ++k) {
-      const float send = hi ? v[k] : v[k + half];
-      const float keep = hi ? v[k + half] : v[k];
-      v[k] = keep + __shfl_xor(send, half);
-    }
+    for (int k = 0; k < 8; ++k) v[k] = rs_pair<kDppRowMirror>(v[k], v[k + 8], (lane & 8) != 0);
   }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) v[k] = rs_pair<kDppHalfMirror>(v[k], v[k + 4], (lane & 4) != 0);
+#pragma unroll
+  for (int k = 0; k < 2; ++k) v[k] = rs_pair<kDppQuadXor2>(v[k], v[k + 2], (lane & 2) != 0);
+  v[0] = rs_pair<kDppQuadXor1>(v[0], v[1], (lane & 1) != 0);
+}
+
+// The same over the groups of a wave (lane bits 32, 16 and, for 8-lane groups,
+// 8): v_permlane32_swap / v_permlane16_swap exchange the halves directly, so
+// that a' + b' is own + partner for the kept index. Afterwards lane l holds
+// indices [off, off + N >> steps) where off adds N/2 for lane bit 32, N/4 for
+// bit 16 (and N/8 for bit 8).
+template <int N, int kL>
+__device__ __forceinline__ int reduce_scatter_groups(float (&v)[N], int lane) {
+#pragma unroll
+  for (int k = 0; k < N / 2; ++k) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[k]), __float_as_uint(v[k + N / 2]), false,
+                                                    false);
+    v[k] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+#pragma unroll
+  for (int k = 0; k < N / 4; ++k) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[k]), __float_as_uint(v[k + N / 4]), false,
+                                                    false);
+    v[k] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  int off = ((lane & 32) ? N / 2 : 0) + ((lane & 16) ? N / 4 : 0);
+  if constexpr (kL == 8) {
+#pragma unroll
+    for (int k = 0; k < N / 8; ++k) v[k] = rs_pair<kDppRor8>(v[k], v[k + N / 8], (lane & 8) != 0);
+    off += (lane & 8) ? N / 8 : 0;
+  }
+  return off;
 }
 
 __device__ __forceinline__ int64_t slot_row(int blk, int Hkv, int kvh, int bs_log2, int j) {
@@ -139,17 +190,6 @@ void bigemm_attn_split_kernel(AttnParams p) {
     }
   }
 
-  const int own = grp + kGroups * gl;  // the position whose score this thread ends with
-  float sh[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float sc[kPer];
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) sc[i] = dot8(q[h], kr[i]);
-    reduce_scatter<kPer>(sc, gl);
-    sh[h] = own < n ? sc[0] * p.scale : -INFINITY;
-  }
-
   i32x4 vr[kPer];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
@@ -162,6 +202,17 @@ void bigemm_attn_split_kernel(AttnParams p) {
       if (blk >= 0 && blk < p.num_blocks)
         vr[i] = *(const i32x4*)(p.V + slot_row(blk, p.Hkv, kvh, p.bs_log2, j) * D + gl * 8);
     }
+  }
+
+  const int own = grp + kGroups * gl;  // the position whose score this thread ends with
+  float sh[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float sc[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) sc[i] = dot8(q[h], kr[i]);
+    reduce_scatter<kPer>(sc, gl);
+    sh[h] = own < n ? sc[0] * p.scale : -INFINITY;
   }
 
   // softmax statistics of the split, per head
@@ -216,23 +267,8 @@ void bigemm_attn_split_kernel(AttnParams p) {
     }
   }
 
-  // reduce-scatter over the groups of this wave (lane bits kL .. 32)
-  int off = 0;
-  int half = kAcc / 2;
-#pragma unroll
-  for (int mask = 32; mask >= kL; mask >>= 1) {
-    const bool hi = (lane & mask) != 0;
-#pragma unroll
-    for (int k = 0; k < kAcc / 2; ++k) {
-      if (k < half) {
-        const float send = hi ? acc[k] : acc[k + half];
-        const float keep = hi ? acc[k + half] : acc[k];
-        acc[k] = keep + __shfl_xor(send, mask);
-      }
-    }
-    if (hi) off += half;
-    half /= 2;
-  }
+  // reduce-scatter over the groups of this wave
+  const int off = reduce_scatter_groups<kAcc, kL>(acc, lane);
   constexpr int kOwn = kAcc * kL / 64;  // values each lane owns afterwards
 #pragma unroll
   for (int k = 0; k < kOwn; ++k) {
@@ -256,30 +292,82 @@ void bigemm_attn_split_kernel(AttnParams p) {
   }
 }
 
+// Merge: one workgroup per (token, query head, slice of kMergeE output
+// elements), so that long contexts (many splits) still spread over the chip.
+//   m = max_s m_s (exact in any order), then per chunk of 256 splits the weights
+//   w_s = exp(m_s - m) and l_s go to LDS;
+//   thread (e, r), r < R = 256 / kMergeE, takes splits s = r + R j in ascending
+//   order into kU interleaved fp32 accumulators (split s to accumulator
+//   (s / R) % kU), adds them in a fixed tree, then the R partials in ascending r.
+// The tree depends on the number of splits only.
+constexpr int kMergeE = 32;
+
 template <int D, bool kBf16>
-__global__ __launch_bounds__(D)
+__global__ __launch_bounds__(kThreads)
 void bigemm_attn_merge_kernel(AttnParams p) {
-  const int th = blockIdx.x;  // t * H + h
+  constexpr int R = kThreads / kMergeE;
+  constexpr int kU = 4;
+  constexpr int kChunk = kThreads;
+  static_assert(kChunk % (R * kU) == 0, "chunks keep the accumulator of every split");
+  __shared__ float w_s[kChunk];
+  __shared__ float l_s[kChunk];
+  __shared__ float red[4];
+  __shared__ float part_a[R][kMergeE];
+  __shared__ float part_l[R][kMergeE];
+  constexpr int kSlices = D / kMergeE;
+  const int th = blockIdx.x / kSlices;  // t * H + h
+  const int e = (blockIdx.x % kSlices) * kMergeE + threadIdx.x % kMergeE;
+  const int r = threadIdx.x / kMergeE;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t = th / p.H;
-  const int e = threadIdx.x;
   const int sq = p.seq_ids[t], pos = p.positions[t];
-  float o;
-  if (sq < 0 || sq >= p.num_seqs || pos < 0 || pos >= p.max_context) {
-    o = __builtin_nanf("");
-  } else {
-    const int ns = pos / kAttnSplit + 1;
-    const float* ml = p.ws_ml + (int64_t)th * p.nsplit * 2;
-    const float* ac = p.ws_acc + (int64_t)th * p.nsplit * D + e;
-    float mx = ml[0];
-    for (int s = 1; s < ns; ++s) mx = fmaxf(mx, ml[2 * s]);
-    float l = 0.f, a = 0.f;
-    for (int s = 0; s < ns; ++s) {
-      const float w = expf(ml[2 * s] - mx);
-      l = fmaf(w, ml[2 * s + 1], l);
-      a = fmaf(w, ac[(int64_t)s * D], a);
+  const bool valid = !(sq < 0 || sq >= p.num_seqs || pos < 0 || pos >= p.max_context);
+  const int ns = valid ? pos / kAttnSplit + 1 : 0;
+  const float* ml = p.ws_ml + (int64_t)th * p.nsplit * 2;
+  const float* ac = p.ws_acc + (int64_t)th * p.nsplit * D + e;
+
+  float mloc = -INFINITY;
+  for (int s = tid; s < ns; s += kThreads) mloc = fmaxf(mloc, ml[2 * s]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, off));
+  if (lane == 0) red[wave] = mloc;
+  __syncthreads();
+  const float mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+
+  float la[kU], aa[kU];
+#pragma unroll
+  for (int u = 0; u < kU; ++u) la[u] = aa[u] = 0.f;
+  for (int c0 = 0; c0 < ns; c0 += kChunk) {
+    if (c0 + tid < ns) {
+      w_s[tid] = expf(ml[2 * (c0 + tid)] - mx);
+      l_s[tid] = ml[2 * (c0 + tid) + 1];
     }
-    o = a / l;
+    __syncthreads();
+    const int cn = min(kChunk, ns - c0);
+    for (int j0 = r; j0 < cn; j0 += R * kU) {
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int j = j0 + u * R;
+        if (j < cn) {
+          la[u] = fmaf(w_s[j], l_s[j], la[u]);
+          aa[u] = fmaf(w_s[j], ac[(int64_t)(c0 + j) * D], aa[u]);
+        }
+      }
+    }
+    __syncthreads();
   }
+  part_l[r][threadIdx.x % kMergeE] = (la[0] + la[1]) + (la[2] + la[3]);
+  part_a[r][threadIdx.x % kMergeE] = (aa[0] + aa[1]) + (aa[2] + aa[3]);
+  __syncthreads();
+  if (r != 0) return;
+  const int ei = threadIdx.x;
+  float l = part_l[0][ei], a = part_a[0][ei];
+#pragma unroll
+  for (int i = 1; i < R; ++i) {
+    l += part_l[i][ei];
+    a += part_a[i][ei];
+  }
+  const float o = valid ? a / l : __builtin_nanf("");
   if (kBf16)
     ((uint16_t*)p.O)[(int64_t)th * D + e] = (uint16_t)f32_to_bf16_rne(__float_as_uint(o));
   else
@@ -318,11 +406,11 @@ void launch_split(const AttnParams& p, hipStream_t stream) {
 
 template <int D>
 void launch_merge(const AttnParams& p, hipStream_t stream) {
-  const dim3 grid((unsigned)((int64_t)p.T * p.H));
+  const dim3 grid((unsigned)((int64_t)p.T * p.H * (D / kMergeE)));
   if (p.out_bf16)
-    hipLaunchKernelGGL((bigemm_attn_merge_kernel<D, true>), grid, dim3(D), 0, stream, p);
+    hipLaunchKernelGGL((bigemm_attn_merge_kernel<D, true>), grid, dim3(kThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL((bigemm_attn_merge_kernel<D, false>), grid, dim3(D), 0, stream, p);
+    hipLaunchKernelGGL((bigemm_attn_merge_kernel<D, false>), grid, dim3(kThreads), 0, stream, p);
 }
 
 }  // namespace
