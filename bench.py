@@ -15,6 +15,10 @@ ABI with inputs resident in HBM. Also reported:
   LLC) and on the long-K workload, against the unsplit kernel (context);
 * ``rmsnorm_bf16_context``: the batch-invariant RMSNorm (bf16, D = 4096) against
   the HBM peak (context);
+* ``paged_attention_decode_context``: the batch-invariant paged attention
+  (fixed 256-position KV splits, bf16 cache in blocks of 32, one query token
+  per sequence at its last position, fp32 output) for several batch / context
+  / head shapes, with algorithmic HBM GB/s against the HBM peak (context);
 * ``invariance_byte_diffs``: every row of every sweep result compared with the
   same row of the M = 4096 result (must be 0);
 * ``roofline``: the kernel's algorithmic flops per launch over its average
@@ -226,6 +230,43 @@ def main():
                          "pct_hbm_peak": round(100 * byts / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 1)})
             del XN, YN
 
+    # ----------------------------------------- paged attention, decode (context)
+    # Algorithmic bytes per call: the K and V rows of every context position read
+    # once (B*L*Hkv*D*2 bytes each), Q read, O written (fp32), and the split
+    # partials (B*H*splits*(D+2)*4 bytes) written once and read once. Inputs are
+    # N(0,1) bf16 from torch's seeded generator on the device (the timing does
+    # not depend on the values); blocks are assigned by a seeded permutation.
+    attn = []
+    if not args.no_sweep:
+        gen = torch.Generator(device=dev)
+        for (B, L, Hq, Hkv, D) in ((64, 4096, 32, 8, 128), (64, 4096, 64, 8, 128), (64, 4096, 8, 8, 128),
+                                   (8, 32768, 32, 8, 128), (1, 131072, 32, 8, 128), (64, 4096, 32, 8, 64)):
+            gen.manual_seed(B * 7 + L)
+            bs = 32
+            nbps = L // bs
+            kc = torch.randn((B * nbps, Hkv, bs, D), device=dev, generator=gen).to(torch.bfloat16)
+            vc = torch.randn((B * nbps, Hkv, bs, D), device=dev, generator=gen).to(torch.bfloat16)
+            bt = torch.randperm(B * nbps, device=dev, generator=gen).to(torch.int32).reshape(B, nbps)
+            q = torch.randn((B, Hq, D), device=dev, generator=gen).to(torch.bfloat16)
+            seqs = torch.arange(B, device=dev, dtype=torch.int32)
+            poss = torch.full((B,), L - 1, device=dev, dtype=torch.int32)
+            o = torch.empty((B, Hq, D), device=dev, dtype=torch.float32)
+            need = bg.bigemm_attn_workspace_size(bg._kv_layout(kc, bt), B, Hq, L)
+            wsa = torch.empty(need, dtype=torch.uint8, device=dev)
+
+            def call(i):
+                bg.paged_attention(q, kc, vc, bt, seqs, poss, max_context=L, out=o, workspace=wsa)
+
+            for i in range(3):
+                call(i)
+            t = _events(torch, stream, call, 20)
+            byts = 4 * B * L * Hkv * D + 2 * B * Hq * D + 4 * B * Hq * D + 2 * need
+            attn.append({"B": B, "context": L, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "us": round(t * 1e3, 2),
+                         "gbs_algorithmic": round(byts / (t * 1e-3) / 1e9, 0),
+                         "pct_hbm_peak": round(100 * byts / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 1)})
+            del kc, vc, bt, q, o, wsa
+        torch.cuda.empty_cache()
+
     # ------------------------------------------------------- MXFP8 (context)
     mx = []
     if not args.no_sweep:
@@ -244,13 +285,13 @@ def main():
         del Xm, Wm, XS, WS
         # fp16 inputs and int8 inputs on the same tile skeleton, and bf16 output (context)
         from bigemm_inputs import int_i8, normal_f16
-        Xh = torch.from_numpy(normal_f16(SEED_X, (4096, K))).view(torch.float16).to(dev)
-        Wh = torch.from_numpy(normal_f16(SEED_W, (K, N), 0.02)).view(torch.float16).to(dev)
+        X16 = torch.from_numpy(normal_f16(SEED_X, (4096, K))).view(torch.float16).to(dev)
+        W16 = torch.from_numpy(normal_f16(SEED_W, (K, N), 0.02)).view(torch.float16).to(dev)
         Xi = torch.from_numpy(int_i8(SEED_X, (4096, K))).to(dev)
         Wi = torch.from_numpy(int_i8(SEED_W, (K, N))).to(dev)
         Yi = torch.empty((4096, N), dtype=torch.int32, device=dev)
         Yb = torch.empty((4096, N), dtype=torch.bfloat16, device=dev)
-        for name, fn, peak in (("f16", lambda m: bg.mm(Xh[:m], Wh, out=Y[:m]), PEAK_BF16_TFLOPS),
+        for name, fn, peak in (("f16", lambda m: bg.mm(X16[:m], W16, out=Y[:m]), PEAK_BF16_TFLOPS),
                                ("bf16_out", lambda m: bg.mm(X[:m], W, out=Yb[:m]), PEAK_BF16_TFLOPS),
                                ("i8", lambda m: bg.mm(Xi[:m], Wi, out=Yi[:m]), PEAK_I8_TOPS)):
             for m in (1024, 4096):
@@ -260,7 +301,7 @@ def main():
                 f = 2.0 * m * N * K
                 mx.append({"kind": name, "M": m, "us": round(t * 1e3, 2), "tflops": round(f / (t * 1e-3) / 1e12, 1),
                            "pct_peak": round(100 * f / (t * 1e-3) / 1e12 / peak, 1)})
-        del Xh, Wh, Xi, Wi, Yi, Yb
+        del X16, W16, Xi, Wi, Yi, Yb
 
     line = {
         "metric": "TFLOP/s vs M (1-4096) at K=N=4096, % MFMA peak; invariance byte-diffs=0",
@@ -286,6 +327,7 @@ def main():
         "other_types_k4096_n4096": mx,
         "split_k_context": split,
         "rmsnorm_bf16_context": norm,
+        "paged_attention_decode_context": attn,
         "invariance_byte_diffs": diffs if sweep else None,
         "timed_wall_s": round(wall, 3),
     }
