@@ -14,20 +14,18 @@
 //
 // Split kernel: one workgroup per (query token t, KV head, split s) covers
 // positions [256 s, min(256 s + 256, pos + 1)) for the G query heads sharing
-// the KV head. Thread layout: groups of D/8 lanes; lane gl of a group holds
-// elements [8 gl, 8 gl + 8) of a row, and group g reads positions
-// g, g + 256/(D/8), ... of the split (16 B per lane, a row per group).
-//   scores: each lane forms 8-element partial dot products (v_dot2_f32_bf16 in
-//           a fixed order) for its group's positions, then a reduce-scatter
-//           butterfly over the group's lanes leaves every thread with the full
-//           dot product of exactly one position;
+// the KV head.
+//   scores: each wave takes 64 positions as four 16 x 16 tiles of
+//           v_mfma_f32_16x16x32_bf16 (query heads as rows, padded with zeros,
+//           positions as columns, the head dimension in steps of 32 in a fixed
+//           order); K rows are read straight into the B-operand layout;
 //   softmax: per head, the split maximum m and p_j = exp(s_j - m) (fp32), and
 //           l = sum_j p_j (wave butterfly, then the four waves in order);
-//   values: each lane accumulates p_j * v_j over its group's positions in
-//           ascending order (fp32 FMA), a reduce-scatter butterfly over the
-//           groups of a wave, then the four waves in order.
-// Every butterfly step adds two partial sums of fixed, disjoint position sets,
-// so each split result is a fixed function of that split's inputs.
+//   values: groups of D/8 lanes each take 256 / (D/8) consecutive positions,
+//           lane gl elements [8 gl, 8 gl + 8); fp32 FMA in ascending position
+//           order, a reduce-scatter over the groups of a wave
+//           (v_permlane32/16_swap), then the four waves in order.
+// Each split result is a fixed function of that split's inputs.
 // Merge kernel: per (token, query head), the splits' (m_s, l_s, acc_s) are
 // combined as m = max_s m_s, w_s = exp(m_s - m),
 // o = (sum_s w_s acc_s) / (sum_s w_s l_s), the sums in a fixed tree that depends
@@ -47,29 +45,18 @@ static_assert(kAttnSplit == kThreads, "one position of a split per thread after 
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-// The elements are copied to scalars before the bit cast: a cast of the vector
-// element expression itself reinterprets element 0.
-__device__ __forceinline__ float dot8(const i32x4 a, const i32x4 b) {
-  float d = 0.f;
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const int ac = a[c], bc = b[c];
-    d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, ac), __builtin_bit_cast(bf16x2, bc), d, false);
-  }
-  return d;
-}
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(uint32_t u) {
   if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x0040u;
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-// Cross-lane moves. DPP: row_mirror pairs lane i of a 16-lane row with 15 - i,
-// row_half_mirror pairs i with 7 - i inside each half row, the two quad
-// permutations swap neighbours at distance 2 and 1, row_ror:8 pairs i with i ^ 8.
-constexpr int kDppRowMirror = 0x140, kDppHalfMirror = 0x141, kDppQuadXor2 = 0x4E, kDppQuadXor1 = 0xB1,
-              kDppRor8 = 0x128;
+// Cross-lane move by DPP: row_ror:8 pairs lane i of a 16-lane row with i ^ 8.
+constexpr int kDppRor8 = 0x128;
 
 template <int kCtrl>
 __device__ __forceinline__ float dpp(float x) {
@@ -87,27 +74,11 @@ __device__ __forceinline__ float rs_pair(float a, float b, bool hi) {
   return hi ? sb : sa;
 }
 
-// v[0..N) of every lane of an aligned group of N lanes (N = 16 or 8, a row or
-// half row) are partial sums over disjoint sets; afterwards v[0] of lane i
-// holds the total of index i (the lane keeps, at each step, the half its own
-// bit selects).
-template <int N>
-__device__ __forceinline__ void reduce_scatter(float (&v)[N], int lane) {
-  static_assert(N == 16 || N == 8, "a row or half row of lanes");
-  if constexpr (N == 16) {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = rs_pair<kDppRowMirror>(v[k], v[k + 8], (lane & 8) != 0);
-  }
-#pragma unroll
-  for (int k = 0; k < 4; ++k) v[k] = rs_pair<kDppHalfMirror>(v[k], v[k + 4], (lane & 4) != 0);
-#pragma unroll
-  for (int k = 0; k < 2; ++k) v[k] = rs_pair<kDppQuadXor2>(v[k], v[k + 2], (lane & 2) != 0);
-  v[0] = rs_pair<kDppQuadXor1>(v[0], v[1], (lane & 1) != 0);
-}
-
-// The same over the groups of a wave (lane bits 32, 16 and, for 8-lane groups,
-// 8): v_permlane32_swap / v_permlane16_swap exchange the halves directly, so
-// that a' + b' is own + partner for the kept index. Afterwards lane l holds
+// v[0..N) of every lane are partial sums; lanes with equal bits below kL hold
+// the same elements for different positions. Reduce-scatter over the other lane
+// bits (32, 16 and, for 8-lane groups, 8): v_permlane32_swap and
+// v_permlane16_swap exchange the halves directly, so that a' + b' is own +
+// partner for the index the lane keeps; the last step uses rs_pair. Afterwards lane l holds
 // indices [off, off + N >> steps) where off adds N/2 for lane bit 32, N/4 for
 // bit 16 (and N/8 for bit 8).
 template <int N, int kL>
@@ -137,22 +108,37 @@ __device__ __forceinline__ int64_t slot_row(int blk, int Hkv, int kvh, int bs_lo
   return ((((int64_t)blk * Hkv + kvh) << bs_log2) + (j & ((1 << bs_log2) - 1)));
 }
 
+// fp32 -> three bf16 parts whose sum is the value exactly (for values of normal
+// bf16 range): hi = RNE(x), mid = RNE(x - hi), lo = x - hi - mid.
+__device__ __forceinline__ void split3(float x, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+  hi = f32_to_bf16_rne(__float_as_uint(x));
+  const float r1 = x - __uint_as_float(hi << 16);
+  mid = f32_to_bf16_rne(__float_as_uint(r1));
+  const float r2 = r1 - __uint_as_float(mid << 16);
+  lo = f32_to_bf16_rne(__float_as_uint(r2));
+}
+
+template <typename T>
+__device__ __forceinline__ __attribute__((address_space(3))) T* lds(const void* p) {
+  return (__attribute__((address_space(3))) T*)(p);
+}
+
 template <int D, int G>
 __global__ __launch_bounds__(kThreads)
 void bigemm_attn_split_kernel(AttnParams p) {
-  constexpr int kL = D / 8;                 // lanes per row
-  constexpr int kGroups = kThreads / kL;    // rows read at once
-  constexpr int kPer = kAttnSplit / kGroups;  // positions per lane
-  static_assert(kPer == kL, "the score reduce-scatter leaves one position per lane");
-  constexpr int kAcc = G * 8;
-  __shared__ __align__(16) float p_s[G][kAttnSplit];
+  constexpr int kC = D / 32;      // MFMA steps along the head dimension (scores)
+  constexpr int kNT = D / 16;     // 16-column output tiles (values)
+  constexpr int kVS = D + 16;     // staged V row stride in elements (D*2 + 32 bytes)
+  static_assert(G <= 16, "the query heads of a group are the rows of one 16 x 16 MFMA tile");
+  __shared__ __align__(16) float p_s[G][kAttnSplit];        // scores, then weights, by position
+  __shared__ __align__(16) uint16_t v_s[4][32][kVS];        // per wave: 32 V rows being consumed
   __shared__ float red_m[4][G];
   __shared__ float red_l[4][G];
-  __shared__ float acc_s[4][G][D];
   __shared__ int32_t blk_s[kAttnSplit];
+  float (*acc_s)[G][D] = (float (*)[G][D])&v_s[0][0][0];   // after the values: per-wave outputs
+  static_assert(sizeof(v_s) >= sizeof(float) * 4 * G * D, "acc_s fits in v_s");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int grp = tid / kL, gl = tid % kL;
   const int s = blockIdx.x % p.nsplit;
   const int rest = blockIdx.x / p.nsplit;
   const int kvh = rest % p.Hkv;
@@ -167,58 +153,74 @@ void bigemm_attn_split_kernel(AttnParams p) {
   const int32_t* bt = p.block_table + (int64_t)sq * p.max_blocks;
   for (int i = tid; i < nb; i += kThreads) blk_s[i] = bt[b0 + i];
 
-  i32x4 q[G];
-  const uint16_t* qrow = p.Q + ((int64_t)t * p.H + (int64_t)kvh * G) * D + gl * 8;
-#pragma unroll
-  for (int h = 0; h < G; ++h) q[h] = *(const i32x4*)(qrow + h * D);
-  __syncthreads();
-
-  // Rows of this split: zero past the context, NaN where the block id is invalid.
+  // Q as the A operand of v_mfma_f32_16x16x32_bf16: lane l supplies head l % 16
+  // (zero rows past G), head-dimension elements 32 c + 8 (l / 16) .. + 7.
+  const int qh = lane & 15, kq = 8 * (lane >> 4);
   const i32x4 kZero = {0, 0, 0, 0};
   const i32x4 kNaN = {0x7FC07FC0, 0x7FC07FC0, 0x7FC07FC0, 0x7FC07FC0};
-  i32x4 kr[kPer];
+  i32x4 qa[kC];
+  const uint16_t* qrow = p.Q + ((int64_t)t * p.H + (int64_t)kvh * G + qh) * D + kq;
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int jj = grp + kGroups * i;
-    kr[i] = kZero;
-    if (jj < n) {
+  for (int c = 0; c < kC; ++c) qa[c] = qh < G ? *(const i32x4*)(qrow + 32 * c) : kZero;
+  __syncthreads();
+
+  // K and V rows in the B-operand layout: wave w takes positions 64 w + 16 b +
+  // (l % 16) of the split, lane l elements 32 c + 8 (l / 16) .. + 7 of the row.
+  // Rows past the context are zero (their weights are zero), rows whose block
+  // id is invalid are NaN.
+  // Row offsets of this lane's four positions (-1: past the context or an
+  // invalid block id).
+  int64_t roff[4];
+  bool past[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int jj = 64 * wave + 16 * b + qh;
+    past[b] = jj >= n;
+    roff[b] = -1;
+    if (!past[b]) {
       const int j = j0 + jj;
       const int blk = blk_s[(j >> p.bs_log2) - b0];
-      kr[i] = kNaN;
-      if (blk >= 0 && blk < p.num_blocks)
-        kr[i] = *(const i32x4*)(p.K + slot_row(blk, p.Hkv, kvh, p.bs_log2, j) * D + gl * 8);
+      if (blk >= 0 && blk < p.num_blocks) roff[b] = slot_row(blk, p.Hkv, kvh, p.bs_log2, j) * D + kq;
     }
   }
-
-  i32x4 vr[kPer];
+  auto load_rows = [&](const uint16_t* base, i32x4 (&dst)[4][kC]) {
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int jj = grp + kGroups * i;
-    vr[i] = kZero;
-    if (jj < n) {
-      const int j = j0 + jj;
-      const int blk = blk_s[(j >> p.bs_log2) - b0];
-      vr[i] = kNaN;
-      if (blk >= 0 && blk < p.num_blocks)
-        vr[i] = *(const i32x4*)(p.V + slot_row(blk, p.Hkv, kvh, p.bs_log2, j) * D + gl * 8);
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int c = 0; c < kC; ++c)
+        dst[b][c] = past[b] ? kZero : roff[b] < 0 ? kNaN : *(const i32x4*)(base + roff[b] + 32 * c);
+  };
+  i32x4 kb[4][kC];
+  load_rows(p.K, kb);
+
+  // Scores: D[head][position] of each 16-position block; lane l holds position
+  // l % 16 for heads 4 (l / 16) + r. The V rows of a block are requested once
+  // its K rows are consumed (so K and V are not both held in registers).
+  i32x4 vb[4][kC];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    f32x4 acc4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < kC; ++c)
+      acc4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[c]),
+                                                     __builtin_bit_cast(bf16x8, kb[b][c]), acc4, 0, 0, 0);
+#pragma unroll
+    for (int c = 0; c < kC; ++c)
+      vb[b][c] = past[b] ? kZero : roff[b] < 0 ? kNaN : *(const i32x4*)(p.V + roff[b] + 32 * c);
+    const int jj = 64 * wave + 16 * b + qh;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int h = 4 * (lane >> 4) + r;
+      if (h < G) p_s[h][jj] = jj < n ? acc4[r] * p.scale : -INFINITY;
     }
   }
+  __syncthreads();
 
-  const int own = grp + kGroups * gl;  // the position whose score this thread ends with
-  float sh[G];
+  // softmax statistics of the split, per head; thread tid owns position tid
+  float sh[G], m[G], l[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    float sc[kPer];
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) sc[i] = dot8(q[h], kr[i]);
-    reduce_scatter<kPer>(sc, gl);
-    sh[h] = own < n ? sc[0] * p.scale : -INFINITY;
-  }
-
-  // softmax statistics of the split, per head
-  float m[G], l[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
+    sh[h] = p_s[h][tid];
     float x = sh[h];
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
@@ -239,42 +241,63 @@ void bigemm_attn_split_kernel(AttnParams p) {
 #pragma unroll
   for (int h = 0; h < G; ++h) l[h] = ((red_l[0][h] + red_l[1][h]) + red_l[2][h]) + red_l[3][h];
 
-  // p * v over this group's positions, ascending; weight of position grp + kGroups*i
-  // sits at p_s[h][grp * kPer + i] (the thread that owned its score)
-  float acc[kAcc];
+  // Values: O[head][d] += P[head][position] V[position][d] by 16 x 16 x 32 MFMA
+  // tiles, positions in two steps of 32 per wave. The fp32 weights enter as
+  // three bf16 parts (exact sum), V through LDS with the transposing read.
+  f32x4 o[kNT];
 #pragma unroll
-  for (int k = 0; k < kAcc; ++k) acc[k] = 0.f;
+  for (int nt = 0; nt < kNT; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // ds_read_b64_tr_b16: in each 16-lane group, lane i element e is element i % 4
+  // of the 8 bytes lane 4 e + i / 4 addresses. Lane j of group g addresses row
+  // 8 g + j / 4 (+ 4), columns 16 nt + 4 (j % 4): lane i then holds column
+  // 16 nt + i, rows 8 g .. 8 g + 7 — the B operand.
+  const int tr_row = kq + ((lane & 15) >> 2), tr_col = 4 * (lane & 3);
 #pragma unroll
-  for (int i4 = 0; i4 < kPer / 4; ++i4) {
-    float4 w4[G];
+  for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) w4[h] = *(const float4*)&p_s[h][grp * kPer + 4 * i4];
+    for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      const i32x4 vv = vr[4 * i4 + ii];
-      float v[8];
+      for (int c = 0; c < kC; ++c) *(i32x4*)&v_s[wave][16 * bb + qh][32 * c + kq] = vb[2 * ks + bb][c];
+    // weights of positions 64 w + 32 ks + 8 (l / 16) .. + 7 for head l % 16
+    i32x4 ph = kZero, pm = kZero, pl = kZero;
+    if (qh < G) {
+      const float4 w0 = *(const float4*)&p_s[qh][64 * wave + 32 * ks + kq];
+      const float4 w1 = *(const float4*)&p_s[qh][64 * wave + 32 * ks + kq + 4];
+      const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        v[2 * c] = __uint_as_float((uint32_t)vv[c] << 16);
-        v[2 * c + 1] = __uint_as_float((uint32_t)vv[c] & 0xFFFF0000u);
-      }
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float w = ii == 0 ? w4[h].x : ii == 1 ? w4[h].y : ii == 2 ? w4[h].z : w4[h].w;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h * 8 + e] = fmaf(w, v[e], acc[h * 8 + e]);
+      for (int e2 = 0; e2 < 4; ++e2) {
+        uint32_t h0, m0, l0, h1, m1, l1;
+        split3(wv[2 * e2], h0, m0, l0);
+        split3(wv[2 * e2 + 1], h1, m1, l1);
+        ph[e2] = (int)(h0 | (h1 << 16));
+        pm[e2] = (int)(m0 | (m1 << 16));
+        pl[e2] = (int)(l0 | (l1 << 16));
       }
     }
+    __syncthreads();
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) {
+      const i16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds<i16x4>(&v_s[wave][tr_row][16 * nt + tr_col]));
+      const i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds<i16x4>(&v_s[wave][tr_row + 4][16 * nt + tr_col]));
+      const i32x2 r0d = __builtin_bit_cast(i32x2, r0), r1d = __builtin_bit_cast(i32x2, r1);
+      const i32x4 vbop = {r0d[0], r0d[1], r1d[0], r1d[1]};
+      const bf16x8 vop = __builtin_bit_cast(bf16x8, vbop);
+      o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ph), vop, o[nt], 0, 0, 0);
+      o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pm), vop, o[nt], 0, 0, 0);
+      o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pl), vop, o[nt], 0, 0, 0);
+    }
+    __syncthreads();
   }
 
-  // reduce-scatter over the groups of this wave
-  const int off = reduce_scatter_groups<kAcc, kL>(acc, lane);
-  constexpr int kOwn = kAcc * kL / 64;  // values each lane owns afterwards
+  // per-wave outputs (lane l: column 16 nt + l % 16, heads 4 (l / 16) + r), then
+  // the four waves added in order
 #pragma unroll
-  for (int k = 0; k < kOwn; ++k) {
-    const int f = off + k;
-    acc_s[wave][f >> 3][gl * 8 + (f & 7)] = acc[k];
-  }
+  for (int nt = 0; nt < kNT; ++nt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int h = 4 * (lane >> 4) + r;
+      if (h < G) acc_s[wave][h][16 * nt + qh] = o[nt][r];
+    }
   __syncthreads();
 
   const int64_t base = ((int64_t)t * p.H + (int64_t)kvh * G) * p.nsplit + s;  // (t, head kvh*G, s)
