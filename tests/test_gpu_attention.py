@@ -198,6 +198,20 @@ def test_batch_composition_and_index_do_not_matter():
             assert H.byte_diff(ob[idx[i]], alone[i]) == 0, (trial, i)
 
 
+def test_long_context_parity_and_max_context():
+    """A 9000-position sequence (36 splits) against the oracle, and tokens of a
+    300-position sequence computed in that call and again with max_context = 300 (a grid
+    of 2 splits per token and a 2-split workspace stride): identical bytes."""
+    P = Paged(365, [9000, 300], 2, 64, 32).write_all()
+    seqs = np.array([0, 0, 0, 1, 1], np.int32)
+    poss = np.array([8999, 4500, 256, 299, 40], np.int32)
+    Q = normal_bf16(366, (5, 8, 64))
+    o = P.attend(Q, seqs, poss, max_context=9000)
+    assert_parity(o, Q, P, seqs, poss)
+    short = P.attend(Q[3:], seqs[3:], poss[3:], max_context=300)
+    assert H.byte_diff(o[3:], short) == 0
+
+
 def test_physical_blocks_do_not_matter():
     P1 = Paged(370, [900, 77], 2, 64, 16).write_all()
     P2 = Paged(370, [900, 77], 2, 64, 16, spare=11, table_seed=999).write_all()

@@ -65,6 +65,24 @@ def test_linspace_row0_prefix_vs_batch():
         assert H.byte_diff(y, Y[r]) == 0, r
 
 
+def test_linspace_vendor_contrast(capsys):
+    """Informative contrast, not a requirement: the vendor GEMM (torch.mm through
+    hipBLASLt, bf16 in and out) on the same experiment. Its row 0 alone and in the
+    batch are allowed to differ (its kernel choice follows the shape); the number of
+    differing bytes is printed. Ours is 0 for the same row."""
+    import torch
+    B, D = 2048, 4096
+    a = dev_bf16(linspace_bf16(-1000.0, 1000.0, B * D, (B, D))).view(torch.bfloat16)
+    b = dev_bf16(linspace_bf16(-1000.0, 1000.0, D * D, (D, D))).view(torch.bfloat16)
+    vendor = H.byte_diff(torch.mm(a[:1], b)[0], torch.mm(a, b)[0])
+    ours = H.byte_diff(run((a[:1].view(torch.int16),), (b.view(torch.int16),))[0],
+                       run((a.view(torch.int16),), (b.view(torch.int16),))[0])
+    torch.cuda.synchronize()
+    with capsys.disabled():
+        print(f"\n  linspace row 0, alone vs in the batch of {B}: torch.mm {vendor} differing bytes, bigemm {ours}")
+    assert ours == 0
+
+
 # ------------------------------------------------------ projection workload (M sweep)
 @pytest.mark.parametrize("N", [4096, 14336])
 def test_projection_msweep(N):
