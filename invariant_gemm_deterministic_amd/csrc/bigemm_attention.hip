@@ -423,7 +423,8 @@ void launch_split(const AttnParams& p, hipStream_t stream) {
     case 1: hipLaunchKernelGGL((bigemm_attn_split_kernel<D, 1>), grid, dim3(kThreads), 0, stream, p); break;
     case 2: hipLaunchKernelGGL((bigemm_attn_split_kernel<D, 2>), grid, dim3(kThreads), 0, stream, p); break;
     case 4: hipLaunchKernelGGL((bigemm_attn_split_kernel<D, 4>), grid, dim3(kThreads), 0, stream, p); break;
-    default: hipLaunchKernelGGL((bigemm_attn_split_kernel<D, 8>), grid, dim3(kThreads), 0, stream, p); break;
+    case 8: hipLaunchKernelGGL((bigemm_attn_split_kernel<D, 8>), grid, dim3(kThreads), 0, stream, p); break;
+    default: hipLaunchKernelGGL((bigemm_attn_split_kernel<D, 16>), grid, dim3(kThreads), 0, stream, p); break;
   }
 }
 

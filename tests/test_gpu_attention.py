@@ -143,6 +143,8 @@ PARITY = [  # (D, H, Hkv, bs, out_dtype)
     (64, 4, 2, 4096, torch.float32),
     (128, 16, 2, 64, torch.bfloat16),
     (64, 8, 2, 32, torch.bfloat16),
+    (128, 32, 2, 32, torch.float32),
+    (64, 16, 1, 16, torch.bfloat16),
 ]
 
 
