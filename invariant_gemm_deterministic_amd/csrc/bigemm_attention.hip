@@ -20,7 +20,8 @@
 //           positions as columns, the head dimension in steps of 32 in a fixed
 //           order); K rows are read straight into the B-operand layout;
 //   softmax: per head, the split maximum m and p_j = exp(s_j - m) (fp32), and
-//           l = sum_j p_j (wave butterfly, then the four waves in order);
+//           l = sum_j p_j (a fixed DPP tree per wave, then the four waves in
+//           order);
 //   values: groups of D/8 lanes each take 256 / (D/8) consecutive positions,
 //           lane gl elements [8 gl, 8 gl + 8); fp32 FMA in ascending position
 //           order, a reduce-scatter over the groups of a wave
@@ -55,12 +56,40 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(uint32_t u) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-// Cross-lane move by DPP: row_ror:8 pairs lane i of a 16-lane row with i ^ 8.
-constexpr int kDppRor8 = 0x128;
+// Cross-lane moves by DPP: the quad permutations swap neighbours at distance 1
+// and 2, row_half_mirror pairs lane i with 7 - i inside each half row,
+// row_mirror pairs i with 15 - i inside each 16-lane row, row_ror:8 pairs i with
+// i ^ 8; row_bcast:15 / row_bcast:31 pass the last lane of a row (of rows 0-1)
+// to the rows that row_mask selects.
+constexpr int kDppQuadXor1 = 0xB1, kDppQuadXor2 = 0x4E, kDppHalfMirror = 0x141, kDppRowMirror = 0x140,
+              kDppRor8 = 0x128, kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
 
 template <int kCtrl>
 __device__ __forceinline__ float dpp(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xF, 0xF, false));
+}
+
+// Rows outside kRowMask keep `id`.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ float dpp_rows(float x, float id) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(id), __float_as_int(x), kCtrl, kRowMask, 0xF,
+                                                    false));
+}
+
+// Max (kMax) or sum of x over the 64 lanes of the wave, valid in lane 63: within
+// quads, half rows and rows, then rows 0+1 and 2+3, then the two halves. A
+// fixed tree of VALU steps (no LDS round trips). The max ignores NaN, as fmaxf.
+template <bool kMax>
+__device__ __forceinline__ float wave_reduce63(float x) {
+  auto op = [](float a, float b) { return kMax ? fmaxf(a, b) : a + b; };
+  const float id = kMax ? -INFINITY : 0.f;
+  x = op(x, dpp<kDppQuadXor1>(x));
+  x = op(x, dpp<kDppQuadXor2>(x));
+  x = op(x, dpp<kDppHalfMirror>(x));
+  x = op(x, dpp<kDppRowMirror>(x));
+  x = op(x, dpp_rows<kDppRowBcast15, 0xA>(x, id));
+  x = op(x, dpp_rows<kDppRowBcast31, 0xC>(x, id));
+  return x;
 }
 
 // One reduce-scatter step between partner lanes (partner differs in the bit
@@ -221,10 +250,8 @@ void bigemm_attn_split_kernel(AttnParams p) {
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     sh[h] = p_s[h][tid];
-    float x = sh[h];
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
-    if (lane == 0) red_m[wave][h] = x;
+    const float x = wave_reduce63<true>(sh[h]);
+    if (lane == 63) red_m[wave][h] = x;
   }
   __syncthreads();
 #pragma unroll
@@ -232,10 +259,8 @@ void bigemm_attn_split_kernel(AttnParams p) {
     m[h] = fmaxf(fmaxf(red_m[0][h], red_m[1][h]), fmaxf(red_m[2][h], red_m[3][h]));
     const float w = expf(sh[h] - m[h]);
     p_s[h][tid] = w;
-    float x = w;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
-    if (lane == 0) red_l[wave][h] = x;
+    const float x = wave_reduce63<false>(w);
+    if (lane == 63) red_l[wave][h] = x;
   }
   __syncthreads();
 #pragma unroll
