@@ -376,9 +376,8 @@ void bigemm_attn_merge_kernel(AttnParams p) {
 
   float mloc = -INFINITY;
   for (int s = tid; s < ns; s += kThreads) mloc = fmaxf(mloc, ml[2 * s]);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, off));
-  if (lane == 0) red[wave] = mloc;
+  mloc = wave_reduce63<true>(mloc);
+  if (lane == 63) red[wave] = mloc;
   __syncthreads();
   const float mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 
