@@ -338,13 +338,24 @@ void bigemm_bf16_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
 // applied inside the instruction, fp32 accumulate. Per stage: X tile 128 x 128
 // bytes, W tile 128 x 128 bytes (both rows of 128 B).
 constexpr int kBkMx = 128;
+// Staged scales: the scale bytes of kScaleGroup consecutive K blocks are
+// moved to LDS by DMA, once per workgroup (X: 128 rows x 4 kScaleGroup bytes;
+// W: 4 kScaleGroup scale rows x 128 bytes, whole lines), into one of two LDS
+// buffers, one group ahead, instead of per-lane loads repeated by the waves
+// that share a row or column.
+#ifndef BIGEMM_MX_SCALE_GROUP
+#define BIGEMM_MX_SCALE_GROUP 4
+#endif
+constexpr int kScaleGroup = BIGEMM_MX_SCALE_GROUP;
+static_assert(kScaleGroup == 4 || kScaleGroup == 8, "scale groups of 4 or 8 K blocks");
+constexpr int kScaleBufBytes = 128 * 4 * kScaleGroup;  // one operand's scales of one group
 #ifndef BIGEMM_MX_STAGES
 #define BIGEMM_MX_STAGES 3
 #endif
 constexpr int kStagesMx = BIGEMM_MX_STAGES;
 static_assert(kStagesMx >= 3 && kStagesMx <= 4, "LDS holds 3 or 4 stages of 32 KiB");
 
-template <bool kVecXs, bool kOutBf16>
+template <bool kStaged, bool kOutBf16>
 __global__ __launch_bounds__(kThreads, 1)
 void bigemm_mxfp8_kernel(const uint8_t* __restrict__ X, const uint8_t* __restrict__ W,
                          void* __restrict__ Y, const uint8_t* __restrict__ XS,
@@ -355,7 +366,14 @@ void bigemm_mxfp8_kernel(const uint8_t* __restrict__ X, const uint8_t* __restric
   __shared__ __attribute__((aligned(1024))) uint8_t stage1[kStageBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t stage2[kStageBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t stage3[kStagesMx > 3 ? kStageBytes : 16];
+  // Staged scales: two buffers (separate objects, so the compiler can tell the
+  // DMA into one from reads of the other), each one group of kScaleGroup K
+  // blocks: X scales [128 rows][4 * kScaleGroup bytes] then W scales
+  // [4 * kScaleGroup rows][128 columns].
+  __shared__ __attribute__((aligned(1024))) uint8_t scales0[kStaged ? 2 * kScaleBufBytes : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t scales1[kStaged ? 2 * kScaleBufBytes : 16];
   uint8_t* const stg[4] = {stage0, stage1, stage2, stage3};
+  uint8_t* const scl[2] = {scales0, scales1};
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -481,60 +499,81 @@ void bigemm_mxfp8_kernel(const uint8_t* __restrict__ X, const uint8_t* __restric
       }
     }
   };
-  // X scales, vector path (16-byte aligned scale rows, K a multiple of 512):
-  // the 16 scale bytes of K blocks 4q .. 4q+3 of the lane's row, one 16-byte
-  // load per fragment, so a scale line is requested once per four K blocks
-  // instead of once per block.
-  auto load_xquad = [&](int q, i32x4 (&xq)[2]) {
+  // Staged path: the scales of group q (K blocks kScaleGroup q ..) into buffer
+  // buf, as 1 KiB DMA loads j = 0 .. 2 kXLoads - 1 spread over the waves. X
+  // load j: chunk p = 64 j + l is 16 bytes of row p / (kScaleGroup / 4) (its
+  // scale bytes 4 kScaleGroup q + 16 (p % (kScaleGroup / 4)) ..), to LDS byte
+  // 16 p. W load kXLoads + j: chunk p = 64 j + l is columns 16 (p % 8) .. + 15 of
+  // scale row 4 kScaleGroup q + p / 8, to LDS byte kScaleBufBytes + 16 p.
+  // Chunks outside the matrix or past K read as zero.
+  constexpr int kXLoads = kScaleGroup / 2;
+  auto issue_scales = [&](int q, uint8_t* buf) {
+    for (int j = wave; j < 2 * kXLoads; j += 4) {
+      if (j < kXLoads) {
+        const int p = j * 64 + lane;
+        const int r = p / (kScaleGroup / 4), cx = q * 4 * kScaleGroup + (p % (kScaleGroup / 4)) * 16;
+        const uint32_t ox = (r < rows_valid && cx < nsb) ? (uint32_t)(r * ldxs + cx) : kOob;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rxs, LDS(void, buf + j * 1024), 16, ox, 0, 0, 0);
+      } else {
+        const int p = (j - kXLoads) * 64 + lane;
+        const int kr = q * 4 * kScaleGroup + (p >> 3), cw = (p & 7) * 16;
+        const uint32_t ow = (kr < nsb && cw < cols_valid) ? (uint32_t)(kr * ldws + cw) : kOob;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rws, LDS(void, buf + kScaleBufBytes + (j - kXLoads) * 1024), 16, ow,
+                                                 0, 0, 0);
+      }
+    }
+  };
+  // The scales of block kb (position b in its group) from its group's buffer:
+  // the X dword of the lane's row (bytes kk * 2 + g), the W byte of the lane's
+  // column in scale row 4 b + kk * 2 + g.
+  auto read_scales = [&](int b, const uint8_t* buf, int (&sa_)[2][2], int (&sb_)[2][2]) {
 #pragma unroll
     for (int f = 0; f < 2; ++f) {
-      const uint32_t o = q * 16 < xs_lim[f] ? xs_base[f] + (uint32_t)(q * 16) : kOob;
-      xq[f] = __builtin_amdgcn_raw_buffer_load_b128(rxs, o, 0, 0);
+      const int r = wm * 64 + f * 32 + (lane & 31);
+      const int d = *LDS(const int, buf + r * 4 * kScaleGroup + b * 4);
+      const int c = wn * 64 + f * 32 + (lane & 31);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        sa_[f][kk] = (d >> (8 * (kk * 2 + g))) & 0xFF;
+        sb_[f][kk] = *LDS(const uint8_t, buf + kScaleBufBytes + (b * 4 + kk * 2 + g) * 128 + c);
+      }
     }
   };
 
-  // Scale registers of the K blocks in flight, one ring slot per stage:
-  // [slot][fragment][MFMA step]. The vector path keeps the X scales of two
-  // groups of four K blocks instead: [group parity][fragment].
+  // Byte path: scale registers of the K blocks in flight, one ring slot per
+  // stage: [slot][fragment][MFMA step].
   int sa[kStagesMx][2][2], sb[kStagesMx][2][2];
-  i32x4 xq[2][2];
   // Unroll length of the K loop: a multiple of the stage count (LDS stages and
-  // scale slots) and, on the vector path, of 8 (two groups of four blocks).
-  constexpr int kUnroll = kVecXs ? (kStagesMx == 3 ? 24 : 8) : 2 * kStagesMx;
+  // scale slots) and, on the staged path, of two scale groups, so that every
+  // step's stage and scale buffer are fixed objects.
+  constexpr int kUnroll = kStaged ? (kStagesMx == 3 ? 6 * kScaleGroup : 2 * kScaleGroup) : 2 * kStagesMx;
+  static_assert(!kStaged || (kUnroll % kStagesMx == 0 && kUnroll % (2 * kScaleGroup) == 0), "unroll");
 
-  // One K block. Each block's scale loads are issued just before its LDS-DMA
-  // loads, kStagesMx - 1 blocks ahead, so the wait for this block's DMA also
-  // covers its scales; younger than them are the next kStagesMx - 2 blocks'
-  // 8 scale and 8 DMA loads each. Then the stage read in the previous block is
-  // refilled and the MFMA chain runs on this stage: kk ascending.
-  // u is the step's position in the unrolled loop (kb % kUnroll).
+  // One K block. Staged path: the next scale group is requested at the first
+  // block of a group (its buffer was last read in the previous block, before
+  // this step's barrier). Byte path: each block's scale loads are issued just
+  // before its LDS-DMA loads, kStagesMx - 1 blocks ahead, so the wait for this
+  // block's DMA also covers its scales. Younger than this block's DMA are the
+  // next kStagesMx - 2 blocks' DMA loads (and byte-path scale loads); a scale
+  // group in flight only makes the wait cover more than it needs to. Then the
+  // stage read in the previous block is refilled and the MFMA chain runs on
+  // this stage: kk ascending. u is the step's position in the unrolled loop.
   auto step = [&](int kb, int u, const uint8_t* st, uint8_t* refill, int (&sac)[2][2], const int (&sbc)[2][2],
                   int (&san)[2][2], int (&sbn)[2][2]) {
-    // Loads younger than this block's DMA: per later block in flight, 4 W
-    // scale loads, 8 DMA loads and (byte path) 4 X scale loads. On the vector
-    // path a group's two X loads come on top every fourth block; the wait
-    // then covers two loads more than it needs to, which is harmless.
-    BIGEMM_WAIT_VMCNT((kVecXs ? 12 : 16) * (kStagesMx - 2));
+    BIGEMM_WAIT_VMCNT((kStaged ? 8 : 16) * (kStagesMx - 2));
     BIGEMM_BARRIER();
     const int nb = kb + kStagesMx - 1;
-    if (kVecXs) {
-      // The group that starts one block after the one being refilled (loaded
-      // a step early: the compiler delays these loads by up to a step).
-      if ((u + kStagesMx) % 4 == 0) load_xquad((nb + 1) / 4, xq[((u + kStagesMx) / 4) % 2]);
+    // u is a multiple of kScaleGroup exactly where kb is (kUnroll is a multiple
+    // of two groups and the loop starts at kb = 0).
+    if (kStaged) {
+      if (u % kScaleGroup == 0) issue_scales(kb / kScaleGroup + 1, scl[(u / kScaleGroup + 1) % 2]);
     } else {
       load_xscales(nb, san);
+      load_wscales(nb, sbn);
     }
-    load_wscales(nb, sbn);
     issue(nb, refill);
-    if (kVecXs) {
-      // This block's X scales: dword kb % 4 of its group, byte kk*2 + g.
-#pragma unroll
-      for (int f = 0; f < 2; ++f) {
-        const int d = xq[(u / 4) % 2][f][u % 4];
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) sac[f][kk] = (d >> (8 * (kk * 2 + g))) & 0xFF;
-      }
-    }
+    int sal[2][2], sbl[2][2];
+    if (kStaged) read_scales(u % kScaleGroup, scl[(u / kScaleGroup) % 2], sal, sbl);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       i32x8 a[2], b[2];
@@ -554,24 +593,24 @@ void bigemm_mxfp8_kernel(const uint8_t* __restrict__ X, const uint8_t* __restric
 #pragma unroll
         for (int fn = 0; fn < 2; ++fn)
           acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              a[fm], b[fn], acc[fm][fn], 0 /*A: E4M3*/, 0 /*B: E4M3*/, 0, sac[fm][kk], 0, sbc[fn][kk]);
+              a[fm], b[fn], acc[fm][fn], 0 /*A: E4M3*/, 0 /*B: E4M3*/, 0, kStaged ? sal[fm][kk] : sac[fm][kk], 0,
+              kStaged ? sbl[fn][kk] : sbc[fn][kk]);
     }
   };
 
-  // Prologue: a dummy (entirely out-of-range) fill of the last stage, then
-  // blocks 0 to kStagesMx - 2 with their scales. The dummy makes the loads in
+  // Prologue: the first scale group (staged path), a dummy (entirely
+  // out-of-range) fill of the last stage, then blocks 0 to kStagesMx - 2 with
+  // their scales. The dummy makes the loads in
   // flight at the loop head target the stages in the same order on entry as on
   // every later iteration.
+  if (kStaged) issue_scales(0, scl[0]);
   issue(nkb, stg[kStagesMx - 1]);
 #pragma unroll
   for (int s = 0; s < kStagesMx - 1; ++s) {
-    if (kVecXs) {
-      if (s == 0) load_xquad(0, xq[0]);
-      if ((s + 1) % 4 == 0) load_xquad((s + 1) / 4, xq[((s + 1) / 4) % 2]);
-    } else {
+    if (!kStaged) {
       load_xscales(s, sa[s]);
+      load_wscales(s, sb[s]);
     }
-    load_wscales(s, sb[s]);
     issue(s, stg[s]);
   }
   // Unrolled by kUnroll so that each stage and scale slot is fixed in every
@@ -839,11 +878,12 @@ hipError_t launch_mxfp8(Op op, const void* X, const void* W, void* Y, const void
                         int64_t ldxs, int64_t ldws, hipStream_t stream) {
   const int tiles_m = (int)((M + 127) / 128);
   const int tiles_n = (int)((N + 127) / 128);
-  // The X-scale load path depends on the scale layout and K only (never on M);
+  // The scale load path depends on the scale layout and K only (never on M);
   // both paths read the same scale values.
-  const bool vec_xs = K % 512 == 0 && ((uintptr_t)XS & 15) == 0 && ldxs % 16 == 0;
+  const bool staged = K % 512 == 0 && ((uintptr_t)XS & 15) == 0 && ldxs % 16 == 0 && ((uintptr_t)WS & 15) == 0 &&
+                      ldws % 16 == 0;
   const bool obf = op.out == 1 /* BIGEMM_BF16 */;
-  auto kern = vec_xs ? (obf ? bigemm_mxfp8_kernel<true, true> : bigemm_mxfp8_kernel<true, false>)
+  auto kern = staged ? (obf ? bigemm_mxfp8_kernel<true, true> : bigemm_mxfp8_kernel<true, false>)
                      : (obf ? bigemm_mxfp8_kernel<false, true> : bigemm_mxfp8_kernel<false, false>);
   hipLaunchKernelGGL(kern, dim3(tiles_m * tiles_n), dim3(kThreads), 0, stream, (const uint8_t*)X,
                      (const uint8_t*)W, Y, (const uint8_t*)XS, (const uint8_t*)WS, (int)M, (int)N, (int)K, ldx, ldw,

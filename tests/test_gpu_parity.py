@@ -206,10 +206,11 @@ def test_mxfp8_scale_shift_bit_identical():
 
 @pytest.mark.parametrize("K", [1024, 2048])
 def test_mxfp8_scale_load_paths_bit_identical(K):
-    """X scales reach the kernel either as 16-byte rows (16-byte aligned scale
-    rows, K a multiple of 512) or one byte at a time (any other layout). Both
-    paths must give the same bytes: compare packed scales with the same values
-    in padded rows and at an odd base address."""
+    """Scales reach the kernel either staged through LDS in groups of four K
+    blocks (X and W scale rows 16-byte aligned, K a multiple of 512) or one byte
+    at a time (any other layout). Both paths must give the same bytes: compare
+    packed scales with the same values in padded rows and at an odd base address,
+    for X scales and for W scales."""
     M, N = 200, 256
     X, W, XS, WS = _mx_inputs(M, N, K, "var", "var", seed=7)
     y_packed = _run_mx(X, W, XS, WS)
@@ -222,6 +223,14 @@ def test_mxfp8_scale_load_paths_bit_identical(K):
     y_odd = run((dev_u8(X), wide[:, 1:1 + nsb]), (dev_u8(W), dev_u8(WS))).cpu().numpy()
     assert y_packed.tobytes() == y_padded.tobytes()
     assert y_packed.tobytes() == y_odd.tobytes()
+    wide_w = torch.zeros((nsb, N + 5), dtype=torch.uint8, device=DEV)
+    wide_w[:, :N] = dev_u8(WS)     # W scale rows N + 5 bytes apart
+    y_wpad = run((dev_u8(X), dev_u8(XS)), (dev_u8(W), wide_w[:, :N])).cpu().numpy()
+    wide_w.zero_()
+    wide_w[:, 1:1 + N] = dev_u8(WS)  # W scales one byte past an aligned allocation
+    y_wodd = run((dev_u8(X), dev_u8(XS)), (dev_u8(W), wide_w[:, 1:1 + N])).cpu().numpy()
+    assert y_packed.tobytes() == y_wpad.tobytes()
+    assert y_packed.tobytes() == y_wodd.tobytes()
 
 
 @pytest.mark.parametrize("K", [160, 1024])
