@@ -10,8 +10,13 @@
  * every shape uses. This library is that recipe on CDNA4: one fixed tile
  * configuration per input type, the K blocks walked in ascending order by a
  * single workgroup, one MFMA shape at every M, no atomics, no workspace.
+ * The same rules give the other entry points below: an opt-in split-K whose
+ * split count follows K only, a batch-invariant RMSNorm, and batch-invariant
+ * paged decode attention (a KV-cache write plus attention with a fixed split
+ * size); each states its own invariance guarantee.
  *
- * Consequences the caller can rely on (per handle, device and library build):
+ * Consequences the caller can rely on for the matrix multiply (per handle,
+ * device and library build):
  *   - the bytes of Y[i, :] depend only on the bytes of X[i, :] (and of
  *     X_scale[i, :] for MXFP8), on W (and W_scale), on N, K and the
  *     leading dimensions' validity — not on M, not on the contents of other
