@@ -22,10 +22,11 @@
 //   softmax: per head, the split maximum m and p_j = exp(s_j - m) (fp32), and
 //           l = sum_j p_j (a fixed DPP tree per wave, then the four waves in
 //           order);
-//   values: groups of D/8 lanes each take 256 / (D/8) consecutive positions,
-//           lane gl elements [8 gl, 8 gl + 8); fp32 FMA in ascending position
-//           order, a reduce-scatter over the groups of a wave
-//           (v_permlane32/16_swap), then the four waves in order.
+//   values: each wave stages its 64 V rows through LDS, 32 at a time, and
+//           reads them back with ds_read_b64_tr_b16 as the B operand of
+//           v_mfma_f32_16x16x32_bf16; the fp32 weights enter as three bf16
+//           parts with an exact sum, positions in a fixed order; then the
+//           four waves' outputs are added in order.
 // Each split result is a fixed function of that split's inputs.
 // Merge kernel: per (token, query head), the splits' (m_s, l_s, acc_s) are
 // combined as m = max_s m_s, w_s = exp(m_s - m),
@@ -45,7 +46,6 @@ constexpr int kThreads = 256;
 static_assert(kAttnSplit == kThreads, "one position of a split per thread after the score reduction");
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -58,11 +58,11 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(uint32_t u) {
 
 // Cross-lane moves by DPP: the quad permutations swap neighbours at distance 1
 // and 2, row_half_mirror pairs lane i with 7 - i inside each half row,
-// row_mirror pairs i with 15 - i inside each 16-lane row, row_ror:8 pairs i with
-// i ^ 8; row_bcast:15 / row_bcast:31 pass the last lane of a row (of rows 0-1)
-// to the rows that row_mask selects.
+// row_mirror pairs i with 15 - i inside each 16-lane row; row_bcast:15 /
+// row_bcast:31 pass the last lane of a row (of rows 0-1) to the rows that
+// row_mask selects.
 constexpr int kDppQuadXor1 = 0xB1, kDppQuadXor2 = 0x4E, kDppHalfMirror = 0x141, kDppRowMirror = 0x140,
-              kDppRor8 = 0x128, kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
+              kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
 
 template <int kCtrl>
 __device__ __forceinline__ float dpp(float x) {
@@ -90,47 +90,6 @@ __device__ __forceinline__ float wave_reduce63(float x) {
   x = op(x, dpp_rows<kDppRowBcast15, 0xA>(x, id));
   x = op(x, dpp_rows<kDppRowBcast31, 0xC>(x, id));
   return x;
-}
-
-// One reduce-scatter step between partner lanes (partner differs in the bit
-// `hi` tests and agrees on the bits already reduced): lanes with hi clear keep
-// index k (own a + partner's a), lanes with hi set keep index k + half (own b +
-// partner's b). Each kept sum is formed by exactly one lane.
-template <int kCtrl>
-__device__ __forceinline__ float rs_pair(float a, float b, bool hi) {
-  const float sa = a + dpp<kCtrl>(a);
-  const float sb = b + dpp<kCtrl>(b);
-  return hi ? sb : sa;
-}
-
-// v[0..N) of every lane are partial sums; lanes with equal bits below kL hold
-// the same elements for different positions. Reduce-scatter over the other lane
-// bits (32, 16 and, for 8-lane groups, 8): v_permlane32_swap and
-// v_permlane16_swap exchange the halves directly, so that a' + b' is own +
-// partner for the index the lane keeps; the last step uses rs_pair. Afterwards lane l holds
-// indices [off, off + N >> steps) where off adds N/2 for lane bit 32, N/4 for
-// bit 16 (and N/8 for bit 8).
-template <int N, int kL>
-__device__ __forceinline__ int reduce_scatter_groups(float (&v)[N], int lane) {
-#pragma unroll
-  for (int k = 0; k < N / 2; ++k) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[k]), __float_as_uint(v[k + N / 2]), false,
-                                                    false);
-    v[k] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-  }
-#pragma unroll
-  for (int k = 0; k < N / 4; ++k) {
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[k]), __float_as_uint(v[k + N / 4]), false,
-                                                    false);
-    v[k] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-  }
-  int off = ((lane & 32) ? N / 2 : 0) + ((lane & 16) ? N / 4 : 0);
-  if constexpr (kL == 8) {
-#pragma unroll
-    for (int k = 0; k < N / 8; ++k) v[k] = rs_pair<kDppRor8>(v[k], v[k + N / 8], (lane & 8) != 0);
-    off += (lane & 8) ? N / 8 : 0;
-  }
-  return off;
 }
 
 __device__ __forceinline__ int64_t slot_row(int blk, int Hkv, int kvh, int bs_log2, int j) {

@@ -182,3 +182,19 @@ def test_paged_attention_check_args():
     assert bg.bigemm_attn_workspace_size(_kv(max_blocks=40), 5, 8, 1280) == 5 * 8 * 5 * 130 * 4
     assert bg.bigemm_attn_workspace_size(_kv(max_blocks=41), 5, 8, 1281) == 5 * 8 * 6 * 130 * 4
     assert bg.load().bigemm_kv_cache_write(None, 1, None, None, None, None, None, None, None, None) == ARG
+
+
+def test_attention_binding_rejects_host_tensors():
+    """The torch wrappers validate before any device call: host tensors, wrong dtypes
+    and wrong shapes raise ValueError."""
+    import torch
+    kc = torch.zeros((4, 2, 16, 64), dtype=torch.bfloat16)
+    bt = torch.zeros((1, 4), dtype=torch.int32)
+    s = torch.zeros(1, dtype=torch.int32)
+    q = torch.zeros((1, 4, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        bg.paged_attention(q, kc, kc, bt, s, s)
+    with pytest.raises(ValueError):
+        bg.kv_cache_write(q[:, :2], q[:, :2], kc, kc, bt, s, s)
+    with pytest.raises(ValueError):
+        bg.rmsnorm(torch.zeros((2, 64)), torch.zeros(64))

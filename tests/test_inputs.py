@@ -68,3 +68,30 @@ def test_row_positions_and_ab_rows():
     assert np.array_equal(XA[4], C[0]) and np.array_equal(XB[4], C[0])
     others = [i for i in range(8) if i != 4]
     assert not np.array_equal(XA[others], XB[others])
+
+
+def test_kv_generator_is_seeded_per_sequence():
+    """Each sequence's keys/values come from its own stream: the same for any set of
+    other sequences, different across sequences, zero past the sequence's length."""
+    K1, V1 = G.kv_bf16(5, [10, 20, 3], 2, 16)
+    K2, V2 = G.kv_bf16(5, [10, 4], 2, 16, threads=1)
+    assert np.array_equal(K1[0, :10], K2[0, :10]) and np.array_equal(V1[0, :10], V2[0, :10])
+    assert not np.array_equal(K1[0, :3], K1[2, :3])
+    assert not K1[2, 3:].any() and not V1[0, 10:].any()
+    k, v = G.seq_kv_bf16(5, 1, 20, 2, 16)
+    assert np.array_equal(k, K1[1]) and np.array_equal(v, V1[1])
+
+
+def test_block_table_assigns_distinct_blocks():
+    lens, bs = [1, 31, 32, 33, 100, 0], 16
+    bt, nb = G.block_table(9, lens, bs, spare=5)
+    need = [-(-L // bs) for L in lens]
+    assert nb == sum(need) + 5 and bt.shape == (len(lens), max(need))
+    used = np.concatenate([bt[s, :n] for s, n in enumerate(need)])
+    assert len(set(used.tolist())) == len(used) and used.min() >= 0 and used.max() < nb
+    for s, n in enumerate(need):
+        assert (bt[s, n:] == -1).all()
+    bt2, _ = G.block_table(9, lens, bs, spare=5)
+    assert np.array_equal(bt, bt2)
+    wide, _ = G.block_table(9, lens, bs, max_blocks=20)
+    assert wide.shape == (len(lens), 20)
