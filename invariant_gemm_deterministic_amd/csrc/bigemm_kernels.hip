@@ -157,6 +157,8 @@ constexpr int kThreadsBf16 = 512;
 #endif
 constexpr int kStagesBf16 = BIGEMM_BF16_STAGES;
 static_assert(kStagesBf16 >= 3 && kStagesBf16 <= 5, "LDS holds 3 to 5 stages of 32 KiB");
+// K-loop unroll of the bf16 kernel (steps per loop iteration).
+constexpr int kUnrollBf16 = 8 * kStagesBf16;
 
 // kSplit: the opt-in split-K variant. The grid is (chunk, tile) pairs; the
 // workgroup runs the same chain over the K blocks of its chunk only
@@ -296,14 +298,16 @@ void bigemm_bf16_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
   issue(nkb, stg[kStagesBf16 - 1]);
 #pragma unroll
   for (int s = 0; s < kStagesBf16 - 1; ++s) issue(s, stg[s]);
-  // Unrolled by 2 * kStagesBf16 so that each stage is a fixed LDS object in
-  // every step. (The compiler cannot track which stage the loads in flight
-  // target across the loop back-edge and drains them before the first step of
-  // an iteration; a longer body makes that the exception.)
+  // Unrolled by kUnrollBf16 steps (a multiple of kStagesBf16) so that each
+  // stage is a fixed LDS object in every step. The compiler cannot track which
+  // stage the loads in flight target across the loop back-edge, and waits for
+  // all of them (vmcnt(0)) before the first step of an iteration; 32 steps
+  // make that drain rare (once for K = 2048, twice for K = 4096). The body is
+  // about 18 KB of code, inside the instruction cache.
   for (int kb = 0;;) {
     bool done = false;
 #pragma unroll
-    for (int u = 0; u < 2 * kStagesBf16; ++u) {
+    for (int u = 0; u < kUnrollBf16; ++u) {
       step(kb, stg[u % kStagesBf16], stg[(u + kStagesBf16 - 1) % kStagesBf16]);
       if (++kb == nkb) {
         done = true;
