@@ -299,32 +299,39 @@ void bigemm_attn_split_kernel(AttnParams p) {
   }
 }
 
-// Merge: one workgroup per (token, query head, slice of kMergeE output
-// elements), so that long contexts (many splits) still spread over the chip.
+// Merge: one workgroup per (token, query head, slice of output elements), so
+// that long contexts (many splits) still spread over the chip.
 //   m = max_s m_s (exact in any order), then per chunk of 256 splits the weights
-//   w_s = exp(m_s - m) and l_s go to LDS;
-//   thread (e, r), r < R = 256 / kMergeE, takes splits s = r + R j in ascending
-//   order into kU interleaved fp32 accumulators (split s to accumulator
-//   (s / R) % kU), adds them in a fixed tree, then the R partials in ascending r.
-// The tree depends on the number of splits only.
-constexpr int kMergeE = 32;
+//   w_s = exp(m_s - m) and l_s go to LDS.
+//   Each output element has kLanes = 32 fp32 accumulator lanes: lane a takes
+//   the splits s = a, a + 32, a + 64, ... in ascending order (one fma chain for
+//   the weight sum, one for the weighted values). The lanes are then added in
+//   a fixed tree: P_r = (lane r + lane r+8) + (lane r+16 + lane r+24) for
+//   r = 0..7, and P_0 + P_1 + ... + P_7 in ascending r.
+// The arithmetic depends on the number of splits only. kRt threads share an
+// element (each holding 32 / kRt lanes): 8 when there are many (token, head)
+// pairs, 32 when there are few and each has many splits. Both give the same
+// bytes; the choice only sets how many workgroups the merge spreads over.
+constexpr int kMergeLanes = 32;
 
-template <int D, bool kBf16>
+template <int D, bool kBf16, int kRt>
 __global__ __launch_bounds__(kThreads)
 void bigemm_attn_merge_kernel(AttnParams p) {
-  constexpr int R = kThreads / kMergeE;
-  constexpr int kU = 4;
+  constexpr int E = kThreads / kRt;        // output elements per workgroup
+  constexpr int kLpt = kMergeLanes / kRt;  // accumulator lanes per thread
   constexpr int kChunk = kThreads;
-  static_assert(kChunk % (R * kU) == 0, "chunks keep the accumulator of every split");
+  static_assert(kChunk % kMergeLanes == 0, "chunks keep the lane of every split");
+  static_assert(D % E == 0, "slices tile the head");
   __shared__ float w_s[kChunk];
   __shared__ float l_s[kChunk];
   __shared__ float red[4];
-  __shared__ float part_a[R][kMergeE];
-  __shared__ float part_l[R][kMergeE];
-  constexpr int kSlices = D / kMergeE;
+  __shared__ float part_a[kMergeLanes][E];
+  __shared__ float part_l[kMergeLanes][E];
+  constexpr int kSlices = D / E;
   const int th = blockIdx.x / kSlices;  // t * H + h
-  const int e = (blockIdx.x % kSlices) * kMergeE + threadIdx.x % kMergeE;
-  const int r = threadIdx.x / kMergeE;
+  const int ei = threadIdx.x % E;
+  const int e = (blockIdx.x % kSlices) * E + ei;
+  const int rt = threadIdx.x / E;       // this thread's lanes: rt + kRt * q
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t = th / p.H;
   const int sq = p.seq_ids[t], pos = p.positions[t];
@@ -340,9 +347,9 @@ void bigemm_attn_merge_kernel(AttnParams p) {
   __syncthreads();
   const float mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 
-  float la[kU], aa[kU];
+  float la[kLpt], aa[kLpt];
 #pragma unroll
-  for (int u = 0; u < kU; ++u) la[u] = aa[u] = 0.f;
+  for (int q = 0; q < kLpt; ++q) la[q] = aa[q] = 0.f;
   for (int c0 = 0; c0 < ns; c0 += kChunk) {
     if (c0 + tid < ns) {
       w_s[tid] = expf(ml[2 * (c0 + tid)] - mx);
@@ -350,28 +357,33 @@ void bigemm_attn_merge_kernel(AttnParams p) {
     }
     __syncthreads();
     const int cn = min(kChunk, ns - c0);
-    for (int j0 = r; j0 < cn; j0 += R * kU) {
+#pragma unroll 4
+    for (int j0 = 0; j0 < cn; j0 += kMergeLanes) {
 #pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const int j = j0 + u * R;
+      for (int q = 0; q < kLpt; ++q) {
+        const int j = j0 + rt + kRt * q;
         if (j < cn) {
-          la[u] = fmaf(w_s[j], l_s[j], la[u]);
-          aa[u] = fmaf(w_s[j], ac[(int64_t)(c0 + j) * D], aa[u]);
+          la[q] = fmaf(w_s[j], l_s[j], la[q]);
+          aa[q] = fmaf(w_s[j], ac[(int64_t)(c0 + j) * D], aa[q]);
         }
       }
     }
     __syncthreads();
   }
-  part_l[r][threadIdx.x % kMergeE] = (la[0] + la[1]) + (la[2] + la[3]);
-  part_a[r][threadIdx.x % kMergeE] = (aa[0] + aa[1]) + (aa[2] + aa[3]);
-  __syncthreads();
-  if (r != 0) return;
-  const int ei = threadIdx.x;
-  float l = part_l[0][ei], a = part_a[0][ei];
 #pragma unroll
-  for (int i = 1; i < R; ++i) {
-    l += part_l[i][ei];
-    a += part_a[i][ei];
+  for (int q = 0; q < kLpt; ++q) {
+    part_l[rt + kRt * q][ei] = la[q];
+    part_a[rt + kRt * q][ei] = aa[q];
+  }
+  __syncthreads();
+  if (threadIdx.x >= E) return;
+  float l = 0.f, a = 0.f;
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const float pl = (part_l[r][ei] + part_l[r + 8][ei]) + (part_l[r + 16][ei] + part_l[r + 24][ei]);
+    const float pa = (part_a[r][ei] + part_a[r + 8][ei]) + (part_a[r + 16][ei] + part_a[r + 24][ei]);
+    l = r == 0 ? pl : l + pl;
+    a = r == 0 ? pa : a + pa;
   }
   const float o = valid ? a / l : __builtin_nanf("");
   if (kBf16)
@@ -411,13 +423,24 @@ void launch_split(const AttnParams& p, hipStream_t stream) {
   }
 }
 
+// Eight threads per element (32 elements per workgroup) unless that leaves
+// fewer than 2048 workgroups; then 32 threads per element (8 per workgroup).
+// The output bytes are the same either way.
+constexpr int64_t kMergeWideBelow = 2048;
+
+template <int D, int kRt>
+void launch_merge_rt(const AttnParams& p, hipStream_t stream) {
+  const dim3 grid((unsigned)((int64_t)p.T * p.H * (D / (kThreads / kRt))));
+  if (p.out_bf16)
+    hipLaunchKernelGGL((bigemm_attn_merge_kernel<D, true, kRt>), grid, dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((bigemm_attn_merge_kernel<D, false, kRt>), grid, dim3(kThreads), 0, stream, p);
+}
+
 template <int D>
 void launch_merge(const AttnParams& p, hipStream_t stream) {
-  const dim3 grid((unsigned)((int64_t)p.T * p.H * (D / kMergeE)));
-  if (p.out_bf16)
-    hipLaunchKernelGGL((bigemm_attn_merge_kernel<D, true>), grid, dim3(kThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL((bigemm_attn_merge_kernel<D, false>), grid, dim3(kThreads), 0, stream, p);
+  if ((int64_t)p.T * p.H * (D / 32) < kMergeWideBelow) launch_merge_rt<D, 32>(p, stream);
+  else launch_merge_rt<D, 8>(p, stream);
 }
 
 }  // namespace

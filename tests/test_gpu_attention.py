@@ -338,3 +338,20 @@ def test_decode_workload_sampled():
     assert_parity(o[torch.as_tensor(pick)], Q[pick], P, seqs[pick], poss[pick])
     for i in pick:
         assert H.byte_diff(P.attend(Q[i:i + 1], seqs[i:i + 1], poss[i:i + 1])[0], o[i]) == 0, i
+
+
+def test_merge_thread_mappings_agree():
+    """The merge spreads each output element over 32 threads when the call has few
+    (token, head) pairs, and over 8 from 2048 workgroups of the narrow mapping on (D = 128,
+    16 heads: from 32 tokens). Both compute the same lane sums and tree: 31 tokens (wide)
+    and the same tokens inside a call of 32 (narrow) give identical bytes."""
+    lens = [3000, 700, 257]
+    P = Paged(470, lens, 4, 128, 32).write_all()
+    rng = np.random.default_rng(471)
+    seqs = rng.integers(0, len(lens), 32).astype(np.int32)
+    poss = np.array([rng.integers(0, lens[s]) for s in seqs], np.int32)
+    Q = normal_bf16(472, (32, 16, 128))
+    wide = P.attend(Q[:31], seqs[:31], poss[:31])
+    narrow = P.attend(Q, seqs, poss)
+    assert H.byte_diff(narrow[:31], wide) == 0
+    assert_parity(narrow, Q, P, seqs, poss)
