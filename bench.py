@@ -7,7 +7,9 @@ ABI with inputs resident in HBM. Also reported:
 
 * ``m_sweep``: TFLOP/s and % of the bf16 MFMA peak for M = 1 ... 4096 at
   K = N = 4096 (small M rotates among buffer sets larger than the 256 MB
-  last-level cache, so W is read from HBM), with achieved algorithmic HBM GB/s;
+  last-level cache, so W is read from HBM; ``us_warm_llc`` is the same call on
+  one buffer set), with achieved algorithmic HBM GB/s and % of the roofline
+  bound max(flops / MFMA peak, algorithmic bytes / HBM peak);
 * ``other_types_k4096_n4096``: the MXFP8 kernel (E4M3, K-varying E8M0 scales),
   fp16 inputs, bf16 output and int8 inputs at M = 1024 and 4096, each against
   its dense MFMA peak (context, not the metric);
@@ -108,8 +110,8 @@ def main():
                     help="one 256 MiB device copy before the GEMMs (scale reference for byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the GEMM shards by rows "
-              f"or columns with no exchange, which this build does not launch.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the GEMM would shard by rows "
+              f"or columns with no exchange, and no multi-GPU launch is implemented.", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -168,10 +170,20 @@ def main():
                     diffs += int((y.view(torch.int32) != Yfull[:m].view(torch.int32)).sum().item())
             f = 2.0 * m * N * K
             byts = 2 * m * K + 2 * K * N + 4 * m * N
-            sweep.append({"M": m, "us": round(t * 1e3, 2), "tflops": round(f / (t * 1e-3) / 1e12, 1),
-                          "pct_peak": round(100 * f / (t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 1),
-                          "hbm_gbs_algorithmic": round(byts / (t * 1e-3) / 1e9, 0),
-                          "cold_llc": nsets > 1})
+            # roofline time: the larger of the MFMA time and the HBM time of the algorithmic bytes
+            t_roof = max(f / (PEAK_BF16_TFLOPS * 1e12), byts / (PEAK_HBM_GBS * 1e9))
+            entry = {"M": m, "us": round(t * 1e3, 2), "tflops": round(f / (t * 1e-3) / 1e12, 1),
+                     "pct_peak": round(100 * f / (t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 1),
+                     "pct_roofline": round(100 * t_roof / (t * 1e-3), 1),
+                     "hbm_gbs_algorithmic": round(byts / (t * 1e-3) / 1e9, 0),
+                     "cold_llc": nsets > 1}
+            if nsets > 1:
+                # the same call with one buffer set, W warm in the last-level cache
+                for _ in range(3):
+                    bg.mm(Xs[0], Ws[0], out=Ys[0])
+                tw = _events(torch, stream, lambda i: bg.mm(Xs[0], Ws[0], out=Ys[0]), 20)
+                entry["us_warm_llc"] = round(tw * 1e3, 2)
+            sweep.append(entry)
             del Ws, Xs, Ys
             torch.cuda.empty_cache()
 

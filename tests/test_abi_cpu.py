@@ -198,3 +198,15 @@ def test_attention_binding_rejects_host_tensors():
         bg.kv_cache_write(q[:, :2], q[:, :2], kc, kc, bt, s, s)
     with pytest.raises(ValueError):
         bg.rmsnorm(torch.zeros((2, 64)), torch.zeros(64))
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: --gpus above 1 exits with status 2 and a message, before it
+    imports torch or touches a device."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr and r.stdout == ""
