@@ -98,6 +98,23 @@ def cpu_baseline(X, W, target_s: float = 15.0):
                       f"({flops / 1e9:.1f} GFLOP in {dt:.1f} s, fp64 accumulate)"}
 
 
+def cpu_baseline_one_thread(X, W, rows: int = 16):
+    """The same oracle on one thread, on a few rows (context beside the all-cores figure)."""
+    import oracle
+    threads = oracle.set_threads(0)
+    oracle.set_threads(1)
+    try:
+        t0 = time.perf_counter()
+        oracle.gemm_bf16(X[:rows], W, want_s=False)
+        dt = time.perf_counter() - t0
+    finally:
+        oracle.set_threads(threads)
+    flops = 2.0 * rows * W.shape[0] * W.shape[1]
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"{rows} of {X.shape[0]} rows of the M=4096 K=N=4096 bf16 workload "
+                      f"({flops / 1e9:.1f} GFLOP in {dt:.1f} s, fp64 accumulate)"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -345,6 +362,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(Xh, Wh)
+        line["cpu_baseline_one_thread"] = cpu_baseline_one_thread(Xh, Wh)
     print(json.dumps(line), flush=True)
 
 
