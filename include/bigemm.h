@@ -128,6 +128,8 @@ BIGEMM_API bigemm_status bigemm_create(const bigemm_desc* desc, bigemm_t* out);
  *
  * Memory: all buffers are device memory owned by the caller. The library
  * allocates nothing per call (this path has no split-K and hence no workspace).
+ * Device: the current HIP device must be the one the handle was created on
+ * (BIGEMM_ERR_ARG otherwise, checked on the host before anything is launched).
  * Errors: BIGEMM_ERR_ARG as above; BIGEMM_ERR_DEVICE if the launch fails (the
  * HIP error is consumed). Concurrent calls on different streams are safe;
  * bigemm_destroy must not race with calls in flight.

@@ -297,27 +297,29 @@ def mm(x, w, x_scale=None, w_scale=None, out=None, stream=None, out_dtype=None, 
         raise ValueError("out must be [M, N] with contiguous rows")
     if stream is None:
         stream = torch.cuda.current_stream(x.device).cuda_stream
-    if k_chunk:
-        if kind not in ("bf16", "f16"):
-            raise ValueError("split-K is provided for bf16 and fp16 inputs")
-        h = _handle(kind, dev, ytypes[out_dtype], int(k_chunk))
-        need = bigemm_workspace_size(h, M, N, K)
-        if workspace is None:
-            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
-        ws_bytes = workspace.numel() * workspace.element_size()
-        bigemm_run_ws(h, M, N, K, x.data_ptr(), _ld(x), w.data_ptr(), _ld(w), out.data_ptr(), _ld(out),
-                      0, 0, 0, 0, workspace.data_ptr(), ws_bytes, stream)
-        return out
-    h = _handle(kind, dev, ytypes[out_dtype])  # raises BigemmError for a combination not provided
-    if mx:
-        for t in (x_scale, w_scale):
-            if not t.is_cuda or t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
-                raise ValueError("scales must be 2-D CUDA tensors with contiguous rows")
-        bigemm_run(h, M, N, K, x.data_ptr(), _ld(x), w.data_ptr(), _ld(w), out.data_ptr(), _ld(out),
-                   x_scale.data_ptr(), _ld(x_scale), w_scale.data_ptr(), _ld(w_scale), stream)
-    else:
-        bigemm_run(h, M, N, K, x.data_ptr(), _ld(x), w.data_ptr(), _ld(w), out.data_ptr(), _ld(out),
-                   0, 0, 0, 0, stream)
+    # The handle belongs to x's device, and the library runs a handle only on its own device.
+    with torch.cuda.device(dev):
+        if k_chunk:
+            if kind not in ("bf16", "f16"):
+                raise ValueError("split-K is provided for bf16 and fp16 inputs")
+            h = _handle(kind, dev, ytypes[out_dtype], int(k_chunk))
+            need = bigemm_workspace_size(h, M, N, K)
+            if workspace is None:
+                workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+            ws_bytes = workspace.numel() * workspace.element_size()
+            bigemm_run_ws(h, M, N, K, x.data_ptr(), _ld(x), w.data_ptr(), _ld(w), out.data_ptr(), _ld(out),
+                          0, 0, 0, 0, workspace.data_ptr(), ws_bytes, stream)
+            return out
+        h = _handle(kind, dev, ytypes[out_dtype])  # raises BigemmError for a combination not provided
+        if mx:
+            for t in (x_scale, w_scale):
+                if not t.is_cuda or t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+                    raise ValueError("scales must be 2-D CUDA tensors with contiguous rows")
+            bigemm_run(h, M, N, K, x.data_ptr(), _ld(x), w.data_ptr(), _ld(w), out.data_ptr(), _ld(out),
+                       x_scale.data_ptr(), _ld(x_scale), w_scale.data_ptr(), _ld(w_scale), stream)
+        else:
+            bigemm_run(h, M, N, K, x.data_ptr(), _ld(x), w.data_ptr(), _ld(w), out.data_ptr(), _ld(out),
+                       0, 0, 0, 0, stream)
     return out
 
 

@@ -110,6 +110,18 @@ bigemm_status current_device_supported() {
   return state == 1 ? BIGEMM_OK : BIGEMM_ERR_UNSUPPORTED;
 }
 
+// A handle runs on the device it was created on: the current device must be
+// that one (a launch on another device would use the caller's stream and
+// buffers of a different GPU).
+bigemm_status handle_device_current(const bigemm_s* h) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return BIGEMM_ERR_DEVICE;
+  }
+  return dev == h->device ? BIGEMM_OK : BIGEMM_ERR_ARG;
+}
+
 // The one fixed kernel of the handle's input family (no split).
 hipError_t launch_unsplit(bigemm::Op op, int64_t M, int64_t N, int64_t K, const void* X, int64_t ldx, const void* W,
                           int64_t ldw, void* Y, int64_t ldy, const void* XS, int64_t ldxs, const void* WS,
@@ -341,6 +353,8 @@ bigemm_status bigemm_run_ws(bigemm_t h, int64_t M, int64_t N, int64_t K, const v
   if (!h) return BIGEMM_ERR_ARG;
   const bigemm_status st = check(h->op, M, N, K, X, ldx, W, ldw, Y, ldy, X_scale, ldxs, W_scale, ldws);
   if (st != BIGEMM_OK || M == 0) return st;
+  const bigemm_status dv = handle_device_current(h);
+  if (dv != BIGEMM_OK) return dv;
   uint64_t need = 0;
   bigemm_workspace_size(h, M, N, K, &need);
   if (need == 0) {  // unsplit handle, or a single chunk: the one fixed kernel
@@ -392,6 +406,8 @@ bigemm_status bigemm_run(bigemm_t h, int64_t M, int64_t N, int64_t K, const void
   if (h->k_chunk > 0) return BIGEMM_ERR_ARG;  // a split-K handle needs bigemm_run_ws
   const bigemm_status st = check(h->op, M, N, K, X, ldx, W, ldw, Y, ldy, X_scale, ldxs, W_scale, ldws);
   if (st != BIGEMM_OK || M == 0) return st;
+  const bigemm_status dv = handle_device_current(h);
+  if (dv != BIGEMM_OK) return dv;
   const hipError_t e = launch_unsplit(h->op, M, N, K, X, ldx, W, ldw, Y, ldy, X_scale, ldxs, W_scale, ldws,
                                       (hipStream_t)stream);
   return e == hipSuccess ? BIGEMM_OK : BIGEMM_ERR_DEVICE;
