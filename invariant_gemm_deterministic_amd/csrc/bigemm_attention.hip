@@ -258,7 +258,11 @@ void bigemm_attn_split_kernel(AttnParams p) {
         pl[e2] = (int)(l0 | (l1 << 16));
       }
     }
-    __syncthreads();
+    // v_s[wave] is this wave's own: its LDS writes and reads complete in order,
+    // so only the compiler must keep them in order.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt) {
       const i16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds<i16x4>(&v_s[wave][tr_row][16 * nt + tr_col]));
@@ -270,8 +274,11 @@ void bigemm_attn_split_kernel(AttnParams p) {
       o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pm), vop, o[nt], 0, 0, 0);
       o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pl), vop, o[nt], 0, 0, 0);
     }
-    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
+  __syncthreads();  // acc_s overlaps every wave's staging rows
 
   // per-wave outputs (lane l: column 16 nt + l % 16, heads 4 (l / 16) + r), then
   // the four waves added in order
