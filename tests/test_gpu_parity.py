@@ -72,6 +72,36 @@ def test_bf16_leading_dimensions():
     assert torch.all(out[:, N:] == -7.0)
 
 
+def test_bf16_largest_leading_dimensions():
+    """Leading dimensions at the documented limit (128 * ld * element size just below 2^31): the
+    kernel's 32-bit tile offsets reach 2.1e9 bytes and stay exact; one element more is rejected."""
+    M, N, K = 200, 136, 64
+    ldx = ldw = (1 << 23) - 8          # bf16: 128 * ld * 2 = 2^31 - 2048
+    ldy = (1 << 22) - 4                # fp32: 128 * ld * 4 = 2^31 - 2048
+    X = normal_bf16(31, (M, K))
+    W = normal_bf16(32, (K, N))
+    xb = torch.empty(M * ldx, dtype=torch.int16, device=DEV)
+    wb = torch.empty(K * ldw, dtype=torch.int16, device=DEV)
+    yb = torch.full((M * ldy,), -7.0, device=DEV)
+    xd = xb.as_strided((M, K), (ldx, 1))
+    wd = wb.as_strided((K, N), (ldw, 1))
+    yd = yb.as_strided((M, N), (ldy, 1))
+    xd.copy_(torch.from_numpy(X.view(np.int16)))
+    wd.copy_(torch.from_numpy(W.view(np.int16)))
+    bg.mm(xd, wd, out=yd)
+    torch.cuda.synchronize()
+    Y, S = oracle.gemm_bf16(X, W)
+    assert oracle.max_normalized_error(yd.cpu().numpy(), Y, S) <= TOL
+    assert torch.all(yb.as_strided((M, 8), (ldy, 1), N) == -7.0)   # past each row's N columns
+    h = bg._handle("bf16", 0)
+    args = dict(x=xd.data_ptr(), w=wd.data_ptr(), y=yd.data_ptr())
+    for lx, lw, ly in ((ldx + 8, ldw, ldy), (ldx, ldw + 8, ldy), (ldx, ldw, ldy + 4)):
+        assert bg.bigemm_run(h, M, N, K, args["x"], lx, args["w"], lw, args["y"], ly,
+                             check=False) == bg.BIGEMM_ERR_ARG
+    del xb, wb, yb
+    torch.cuda.empty_cache()
+
+
 def test_bf16_m_zero_is_noop_and_bad_args_rejected():
     xd = dev_bf16(normal_bf16(1, (4, 64)))
     wd = dev_bf16(normal_bf16(2, (64, 32)))
