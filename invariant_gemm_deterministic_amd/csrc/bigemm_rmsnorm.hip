@@ -15,8 +15,9 @@
 //   pass 2: y = (x * r) * gamma with r = 1 / sqrt(sum / d + eps), rounded once
 //           to the output type (round to nearest even for bf16).
 //
-// The reduction tree depends on d only. The row is read twice; the second
-// read is served by the caches (one row is at most 2 * 65536 * 4 bytes).
+// The reduction tree depends on d only. A thread keeps its first four chunks
+// in registers between the passes (all of a row up to d = 8192); chunks past
+// them are read again in pass 2, from the caches.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -27,6 +28,7 @@ namespace bigemm {
 namespace {
 
 constexpr int kNormThreads = 256;
+constexpr int kCached = 4;  // chunks of 8 elements a thread keeps in registers (D <= 8192)
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
@@ -82,8 +84,20 @@ void bigemm_rmsnorm_kernel(const uint8_t* __restrict__ X, int64_t ldx_bytes, con
   uint8_t* y = Y + (int64_t)blockIdx.x * ldy_bytes;
   const int nchunk = D / 8;
 
+  // The thread's first kCached chunks stay in registers for pass 2; chunks
+  // beyond them (D > 8192) are read again there. The order is the same.
+  float xv[kCached][8];
   float ss = 0.f;
-  for (int c = tid; c < nchunk; c += kNormThreads) {
+#pragma unroll
+  for (int i = 0; i < kCached; ++i) {
+    const int c = tid + i * kNormThreads;
+    if (c < nchunk) {
+      load8<kBf16>(x, c, xv[i]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss = fmaf(xv[i][e], xv[i][e], ss);
+    }
+  }
+  for (int c = tid + kCached * kNormThreads; c < nchunk; c += kNormThreads) {
     float v[8];
     load8<kBf16>(x, c, v);
 #pragma unroll
@@ -96,7 +110,18 @@ void bigemm_rmsnorm_kernel(const uint8_t* __restrict__ X, int64_t ldx_bytes, con
   const float total = ((wave_sum[0] + wave_sum[1]) + wave_sum[2]) + wave_sum[3];
   const float r = 1.0f / sqrtf(total / (float)D + eps);
 
-  for (int c = tid; c < nchunk; c += kNormThreads) {
+#pragma unroll
+  for (int i = 0; i < kCached; ++i) {
+    const int c = tid + i * kNormThreads;
+    if (c < nchunk) {
+      float g[8];
+      load8<kBf16>(gamma, c, g);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xv[i][e] = (xv[i][e] * r) * g[e];
+      store8<kBf16>(y, c, xv[i]);
+    }
+  }
+  for (int c = tid + kCached * kNormThreads; c < nchunk; c += kNormThreads) {
     float v[8], g[8];
     load8<kBf16>(x, c, v);
     load8<kBf16>(gamma, c, g);

@@ -38,7 +38,7 @@ def _check(y, ref, D, bf16_out):
     assert (err <= bound).all(), float((err / (np.abs(ref) + 1e-30)).max())
 
 
-SHAPES = [(1, 8), (7, 4096), (300, 1024), (64, 8192), (33, 520), (2, 65536)]
+SHAPES = [(1, 8), (7, 4096), (300, 1024), (64, 8192), (5, 8200), (33, 520), (2, 65536)]
 
 
 @pytest.mark.parametrize("M,D", SHAPES)
