@@ -301,7 +301,8 @@ BIGEMM_API bigemm_status bigemm_attn_workspace_size(const bigemm_kv_layout* kv, 
  *   max_context: an upper bound on positions[t] + 1, at most
  *   max_blocks * block_size (it sizes the grid and the workspace only);
  *   scale: the score scale, normally 1/sqrt(head_dim) rounded to float.
- * num_heads must be num_kv_heads times 1, 2, 4, 8 or 16.
+ * num_heads must be num_kv_heads times G, 1 <= G <= 16 (a group's query heads
+ * are the rows of one 16-row MFMA tile).
  * Data-dependent cases, handled on the device without faulting: a token whose
  * sequence or position is out of range (position >= max_context included)
  * gets an all-NaN output; a block-table entry outside [0, num_blocks) reached

@@ -157,7 +157,7 @@ bigemm_status attn_sizes(const bigemm_kv_layout* kv, int64_t T, int32_t H, int32
   if (st != BIGEMM_OK) return st;
   if (T < 0 || H < 1 || H % kv->num_kv_heads != 0) return BIGEMM_ERR_ARG;
   const int32_t G = H / kv->num_kv_heads;
-  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return BIGEMM_ERR_ARG;
+  if (G < 1 || G > 16) return BIGEMM_ERR_ARG;  // the query heads of a group fill one 16-row MFMA tile
   if (max_context < 1 || (int64_t)max_context > (int64_t)kv->max_blocks * kv->block_size) return BIGEMM_ERR_ARG;
   const int64_t ns = ((int64_t)max_context + bigemm::kAttnSplit - 1) / bigemm::kAttnSplit;
   if (T * kv->num_kv_heads * ns > INT32_MAX || T * H * (kv->head_dim / 32) > INT32_MAX) return BIGEMM_ERR_ARG;

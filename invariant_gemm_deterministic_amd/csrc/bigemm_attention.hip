@@ -123,8 +123,12 @@ void bigemm_attn_split_kernel(AttnParams p) {
   __shared__ float red_m[4][G];
   __shared__ float red_l[4][G];
   __shared__ int32_t blk_s[kAttnSplit];
-  float (*acc_s)[G][D] = (float (*)[G][D])&v_s[0][0][0];   // after the values: per-wave outputs
-  static_assert(sizeof(v_s) >= sizeof(float) * 4 * G * D, "acc_s fits in v_s");
+  // After the values: per-wave outputs for all 16 rows of the MFMA tile (rows
+  // past G hold zeros and are not read). Every row is stored unconditionally:
+  // with stores predicated on h < G, this compiler placed one output of the
+  // G = 15, D = 64 kernel at a wrong offset when it paired the stores.
+  float (*acc_s)[16][D] = (float (*)[16][D])&v_s[0][0][0];
+  static_assert(sizeof(v_s) >= sizeof(float) * 4 * 16 * D, "acc_s fits in v_s");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int s = blockIdx.x % p.nsplit;
@@ -285,10 +289,7 @@ void bigemm_attn_split_kernel(AttnParams p) {
 #pragma unroll
   for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int h = 4 * (lane >> 4) + r;
-      if (h < G) acc_s[wave][h][16 * nt + qh] = o[nt][r];
-    }
+    for (int r = 0; r < 4; ++r) acc_s[wave][4 * (lane >> 4) + r][16 * nt + qh] = o[nt][r];
   __syncthreads();
 
   const int64_t base = ((int64_t)t * p.H + (int64_t)kvh * G) * p.nsplit + s;  // (t, head kvh*G, s)
@@ -418,16 +419,20 @@ void bigemm_kv_write_kernel(KvWriteParams p) {
   *(i32x4*)(p.V + dst) = *(const i32x4*)(p.V_new + src);
 }
 
+// One instantiation per group size G = H / Hkv in 1..16 (the callers check the range).
+template <int D, int G>
+void launch_split_g(const AttnParams& p, hipStream_t stream, dim3 grid) {
+  if (p.H / p.Hkv == G) {
+    hipLaunchKernelGGL((bigemm_attn_split_kernel<D, G>), grid, dim3(kThreads), 0, stream, p);
+  } else if constexpr (G < 16) {
+    launch_split_g<D, G + 1>(p, stream, grid);
+  }
+}
+
 template <int D>
 void launch_split(const AttnParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)((int64_t)p.T * p.Hkv * p.nsplit));
-  switch (p.H / p.Hkv) {
-    case 1: hipLaunchKernelGGL((bigemm_attn_split_kernel<D, 1>), grid, dim3(kThreads), 0, stream, p); break;
-    case 2: hipLaunchKernelGGL((bigemm_attn_split_kernel<D, 2>), grid, dim3(kThreads), 0, stream, p); break;
-    case 4: hipLaunchKernelGGL((bigemm_attn_split_kernel<D, 4>), grid, dim3(kThreads), 0, stream, p); break;
-    case 8: hipLaunchKernelGGL((bigemm_attn_split_kernel<D, 8>), grid, dim3(kThreads), 0, stream, p); break;
-    default: hipLaunchKernelGGL((bigemm_attn_split_kernel<D, 16>), grid, dim3(kThreads), 0, stream, p); break;
-  }
+  launch_split_g<D, 1>(p, stream, grid);
 }
 
 // Eight threads per element (32 elements per workgroup) unless that leaves

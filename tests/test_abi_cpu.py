@@ -159,9 +159,9 @@ def test_paged_attention_check_args():
     assert achk() == OK
     assert achk(odt=bg.BIGEMM_BF16) == OK
     assert achk(T=0, Q=0, K=0, V=0, s=0, p=0, bt=0, O=0, ws=0, wsb=0) == OK
-    for H in (2, 8, 16, 32):
+    for H in (2, 6, 8, 10, 14, 16, 30, 32):  # groups of 1 to 16 query heads per KV head
         assert achk(H=H) == OK, H
-    for H in (0, 3, 6, 64):  # not a multiple of 2 KV heads, or a group of 3 or 32
+    for H in (0, 3, 34, 64):  # not a multiple of 2 KV heads, or a group of 17 or 32
         assert achk(H=H) == ARG, H
     assert achk(kv=_kv(head_dim=64)) == OK and achk(kv=_kv(head_dim=96)) == ARG
     for bs, ok in ((1, OK), (4096, OK), (24, ARG), (0, ARG), (8192, ARG)):

@@ -145,6 +145,12 @@ PARITY = [  # (D, H, Hkv, bs, out_dtype)
     (64, 8, 2, 32, torch.bfloat16),
     (128, 32, 2, 32, torch.float32),
     (64, 16, 1, 16, torch.bfloat16),
+    # group sizes that are not powers of two (28 query heads over 4 KV heads is a common layout)
+    (128, 28, 4, 32, torch.float32),
+    (64, 9, 3, 16, torch.bfloat16),
+    (128, 10, 2, 8, torch.float32),
+    (128, 12, 2, 64, torch.bfloat16),
+    (64, 15, 1, 32, torch.float32),
 ]
 
 
@@ -314,7 +320,7 @@ def test_bad_arguments_launch_nothing():
             seqs.data_ptr(), poss.data_ptr(), P.bt_d.data_ptr(), out.data_ptr())
     assert bg.bigemm_paged_attention(*args, ws.data_ptr(), need - 4, 0, check=False) == bg.BIGEMM_ERR_ARG
     assert bg.bigemm_paged_attention(*args, ws.data_ptr() + 4, need, 0, check=False) == bg.BIGEMM_ERR_ARG
-    bad = (kv, 2, 12, 64) + args[4:]  # 12 heads over 2 KV heads: groups of 6 are not provided
+    bad = (kv, 2, 34, 64) + args[4:]  # 34 heads over 2 KV heads: a group of 17 is more than one MFMA tile
     assert bg.bigemm_paged_attention(*bad, ws.data_ptr(), 1 << 20, 0, check=False) == bg.BIGEMM_ERR_ARG
     torch.cuda.synchronize()
     assert (out == 7.0).all()
