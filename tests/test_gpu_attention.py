@@ -361,3 +361,18 @@ def test_merge_thread_mappings_agree():
     narrow = P.attend(Q, seqs, poss)
     assert H.byte_diff(narrow[:31], wide) == 0
     assert_parity(narrow, Q, P, seqs, poss)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_every_group_size(D):
+    """Every group size G = H / Hkv from 1 to 16 has its own compiled split kernel: each
+    against the oracle on tokens that end inside the first split, on a split boundary and in
+    a later split (one KV head, so H = G)."""
+    lens = [1, 257, 700]
+    P = Paged(480 + D, lens, 1, D, 32).write_all()
+    seqs = np.array([0, 1, 1, 2, 2], np.int32)
+    poss = np.array([0, 0, 256, 255, 699], np.int32)
+    for G in range(1, 17):
+        Q = normal_bf16(481 + G, (len(seqs), G, D))
+        o = P.attend(Q, seqs, poss)
+        assert_parity(o, Q, P, seqs, poss)
