@@ -269,7 +269,8 @@ def main():
     if not args.no_sweep:
         gen = torch.Generator(device=dev)
         for (B, L, Hq, Hkv, D) in ((64, 4096, 32, 8, 128), (64, 4096, 64, 8, 128), (64, 4096, 8, 8, 128),
-                                   (8, 32768, 32, 8, 128), (1, 131072, 32, 8, 128), (64, 4096, 32, 8, 64)):
+                                   (64, 4096, 28, 4, 128), (8, 32768, 32, 8, 128), (1, 131072, 32, 8, 128),
+                                   (64, 4096, 32, 8, 64)):
             gen.manual_seed(B * 7 + L)
             bs = 32
             nbps = L // bs
