@@ -14,7 +14,7 @@
 //
 // Split kernel: one workgroup per (query token t, KV head, split s) covers
 // positions [256 s, min(256 s + 256, pos + 1)) for the G query heads sharing
-// the KV head.
+// the KV head (G = 1..16, one instantiation each).
 //   scores: each wave takes 64 positions as four 16 x 16 tiles of
 //           v_mfma_f32_16x16x32_bf16 (query heads as rows, padded with zeros,
 //           positions as columns, the head dimension in steps of 32 in a fixed
@@ -22,10 +22,11 @@
 //   softmax: per head, the split maximum m and p_j = exp(s_j - m) (fp32), and
 //           l = sum_j p_j (a fixed DPP tree per wave, then the four waves in
 //           order);
-//   values: each wave stages its 64 V rows through LDS, 32 at a time, and
-//           reads them back with ds_read_b64_tr_b16 as the B operand of
-//           v_mfma_f32_16x16x32_bf16; the fp32 weights enter as three bf16
-//           parts with an exact sum, positions in a fixed order; then the
+//   values: each wave stages its 64 V rows through its own LDS rows, 32 at a
+//           time, and reads them back with ds_read_b64_tr_b16 as the B
+//           operand of v_mfma_f32_16x16x32_bf16 (no block barrier: one wave's
+//           LDS accesses complete in order); the fp32 weights enter as three
+//           bf16 parts with an exact sum, positions in a fixed order; then the
 //           four waves' outputs are added in order.
 // Each split result is a fixed function of that split's inputs.
 // Merge kernel: per (token, query head), the splits' (m_s, l_s, acc_s) are
