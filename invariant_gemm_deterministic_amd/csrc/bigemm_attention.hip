@@ -337,12 +337,12 @@ void bigemm_attn_merge_kernel(AttnParams p) {
   __shared__ float part_a[kMergeLanes][E];
   __shared__ float part_l[kMergeLanes][E];
   constexpr int kSlices = D / E;
-  // Placement only: workgroups are dispatched round-robin over the 8 XCDs;
+  // Placement only: workgroups are dispatched round-robin over the 8 XCDs.
+  // When slices are narrower than a 128-byte line of the partials (E < 32),
   // renumbering them so that consecutive numbers share an XCD keeps the
-  // slices of one (token, head), which split each 128-byte line of the
-  // partials, on one L2.
+  // slices of one (token, head) on one L2.
   const int nwg = (int)gridDim.x, per = nwg / 8, bid = (int)blockIdx.x;
-  const int vb = bid < per * 8 ? (bid % 8) * per + bid / 8 : bid;
+  const int vb = (E < 32 && bid < per * 8) ? (bid % 8) * per + bid / 8 : bid;
   const int th = vb / kSlices;  // t * H + h
   const int ei = threadIdx.x % E;
   const int e = (vb % kSlices) * E + ei;
