@@ -26,6 +26,7 @@ Sources of truth used here, none of which is the oracle itself:
 """
 from __future__ import annotations
 
+import functools
 import math
 import os
 from fractions import Fraction
@@ -192,17 +193,26 @@ def check_linspace_closed_form(orc: oracle.Oracle):
         assert abs(Y[0, t] - float(exact_val)) <= bound, (j, Y[0, t], float(exact_val))
 
 
+@functools.lru_cache(maxsize=1)
+def _linspace_row0_and_cols():
+    """Row 0 of the blog's bf16 linspace a [2048, 4096] and six columns of b [4096, 4096]
+    (generated once per process: the full matrices are 24M elements)."""
+    B, D = 2048, 4096
+    a_row0 = linspace_bf16(-1000.0, 1000.0, B * D)[:D].copy()
+    b = linspace_bf16(-1000.0, 1000.0, D * D, (D, D))
+    cols = [0, 1, 2047, 2048, 4094, 4095]
+    return a_row0, np.ascontiguousarray(b[:, cols]), cols
+
+
 def check_linspace_bf16_row0(orc: oracle.Oracle):
     """bf16-rounded linspace: row 0 of a rounds to exactly -1000, so (a.b)[0, j] is
     -1000 times the exact column sum of b; the exact sums are antisymmetric,
     y[0, j] = -y[0, D-1-j], because b[k, j] = -b[D-1-k, D-1-j]."""
-    B, D = 2048, 4096
-    a_full_row0 = linspace_bf16(-1000.0, 1000.0, B * D)[:D]  # row 0 of a
+    D = 4096
+    a_full_row0, bcols, cols = _linspace_row0_and_cols()
     assert np.all(t_bf16(a_full_row0) == -1000.0)
-    b = linspace_bf16(-1000.0, 1000.0, D * D, (D, D))
-    cols = [0, 1, 2047, 2048, 4094, 4095]
-    Y, S = orc.gemm_bf16(a_full_row0[None, :], np.ascontiguousarray(b[:, cols]))
-    bd = t_bf16(b[:, cols])
+    Y, S = orc.gemm_bf16(a_full_row0[None, :], bcols)
+    bd = t_bf16(bcols)
     sums = np.array([math.fsum(bd[:, t]) for t in range(len(cols))])
     _close(Y[0], -1000.0 * sums, oracle.gamma(D - 1, U64) * S[0], "bf16 linspace row 0")
     assert sums[0] == -sums[5] and sums[1] == -sums[4] and sums[2] == -sums[3]
