@@ -11,8 +11,10 @@ ABI with inputs resident in HBM. Also reported:
   one buffer set), with achieved algorithmic HBM GB/s and % of the roofline
   bound max(flops / MFMA peak, algorithmic bytes / HBM peak);
 * ``other_types_k4096_n4096``: the MXFP8 kernel (E4M3, K-varying E8M0 scales),
-  fp16 inputs, bf16 output and int8 inputs at M = 1024 and 4096, each against
-  its dense MFMA peak (context, not the metric);
+  fp16 inputs, bf16 output, bf16 with W given as [N, K] rows, and int8 inputs
+  at M = 1024 and 4096, each against its dense MFMA peak (context, not the
+  metric); ``w_transposed_byte_diffs`` compares the [N, K]-row call at
+  M = 4096 with the headline output bit for bit (must be 0);
 * ``split_k_context``: the opt-in pinned-chunk split-K handle at small M (cold
   LLC) and on the long-K workload, against the unsplit kernel (context);
 * ``rmsnorm_bf16_context``: the batch-invariant RMSNorm (bf16, D = 4096) against
@@ -299,6 +301,7 @@ def main():
 
     # ------------------------------------------------------- MXFP8 (context)
     mx = []
+    wt_byte_diffs = None
     if not args.no_sweep:
         from bigemm_inputs import SCALE_SEED_OFFSET, e8m0_scales, normal_e4m3
         Xm = torch.from_numpy(normal_e4m3(SEED_X, (4096, K))).to(dev)
@@ -321,8 +324,15 @@ def main():
         Wi = torch.from_numpy(int_i8(SEED_W, (K, N))).to(dev)
         Yi = torch.empty((4096, N), dtype=torch.int32, device=dev)
         Yb = torch.empty((4096, N), dtype=torch.bfloat16, device=dev)
+        # W given as [N, K] rows (a linear layer's weight layout): same bytes as the [K, N] call
+        WT = W.t().contiguous()
+        for _ in range(2):
+            bg.mm(X, WT.t(), out=Y)
+        torch.cuda.synchronize()
+        wt_byte_diffs = int((Y.view(torch.int32) != Yfull.view(torch.int32)).sum().item()) if M == 4096 else None
         for name, fn, peak in (("f16", lambda m: bg.mm(X16[:m], W16, out=Y[:m]), PEAK_BF16_TFLOPS),
                                ("bf16_out", lambda m: bg.mm(X[:m], W, out=Yb[:m]), PEAK_BF16_TFLOPS),
+                               ("bf16_w_transposed", lambda m: bg.mm(X[:m], WT.t(), out=Y[:m]), PEAK_BF16_TFLOPS),
                                ("i8", lambda m: bg.mm(Xi[:m], Wi, out=Yi[:m]), PEAK_I8_TOPS)):
             for m in (1024, 4096):
                 for _ in range(5):
@@ -331,7 +341,7 @@ def main():
                 f = 2.0 * m * N * K
                 mx.append({"kind": name, "M": m, "us": round(t * 1e3, 2), "tflops": round(f / (t * 1e-3) / 1e12, 1),
                            "pct_peak": round(100 * f / (t * 1e-3) / 1e12 / peak, 1)})
-        del X16, W16, Xi, Wi, Yi, Yb
+        del X16, W16, Xi, Wi, Yi, Yb, WT
 
     line = {
         "metric": "TFLOP/s vs M (1-4096) at K=N=4096, % MFMA peak; invariance byte-diffs=0",
@@ -355,6 +365,7 @@ def main():
                      "traffic": measured_traffic() if M == 4096 else None},
         "m_sweep": sweep,
         "other_types_k4096_n4096": mx,
+        "w_transposed_byte_diffs": wt_byte_diffs if mx else None,
         "split_k_context": split,
         "rmsnorm_bf16_context": norm,
         "paged_attention_decode_context": attn,

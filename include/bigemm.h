@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define BIGEMM_ABI_VERSION 5
+#define BIGEMM_ABI_VERSION 6
 
 /* Exported entry points (the library is built with hidden visibility by default). */
 #if defined(__GNUC__)
@@ -165,6 +165,32 @@ BIGEMM_API bigemm_status bigemm_run(bigemm_t h, int64_t M, int64_t N, int64_t K,
  * BIGEMM_ERR_ARG on such a handle: it needs a workspace).
  */
 BIGEMM_API bigemm_status bigemm_create_split_k(const bigemm_desc* desc, int32_t k_chunk, bigemm_t* out);
+
+/*
+ * Handle for bf16 or fp16 inputs whose W is given as its transpose: an
+ * [N, K] row-major array with leading dimension ldw >= K (the layout in
+ * which a linear layer keeps its weight), so such a weight needs no copy.
+ * It is the same multiply, Y = X * W with W[k, j] read from element
+ * [j, k] of that array, and the same fixed recipe as bigemm_run (one tile
+ * configuration, whole K in one workgroup, ascending K blocks, one MFMA
+ * shape): the MFMA chain sees the same operands in the same order, so Y has
+ * exactly the bytes of a bigemm_create handle given the same logical W as
+ * [K, N]. Only the staging of W's tile differs.
+ * Run it with bigemm_run or bigemm_run_ws (no workspace); the requirements of
+ * bigemm_run hold with ldw >= K in place of ldw >= N (still: every row of the
+ * array 16-byte aligned and 128 * ldw * 2 below 2^31). MXFP8 and int8
+ * descriptors return BIGEMM_ERR_UNSUPPORTED, as do devices other than gfx950;
+ * there is no split-K form. *out is NULL on failure.
+ */
+BIGEMM_API bigemm_status bigemm_create_wt(const bigemm_desc* desc, bigemm_t* out);
+
+/*
+ * The argument checks of a bigemm_create_wt handle's bigemm_run, as a pure
+ * host function (no HIP call): W [N, K] with ldw >= K; no scale arrays.
+ */
+BIGEMM_API bigemm_status bigemm_check_args_wt(const bigemm_desc* desc, int64_t M, int64_t N, int64_t K,
+                                   const void* X, int64_t ldx, const void* W, int64_t ldw,
+                                   const void* Y, int64_t ldy);
 
 /*
  * Device workspace, in bytes, that bigemm_run_ws needs for this shape:

@@ -20,7 +20,7 @@ __all__ = [
     "BIGEMM_BF16", "BIGEMM_F32", "BIGEMM_E4M3", "BIGEMM_E8M0",
     "BigemmError", "bigemm_desc", "library_path", "load",
     "bigemm_create", "bigemm_run", "bigemm_destroy", "bigemm_status_str", "bigemm_get_config",
-    "bigemm_check_args", "bigemm_abi_version", "mm",
+    "bigemm_check_args", "bigemm_abi_version", "mm", "bigemm_create_wt", "bigemm_check_args_wt",
     "bigemm_kv_layout", "bigemm_kv_cache_write", "bigemm_attn_workspace_size", "bigemm_paged_attention",
     "bigemm_paged_attention_check_args", "kv_cache_write", "paged_attention", "ATTN_SPLIT",
 ]
@@ -90,6 +90,10 @@ def load():
         lib.bigemm_check_args.restype = ctypes.c_int
         lib.bigemm_check_args.argtypes = [ctypes.POINTER(bigemm_desc), i64, i64, i64, vp, i64, vp, i64,
                                           vp, i64, vp, i64, vp, i64]
+        lib.bigemm_create_wt.restype = ctypes.c_int
+        lib.bigemm_create_wt.argtypes = [ctypes.POINTER(bigemm_desc), ctypes.POINTER(vp)]
+        lib.bigemm_check_args_wt.restype = ctypes.c_int
+        lib.bigemm_check_args_wt.argtypes = [ctypes.POINTER(bigemm_desc), i64, i64, i64, vp, i64, vp, i64, vp, i64]
         lib.bigemm_abi_version.restype = i32
         lib.bigemm_abi_version.argtypes = []
         lib.bigemm_rmsnorm.restype = ctypes.c_int
@@ -157,6 +161,16 @@ def bigemm_create_split_k(x_type: int, w_type: int, y_type: int, k_chunk: int) -
     return int(h.value)
 
 
+def bigemm_create_wt(x_type: int, w_type: int, y_type: int = BIGEMM_F32) -> int:
+    """Create a handle whose W is given as [N, K] (bf16 / fp16 inputs). Raises BigemmError."""
+    h = ctypes.c_void_p()
+    d = _desc(x_type, w_type, y_type, 0)
+    st = load().bigemm_create_wt(ctypes.byref(d), ctypes.byref(h))
+    if st != BIGEMM_OK:
+        raise BigemmError(st, "bigemm_create_wt")
+    return int(h.value)
+
+
 def bigemm_workspace_size(h: int, M: int, N: int, K: int) -> int:
     n = ctypes.c_uint64()
     st = load().bigemm_workspace_size(ctypes.c_void_p(h) if h else None, M, N, K, ctypes.byref(n))
@@ -212,6 +226,14 @@ def bigemm_check_args(x_type: int, w_type: int, y_type: int, scale_block: int, M
                                         Y or None, ldy, X_scale or None, ldxs, W_scale or None, ldws))
 
 
+def bigemm_check_args_wt(x_type: int, w_type: int, y_type: int, M: int, N: int, K: int,
+                         X: int, ldx: int, W: int, ldw: int, Y: int, ldy: int) -> int:
+    """Argument validation of a bigemm_create_wt handle (W [N, K], ldw >= K); returns the status code."""
+    d = _desc(x_type, w_type, y_type, 0)
+    return int(load().bigemm_check_args_wt(ctypes.byref(d), M, N, K, X or None, ldx, W or None, ldw,
+                                           Y or None, ldy))
+
+
 # ------------------------------------------------------------------ torch wrapper
 _handles = {}
 
@@ -220,16 +242,21 @@ _handles = {}
 _FAMILIES = {"bf16": (BIGEMM_BF16, 0), "f16": (BIGEMM_F16, 0), "mx": (BIGEMM_E4M3, 32), "i8": (BIGEMM_I8, 0)}
 
 
-def _handle(kind: str, device_index: int, y_type: int = BIGEMM_F32, k_chunk: int = 0) -> int:
-    """One cached handle per (input family, output type, split-K chunk, device)."""
+def _handle(kind: str, device_index: int, y_type: int = BIGEMM_F32, k_chunk: int = 0, wt: bool = False) -> int:
+    """One cached handle per (input family, output type, split-K chunk, W layout, device)."""
     import torch
 
-    key = (kind, y_type, k_chunk, device_index)
+    key = (kind, y_type, k_chunk, wt, device_index)
     h = _handles.get(key)
     if h is None:
         t, sb = _FAMILIES[kind]
         with torch.cuda.device(device_index):
-            h = bigemm_create_split_k(t, t, y_type, k_chunk) if k_chunk else bigemm_create(t, t, y_type, sb)
+            if k_chunk:
+                h = bigemm_create_split_k(t, t, y_type, k_chunk)
+            elif wt:
+                h = bigemm_create_wt(t, t, y_type)
+            else:
+                h = bigemm_create(t, t, y_type, sb)
         _handles[key] = h
     return h
 
@@ -248,6 +275,10 @@ def mm(x, w, x_scale=None, w_scale=None, out=None, stream=None, out_dtype=None, 
     MXFP8: ``x``/``w`` are torch.float8_e4m3fn (or uint8 codes) and
     ``x_scale`` [M, K/32], ``w_scale`` [K/32, N] are uint8 E8M0 bytes. Rows
     must be contiguous; the leading dimension is taken from ``stride(0)``.
+    For bf16 and fp16, ``w`` may instead be the transpose of an [N, K] array
+    with contiguous rows (``weight.t()`` of a linear layer's weight, so
+    ``stride(0) == 1``): it then runs through the W-transposed handle with no
+    copy, and the output bytes are those of the [K, N] layout.
     Output: ``out`` if given (its dtype selects the output type), else a new
     [M, N] tensor of ``out_dtype`` (float32 or bfloat16 for floating inputs,
     default float32; int32 for int8).
@@ -263,7 +294,9 @@ def mm(x, w, x_scale=None, w_scale=None, out=None, stream=None, out_dtype=None, 
     K2, N = w.shape
     if K != K2:
         raise ValueError(f"inner dimensions differ: {K} vs {K2}")
-    for t in (x, w):
+    # W given as the transposed view of an [N, K] array with contiguous rows.
+    wt = N > 1 and w.stride(1) != 1 and (K == 1 or w.stride(0) == 1)
+    for t in (x, w.t() if wt else w):
         if not t.is_cuda or (t.shape[1] > 1 and t.stride(1) != 1):
             raise ValueError("operands must be CUDA tensors with contiguous rows")
     if x.dtype != w.dtype:
@@ -299,6 +332,8 @@ def mm(x, w, x_scale=None, w_scale=None, out=None, stream=None, out_dtype=None, 
         stream = torch.cuda.current_stream(x.device).cuda_stream
     # The handle belongs to x's device, and the library runs a handle only on its own device.
     with torch.cuda.device(dev):
+        if wt and (k_chunk or kind not in ("bf16", "f16")):
+            raise ValueError("a transposed w ([N, K] rows) is taken for bf16 and fp16 without split-K")
         if k_chunk:
             if kind not in ("bf16", "f16"):
                 raise ValueError("split-K is provided for bf16 and fp16 inputs")
@@ -310,7 +345,7 @@ def mm(x, w, x_scale=None, w_scale=None, out=None, stream=None, out_dtype=None, 
             bigemm_run_ws(h, M, N, K, x.data_ptr(), _ld(x), w.data_ptr(), _ld(w), out.data_ptr(), _ld(out),
                           0, 0, 0, 0, workspace.data_ptr(), ws_bytes, stream)
             return out
-        h = _handle(kind, dev, ytypes[out_dtype])  # raises BigemmError for a combination not provided
+        h = _handle(kind, dev, ytypes[out_dtype], 0, wt)  # raises BigemmError for a combination not provided
         if mx:
             for t in (x_scale, w_scale):
                 if not t.is_cuda or t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
@@ -318,7 +353,8 @@ def mm(x, w, x_scale=None, w_scale=None, out=None, stream=None, out_dtype=None, 
             bigemm_run(h, M, N, K, x.data_ptr(), _ld(x), w.data_ptr(), _ld(w), out.data_ptr(), _ld(out),
                        x_scale.data_ptr(), _ld(x_scale), w_scale.data_ptr(), _ld(w_scale), stream)
         else:
-            bigemm_run(h, M, N, K, x.data_ptr(), _ld(x), w.data_ptr(), _ld(w), out.data_ptr(), _ld(out),
+            ldw = _ld(w.t()) if wt else _ld(w)
+            bigemm_run(h, M, N, K, x.data_ptr(), _ld(x), w.data_ptr(), ldw, out.data_ptr(), _ld(out),
                        0, 0, 0, 0, stream)
     return out
 

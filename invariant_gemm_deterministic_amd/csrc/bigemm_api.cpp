@@ -23,6 +23,7 @@ struct bigemm_s {
   bigemm::Op op;
   int device;
   int32_t k_chunk;  // 0: no split-K
+  bool w_trans;     // W given as its transpose, [N, K] (bigemm_create_wt)
 };
 
 namespace {
@@ -45,10 +46,12 @@ bigemm::Op desc_op(const bigemm_desc* d) {
   return op;
 }
 
+// wt: W is [N, K] with ldw >= K (bf16 / fp16 only) instead of [K, N] with ldw >= N.
 bigemm_status check(bigemm::Op op, int64_t M, int64_t N, int64_t K, const void* X, int64_t ldx,
                     const void* W, int64_t ldw, const void* Y, int64_t ldy, const void* XS,
-                    int64_t ldxs, const void* WS, int64_t ldws) {
+                    int64_t ldxs, const void* WS, int64_t ldws, bool wt = false) {
   if (op.in == 0) return BIGEMM_ERR_UNSUPPORTED;
+  if (wt && op.in != bigemm::kInBf16 && op.in != bigemm::kInF16) return BIGEMM_ERR_UNSUPPORTED;
   if (M < 0 || N < 1 || K < 1) return BIGEMM_ERR_ARG;
   if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return BIGEMM_ERR_ARG;
   if (((M + 127) / 128) * ((N + 127) / 128) > INT32_MAX) return BIGEMM_ERR_ARG;  // grid size
@@ -58,7 +61,7 @@ bigemm_status check(bigemm::Op op, int64_t M, int64_t N, int64_t K, const void* 
   if (es == 2 && (K % 8 != 0 || N % 8 != 0)) return BIGEMM_ERR_ARG;
   if (mx && (K % 32 != 0 || N % 16 != 0)) return BIGEMM_ERR_ARG;
   if (op.in == bigemm::kInI8 && (K % 16 != 0 || N % 16 != 0)) return BIGEMM_ERR_ARG;
-  if (ldx < K || ldw < N || ldy < N) return BIGEMM_ERR_ARG;
+  if (ldx < K || ldw < (wt ? K : N) || ldy < N) return BIGEMM_ERR_ARG;
   if ((ldx * es) % 16 != 0 || (ldw * es) % 16 != 0 || (ldy * eo) % 16 != 0) return BIGEMM_ERR_ARG;
   if (128 * ldx * es >= kOffsetLimit || 128 * ldw * es >= kOffsetLimit || 128 * ldy * eo >= kOffsetLimit)
     return BIGEMM_ERR_ARG;
@@ -123,13 +126,13 @@ bigemm_status handle_device_current(const bigemm_s* h) {
 }
 
 // The one fixed kernel of the handle's input family (no split).
-hipError_t launch_unsplit(bigemm::Op op, int64_t M, int64_t N, int64_t K, const void* X, int64_t ldx, const void* W,
-                          int64_t ldw, void* Y, int64_t ldy, const void* XS, int64_t ldxs, const void* WS,
-                          int64_t ldws, hipStream_t stream) {
+hipError_t launch_unsplit(bigemm::Op op, bool wt, int64_t M, int64_t N, int64_t K, const void* X, int64_t ldx,
+                          const void* W, int64_t ldw, void* Y, int64_t ldy, const void* XS, int64_t ldxs,
+                          const void* WS, int64_t ldws, hipStream_t stream) {
   if (op.in == bigemm::kInMx)
     return bigemm::launch_mxfp8(op, X, W, Y, XS, WS, M, N, K, ldx, ldw, ldy, ldxs, ldws, stream);
   if (op.in == bigemm::kInI8) return bigemm::launch_i8(X, W, Y, M, N, K, ldx, ldw, ldy, stream);
-  return bigemm::launch_bf16(op, X, W, Y, M, N, K, ldx, ldw, ldy, stream);
+  return bigemm::launch_bf16(op, wt, X, W, Y, M, N, K, ldx, ldw, ldy, stream);
 }
 
 // ------------------------------------------------------------------ attention
@@ -295,6 +298,13 @@ bigemm_status bigemm_check_args(const bigemm_desc* desc, int64_t M, int64_t N, i
   return check(desc_op(desc), M, N, K, X, ldx, W, ldw, Y, ldy, X_scale, ldxs, W_scale, ldws);
 }
 
+bigemm_status bigemm_check_args_wt(const bigemm_desc* desc, int64_t M, int64_t N, int64_t K,
+                                   const void* X, int64_t ldx, const void* W, int64_t ldw,
+                                   const void* Y, int64_t ldy) {
+  if (!desc) return BIGEMM_ERR_ARG;
+  return check(desc_op(desc), M, N, K, X, ldx, W, ldw, Y, ldy, nullptr, 0, nullptr, 0, true);
+}
+
 bigemm_status bigemm_create(const bigemm_desc* desc, bigemm_t* out) {
   if (!out) return BIGEMM_ERR_ARG;
   *out = nullptr;
@@ -319,7 +329,20 @@ bigemm_status bigemm_create(const bigemm_desc* desc, bigemm_t* out) {
   h->op = op;
   h->device = dev;
   h->k_chunk = 0;
+  h->w_trans = false;
   *out = h;
+  return BIGEMM_OK;
+}
+
+bigemm_status bigemm_create_wt(const bigemm_desc* desc, bigemm_t* out) {
+  if (!out) return BIGEMM_ERR_ARG;
+  *out = nullptr;
+  if (!desc) return BIGEMM_ERR_ARG;
+  const bigemm::Op op = desc_op(desc);
+  if (op.in != bigemm::kInBf16 && op.in != bigemm::kInF16) return BIGEMM_ERR_UNSUPPORTED;
+  const bigemm_status st = bigemm_create(desc, out);
+  if (st != BIGEMM_OK) return st;
+  (*out)->w_trans = true;
   return BIGEMM_OK;
 }
 
@@ -351,15 +374,15 @@ bigemm_status bigemm_run_ws(bigemm_t h, int64_t M, int64_t N, int64_t K, const v
                             int64_t ldxs, const void* W_scale, int64_t ldws, void* workspace,
                             uint64_t workspace_bytes, void* stream) {
   if (!h) return BIGEMM_ERR_ARG;
-  const bigemm_status st = check(h->op, M, N, K, X, ldx, W, ldw, Y, ldy, X_scale, ldxs, W_scale, ldws);
+  const bigemm_status st = check(h->op, M, N, K, X, ldx, W, ldw, Y, ldy, X_scale, ldxs, W_scale, ldws, h->w_trans);
   if (st != BIGEMM_OK || M == 0) return st;
   const bigemm_status dv = handle_device_current(h);
   if (dv != BIGEMM_OK) return dv;
   uint64_t need = 0;
   bigemm_workspace_size(h, M, N, K, &need);
   if (need == 0) {  // unsplit handle, or a single chunk: the one fixed kernel
-    const hipError_t e = launch_unsplit(h->op, M, N, K, X, ldx, W, ldw, Y, ldy, X_scale, ldxs, W_scale, ldws,
-                                        (hipStream_t)stream);
+    const hipError_t e = launch_unsplit(h->op, h->w_trans, M, N, K, X, ldx, W, ldw, Y, ldy, X_scale, ldxs,
+                                        W_scale, ldws, (hipStream_t)stream);
     return e == hipSuccess ? BIGEMM_OK : BIGEMM_ERR_DEVICE;
   }
   if (!workspace || !aligned16(workspace) || workspace_bytes < need) return BIGEMM_ERR_ARG;
@@ -404,12 +427,12 @@ bigemm_status bigemm_run(bigemm_t h, int64_t M, int64_t N, int64_t K, const void
                          int64_t ldxs, const void* W_scale, int64_t ldws, void* stream) {
   if (!h) return BIGEMM_ERR_ARG;
   if (h->k_chunk > 0) return BIGEMM_ERR_ARG;  // a split-K handle needs bigemm_run_ws
-  const bigemm_status st = check(h->op, M, N, K, X, ldx, W, ldw, Y, ldy, X_scale, ldxs, W_scale, ldws);
+  const bigemm_status st = check(h->op, M, N, K, X, ldx, W, ldw, Y, ldy, X_scale, ldxs, W_scale, ldws, h->w_trans);
   if (st != BIGEMM_OK || M == 0) return st;
   const bigemm_status dv = handle_device_current(h);
   if (dv != BIGEMM_OK) return dv;
-  const hipError_t e = launch_unsplit(h->op, M, N, K, X, ldx, W, ldw, Y, ldy, X_scale, ldxs, W_scale, ldws,
-                                      (hipStream_t)stream);
+  const hipError_t e = launch_unsplit(h->op, h->w_trans, M, N, K, X, ldx, W, ldw, Y, ldy, X_scale, ldxs,
+                                      W_scale, ldws, (hipStream_t)stream);
   return e == hipSuccess ? BIGEMM_OK : BIGEMM_ERR_DEVICE;
 }
 

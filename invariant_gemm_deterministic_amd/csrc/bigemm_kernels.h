@@ -18,7 +18,8 @@ struct Op {
   int32_t out;
 };
 
-hipError_t launch_bf16(Op op, const void* X, const void* W, void* Y, int64_t M, int64_t N, int64_t K,
+// wt: W is given as its transpose, [N][ldw] with ldw >= K (bf16 / fp16 only).
+hipError_t launch_bf16(Op op, bool wt, const void* X, const void* W, void* Y, int64_t M, int64_t N, int64_t K,
                        int64_t ldx, int64_t ldw, int64_t ldy, hipStream_t stream);
 
 // Opt-in split-K (bf16 / fp16 inputs): chunk sums of k_chunk K values into P

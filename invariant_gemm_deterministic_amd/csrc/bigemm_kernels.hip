@@ -163,7 +163,12 @@ constexpr int kUnrollBf16 = 8 * kStagesBf16;
 // kSplit: the opt-in split-K variant. The grid is (chunk, tile) pairs; the
 // workgroup runs the same chain over the K blocks of its chunk only
 // (kb_per_split blocks) and stores the fp32 chunk sum at Y + chunk * split_stride.
-template <bool kF16, bool kOutBf16, bool kSplit>
+// kWT: W is given as its transpose, an [N, K] row-major array (the layout of a
+// linear layer's weight), leading dimension ldw >= K. Its tile is then staged
+// like the X tile (128 rows of K-contiguous bytes) and the B fragments are
+// plain 16-byte reads; the MFMA chain and its operands are the same as for
+// W [K, N], so the output bytes are too.
+template <bool kF16, bool kOutBf16, bool kSplit, bool kWT = false>
 __global__ __launch_bounds__(kThreadsBf16, 1)
 void bigemm_bf16_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
                         void* __restrict__ Y, int M, int N, int K,
@@ -215,12 +220,18 @@ void bigemm_bf16_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
     const int r = p >> 3, s = p & 7, c = s ^ swz_x(r);
     xoff[i] = (uint32_t)((r * ldx + c * 8) * 2);
     xk[i] = r < rows_valid ? c * 8 : 0x7FFFFFFF;
-    const int kr = p >> 4, sw = p & 15, cw = sw ^ swz_w16(kr);
-    woff[i] = (uint32_t)((kr * ldw + cw * 8) * 2);
-    wk[i] = cw * 8 < cols_valid ? kr : 0x7FFFFFFF;
+    if constexpr (kWT) {  // W^T tile: 128 columns (rows of W^T) of 128 bytes, swizzled like X
+      woff[i] = (uint32_t)((r * ldw + c * 8) * 2);
+      wk[i] = r < cols_valid ? c * 8 : 0x7FFFFFFF;
+    } else {
+      const int kr = p >> 4, sw = p & 15, cw = sw ^ swz_w16(kr);
+      woff[i] = (uint32_t)((kr * ldw + cw * 8) * 2);
+      wk[i] = cw * 8 < cols_valid ? kr : 0x7FFFFFFF;
+    }
   }
   const uint16_t* Xt = X + (int64_t)row0 * ldx + (int64_t)kb_first * kBkBf16;
-  const uint16_t* Wt = W + col0 + (int64_t)kb_first * kBkBf16 * ldw;
+  const uint16_t* Wt = kWT ? W + (int64_t)col0 * ldw + (int64_t)kb_first * kBkBf16
+                           : W + col0 + (int64_t)kb_first * kBkBf16 * ldw;
   const int Kr = K - kb_first * kBkBf16;           // K remaining from this workgroup's first block
 
   // Issue the 4 LDS-DMA loads of K block kb into `stage`. A block past the
@@ -232,7 +243,7 @@ void bigemm_bf16_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
     const int k0 = live ? kb * kBkBf16 : 0;
     const int kleft = live ? Kr - k0 : 0;
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(Xt + k0);
-    const __amdgpu_buffer_rsrc_t rw = make_rsrc(Wt + (int64_t)k0 * ldw);
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(kWT ? Wt + k0 : Wt + (int64_t)k0 * ldw);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const uint32_t o = xk[i] < kleft ? xoff[i] : kOob;
@@ -251,6 +262,7 @@ void bigemm_bf16_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
   const int wm = wave >> 2, wn = wave & 3;
   int a_addr[2][4];     // [fm][kk]
   int b_addr[4][2];     // [kk][half]
+  int bt_addr[4];       // kWT: [kk], the 16 bytes of the lane's column
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
@@ -258,6 +270,11 @@ void bigemm_bf16_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
       const int r = wm * 64 + f * 32 + (lane & 31);
       const int c = kk * 2 + (lane >> 5);
       a_addr[f][kk] = r * 128 + ((c ^ swz_x(r)) << 4);
+    }
+    if constexpr (kWT) {
+      const int n = wn * 32 + (lane & 31);
+      const int c = kk * 2 + (lane >> 5);
+      bt_addr[kk] = kTileBytes + n * 128 + ((c ^ swz_x(n)) << 4);
     }
     const int g = lane >> 4, j = lane & 15;
     const int col = wn * 32 + (g & 1) * 16 + (j & 3) * 4;
@@ -282,10 +299,15 @@ void bigemm_bf16_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
       i32x4 a[2];
 #pragma unroll
       for (int f = 0; f < 2; ++f) a[f] = *LDS(const i32x4, st + a_addr[f][kk]);
-      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS(i16x4, st + b_addr[kk][0]));
-      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS(i16x4, st + b_addr[kk][1]));
-      const i32x2 lo2 = __builtin_bit_cast(i32x2, lo), hi2 = __builtin_bit_cast(i32x2, hi);
-      const i32x4 b = {lo2[0], lo2[1], hi2[0], hi2[1]};
+      i32x4 b;
+      if constexpr (kWT) {
+        b = *LDS(const i32x4, st + bt_addr[kk]);
+      } else {
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS(i16x4, st + b_addr[kk][0]));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS(i16x4, st + b_addr[kk][1]));
+        const i32x2 lo2 = __builtin_bit_cast(i32x2, lo), hi2 = __builtin_bit_cast(i32x2, hi);
+        b = i32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
+      }
 #pragma unroll
       for (int f = 0; f < 2; ++f) acc[f] = mfma_16bit<kF16>(a[f], b, acc[f]);
     }
@@ -845,13 +867,15 @@ void bigemm_split_merge_kernel(const float* __restrict__ P, void* __restrict__ Y
 
 // ------------------------------------------------------------------ launchers
 
-hipError_t launch_bf16(Op op, const void* X, const void* W, void* Y, int64_t M, int64_t N, int64_t K,
+hipError_t launch_bf16(Op op, bool wt, const void* X, const void* W, void* Y, int64_t M, int64_t N, int64_t K,
                        int64_t ldx, int64_t ldw, int64_t ldy, hipStream_t stream) {
   const int tiles_m = (int)((M + 127) / 128);
   const int tiles_n = (int)((N + 127) / 128);
   const bool f16 = op.in == kInF16, obf = op.out == 1 /* BIGEMM_BF16 */;
-  auto kern = f16 ? (obf ? bigemm_bf16_kernel<true, true, false> : bigemm_bf16_kernel<true, false, false>)
-                  : (obf ? bigemm_bf16_kernel<false, true, false> : bigemm_bf16_kernel<false, false, false>);
+  auto kern = wt ? (f16 ? (obf ? bigemm_bf16_kernel<true, true, false, true> : bigemm_bf16_kernel<true, false, false, true>)
+                        : (obf ? bigemm_bf16_kernel<false, true, false, true> : bigemm_bf16_kernel<false, false, false, true>))
+                 : (f16 ? (obf ? bigemm_bf16_kernel<true, true, false> : bigemm_bf16_kernel<true, false, false>)
+                        : (obf ? bigemm_bf16_kernel<false, true, false> : bigemm_bf16_kernel<false, false, false>));
   hipLaunchKernelGGL(kern, dim3(tiles_m * tiles_n), dim3(kThreadsBf16), 0, stream, (const uint16_t*)X,
                      (const uint16_t*)W, Y, (int)M, (int)N, (int)K, ldx, ldw, ldy, tiles_m, tiles_n, 0, (int64_t)0);
   return hipGetLastError();

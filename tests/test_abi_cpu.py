@@ -25,7 +25,8 @@ def test_header_declares_the_boundary():
                  "bigemm_get_config", "bigemm_check_args", "bigemm_abi_version",
                  "bigemm_create_split_k", "bigemm_workspace_size", "bigemm_run_ws",
                  "bigemm_rmsnorm", "bigemm_rmsnorm_check_args", "bigemm_kv_cache_write",
-                 "bigemm_attn_workspace_size", "bigemm_paged_attention", "bigemm_paged_attention_check_args"):
+                 "bigemm_attn_workspace_size", "bigemm_paged_attention", "bigemm_paged_attention_check_args",
+                 "bigemm_create_wt", "bigemm_check_args_wt"):
         assert name in fns
 
 
@@ -36,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert bg.bigemm_abi_version() == 5
+    assert bg.bigemm_abi_version() == 6
     for s in range(5):
         assert bg.bigemm_status_str(s)
     assert "unknown" in bg.bigemm_status_str(99)
@@ -49,6 +50,10 @@ def test_null_handle_paths():
     assert lib.bigemm_get_config(None, None, None, None) == bg.BIGEMM_ERR_ARG
     assert lib.bigemm_create(None, None) == bg.BIGEMM_ERR_ARG
     assert lib.bigemm_create_split_k(None, 512, None) == bg.BIGEMM_ERR_ARG
+    assert lib.bigemm_create_wt(None, None) == bg.BIGEMM_ERR_ARG
+    h = ctypes.c_void_p(1)
+    assert lib.bigemm_create_wt(None, ctypes.byref(h)) == bg.BIGEMM_ERR_ARG and h.value is None
+    assert lib.bigemm_check_args_wt(None, 1, 8, 8, A, 8, A, 8, A, 8) == bg.BIGEMM_ERR_ARG
     assert bg.bigemm_run_ws(0, 1, 8, 8, A, 8, A, 8, A, 8, check=False) == bg.BIGEMM_ERR_ARG
     n = ctypes.c_uint64()
     assert lib.bigemm_workspace_size(None, 1, 8, 8, ctypes.byref(n)) == bg.BIGEMM_ERR_ARG
@@ -127,6 +132,34 @@ def test_check_args_other_types():
     assert chk(I8, 16, 40, 64) == bg.BIGEMM_ERR_ARG
     assert chk(I8, 16, 64, 64, ldy=66) == bg.BIGEMM_ERR_ARG
     assert chk(I8, 16, 64, 64, XS=A, ldxs=2) == bg.BIGEMM_ERR_ARG
+
+
+def chk_wt(desc, M, N, K, X=A, ldx=None, W=A, ldw=None, Y=A, ldy=None):
+    return bg.bigemm_check_args_wt(desc[0], desc[1], desc[2], M, N, K, X, K if ldx is None else ldx,
+                                   W, K if ldw is None else ldw, Y, N if ldy is None else ldy)
+
+
+def test_check_args_w_transposed():
+    # W is [N, K]: its leading dimension is checked against K, not N
+    assert chk_wt(BF, 4096, 4096, 4096) == bg.BIGEMM_OK
+    assert chk_wt(BF, 16, 64, 256) == bg.BIGEMM_OK                       # ldw = K
+    assert chk(BF, 16, 512, 256, ldw=256) == bg.BIGEMM_ERR_ARG          # the same ldw is short for [K, N]
+    assert chk_wt(BF, 16, 512, 256, ldw=256) == bg.BIGEMM_OK
+    assert chk_wt(BF, 16, 64, 256, ldw=64) == bg.BIGEMM_ERR_ARG          # ldw < K
+    assert chk_wt(BF, 16, 64, 256, ldw=264) == bg.BIGEMM_OK              # padded rows
+    assert chk_wt(BF, 16, 64, 256, ldw=260) == bg.BIGEMM_ERR_ARG         # rows not 16-byte aligned
+    assert chk_wt(BF, 16, 64, 256, ldw=(1 << 23) - 8) == bg.BIGEMM_OK    # 128 * ldw * 2 just below 2^31
+    assert chk_wt(BF, 16, 64, 256, ldw=1 << 23) == bg.BIGEMM_ERR_ARG
+    assert chk_wt(BF, 16, 64, 12) == bg.BIGEMM_ERR_ARG                   # K % 8
+    assert chk_wt(BF, 16, 12, 64) == bg.BIGEMM_ERR_ARG                   # N % 8
+    assert chk_wt(BF, 16, 64, 64, W=A + 2) == bg.BIGEMM_ERR_ARG
+    assert chk_wt(BF, 0, 64, 64, X=0, W=0, Y=0) == bg.BIGEMM_OK
+    assert chk_wt(F16, 16, 64, 64) == bg.BIGEMM_OK
+    assert chk_wt(BF_OUT_BF, 16, 64, 64) == bg.BIGEMM_OK
+    # bf16 and fp16 only
+    assert chk_wt(MX, 16, 64, 128) == bg.BIGEMM_ERR_UNSUPPORTED
+    assert chk_wt(I8, 16, 64, 64) == bg.BIGEMM_ERR_UNSUPPORTED
+    assert chk_wt((bg.BIGEMM_BF16, bg.BIGEMM_F16, bg.BIGEMM_F32, 0), 4, 64, 64) == bg.BIGEMM_ERR_UNSUPPORTED
 
 
 def test_rmsnorm_check_args():
