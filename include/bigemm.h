@@ -167,30 +167,35 @@ BIGEMM_API bigemm_status bigemm_run(bigemm_t h, int64_t M, int64_t N, int64_t K,
 BIGEMM_API bigemm_status bigemm_create_split_k(const bigemm_desc* desc, int32_t k_chunk, bigemm_t* out);
 
 /*
- * Handle for bf16 or fp16 inputs whose W is given as its transpose: an
- * [N, K] row-major array with leading dimension ldw >= K (the layout in
- * which a linear layer keeps its weight), so such a weight needs no copy.
- * It is the same multiply, Y = X * W with W[k, j] read from element
- * [j, k] of that array, and the same fixed recipe as bigemm_run (one tile
- * configuration, whole K in one workgroup, ascending K blocks, one MFMA
- * shape): the MFMA chain sees the same operands in the same order, so Y has
- * exactly the bytes of a bigemm_create handle given the same logical W as
- * [K, N]. Only the staging of W's tile differs.
- * Run it with bigemm_run or bigemm_run_ws (no workspace); the requirements of
- * bigemm_run hold with ldw >= K in place of ldw >= N (still: every row of the
- * array 16-byte aligned and 128 * ldw * 2 below 2^31). MXFP8 and int8
- * descriptors return BIGEMM_ERR_UNSUPPORTED, as do devices other than gfx950;
- * there is no split-K form. *out is NULL on failure.
+ * Handle whose W is given as its transpose: an [N, K] row-major array with
+ * leading dimension ldw >= K (the layout in which a linear layer keeps its
+ * weight), so such a weight needs no copy. For MXFP8, W_scale is then
+ * [N, K/32] with ldws >= K/32 (W's E8M0 scales next to its rows, as X_scale
+ * is for X). Every descriptor of bigemm_create is accepted.
+ * It is the same multiply, Y = X * W with W[k, j] read from element [j, k]
+ * of that array (and its scale from W_scale[j, k/32]), under the same fixed
+ * recipe as bigemm_run: one tile configuration, the whole K in one
+ * workgroup, ascending K blocks, one MFMA shape. The MFMA chain sees the
+ * same operands and scales in the same order, so Y has exactly the bytes of
+ * a bigemm_create handle given the same logical W as [K, N]. Only the staging
+ * of W's tile and scales differs.
+ * Run it with bigemm_run or bigemm_run_ws (no workspace). The requirements of
+ * bigemm_run hold with ldw >= K in place of ldw >= N and, for MXFP8,
+ * ldws >= K/32 in place of ldws >= N and 128 * ldws below 2^31. Devices other
+ * than gfx950 return BIGEMM_ERR_UNSUPPORTED; there is no split-K form.
+ * *out is NULL on failure.
  */
 BIGEMM_API bigemm_status bigemm_create_wt(const bigemm_desc* desc, bigemm_t* out);
 
 /*
  * The argument checks of a bigemm_create_wt handle's bigemm_run, as a pure
- * host function (no HIP call): W [N, K] with ldw >= K; no scale arrays.
+ * host function (no HIP call): W [N, K] with ldw >= K, MXFP8 W_scale
+ * [N, K/32] with ldws >= K/32; otherwise as bigemm_check_args.
  */
 BIGEMM_API bigemm_status bigemm_check_args_wt(const bigemm_desc* desc, int64_t M, int64_t N, int64_t K,
                                    const void* X, int64_t ldx, const void* W, int64_t ldw,
-                                   const void* Y, int64_t ldy);
+                                   const void* Y, int64_t ldy, const void* X_scale, int64_t ldxs,
+                                   const void* W_scale, int64_t ldws);
 
 /*
  * Device workspace, in bytes, that bigemm_run_ws needs for this shape:

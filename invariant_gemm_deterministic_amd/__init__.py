@@ -93,7 +93,8 @@ def load():
         lib.bigemm_create_wt.restype = ctypes.c_int
         lib.bigemm_create_wt.argtypes = [ctypes.POINTER(bigemm_desc), ctypes.POINTER(vp)]
         lib.bigemm_check_args_wt.restype = ctypes.c_int
-        lib.bigemm_check_args_wt.argtypes = [ctypes.POINTER(bigemm_desc), i64, i64, i64, vp, i64, vp, i64, vp, i64]
+        lib.bigemm_check_args_wt.argtypes = [ctypes.POINTER(bigemm_desc), i64, i64, i64, vp, i64, vp, i64,
+                                             vp, i64, vp, i64, vp, i64]
         lib.bigemm_abi_version.restype = i32
         lib.bigemm_abi_version.argtypes = []
         lib.bigemm_rmsnorm.restype = ctypes.c_int
@@ -161,10 +162,10 @@ def bigemm_create_split_k(x_type: int, w_type: int, y_type: int, k_chunk: int) -
     return int(h.value)
 
 
-def bigemm_create_wt(x_type: int, w_type: int, y_type: int = BIGEMM_F32) -> int:
-    """Create a handle whose W is given as [N, K] (bf16 / fp16 inputs). Raises BigemmError."""
+def bigemm_create_wt(x_type: int, w_type: int, y_type: int = BIGEMM_F32, scale_block: int = 0) -> int:
+    """Create a handle whose W is given as [N, K] (MXFP8: W_scale [N, K/32]). Raises BigemmError."""
     h = ctypes.c_void_p()
-    d = _desc(x_type, w_type, y_type, 0)
+    d = _desc(x_type, w_type, y_type, scale_block)
     st = load().bigemm_create_wt(ctypes.byref(d), ctypes.byref(h))
     if st != BIGEMM_OK:
         raise BigemmError(st, "bigemm_create_wt")
@@ -226,12 +227,13 @@ def bigemm_check_args(x_type: int, w_type: int, y_type: int, scale_block: int, M
                                         Y or None, ldy, X_scale or None, ldxs, W_scale or None, ldws))
 
 
-def bigemm_check_args_wt(x_type: int, w_type: int, y_type: int, M: int, N: int, K: int,
-                         X: int, ldx: int, W: int, ldw: int, Y: int, ldy: int) -> int:
+def bigemm_check_args_wt(x_type: int, w_type: int, y_type: int, scale_block: int, M: int, N: int, K: int,
+                         X: int, ldx: int, W: int, ldw: int, Y: int, ldy: int,
+                         X_scale: int = 0, ldxs: int = 0, W_scale: int = 0, ldws: int = 0) -> int:
     """Argument validation of a bigemm_create_wt handle (W [N, K], ldw >= K); returns the status code."""
-    d = _desc(x_type, w_type, y_type, 0)
+    d = _desc(x_type, w_type, y_type, scale_block)
     return int(load().bigemm_check_args_wt(ctypes.byref(d), M, N, K, X or None, ldx, W or None, ldw,
-                                           Y or None, ldy))
+                                           Y or None, ldy, X_scale or None, ldxs, W_scale or None, ldws))
 
 
 # ------------------------------------------------------------------ torch wrapper
@@ -254,7 +256,7 @@ def _handle(kind: str, device_index: int, y_type: int = BIGEMM_F32, k_chunk: int
             if k_chunk:
                 h = bigemm_create_split_k(t, t, y_type, k_chunk)
             elif wt:
-                h = bigemm_create_wt(t, t, y_type)
+                h = bigemm_create_wt(t, t, y_type, sb)
             else:
                 h = bigemm_create(t, t, y_type, sb)
         _handles[key] = h
@@ -275,10 +277,11 @@ def mm(x, w, x_scale=None, w_scale=None, out=None, stream=None, out_dtype=None, 
     MXFP8: ``x``/``w`` are torch.float8_e4m3fn (or uint8 codes) and
     ``x_scale`` [M, K/32], ``w_scale`` [K/32, N] are uint8 E8M0 bytes. Rows
     must be contiguous; the leading dimension is taken from ``stride(0)``.
-    For bf16 and fp16, ``w`` may instead be the transpose of an [N, K] array
-    with contiguous rows (``weight.t()`` of a linear layer's weight, so
-    ``stride(0) == 1``): it then runs through the W-transposed handle with no
-    copy, and the output bytes are those of the [K, N] layout.
+    ``w`` may instead be the transpose of an [N, K] array with contiguous rows
+    (``weight.t()`` of a linear layer's weight, so ``stride(0) == 1``): it then
+    runs through the W-transposed handle with no copy, and the output bytes are
+    those of the [K, N] layout. For MXFP8, ``w_scale`` must then be the
+    transpose of an [N, K/32] array likewise.
     Output: ``out`` if given (its dtype selects the output type), else a new
     [M, N] tensor of ``out_dtype`` (float32 or bfloat16 for floating inputs,
     default float32; int32 for int8).
@@ -332,8 +335,8 @@ def mm(x, w, x_scale=None, w_scale=None, out=None, stream=None, out_dtype=None, 
         stream = torch.cuda.current_stream(x.device).cuda_stream
     # The handle belongs to x's device, and the library runs a handle only on its own device.
     with torch.cuda.device(dev):
-        if wt and (k_chunk or kind not in ("bf16", "f16")):
-            raise ValueError("a transposed w ([N, K] rows) is taken for bf16 and fp16 without split-K")
+        if wt and k_chunk:
+            raise ValueError("split-K takes w as [K, N] with contiguous rows")
         if k_chunk:
             if kind not in ("bf16", "f16"):
                 raise ValueError("split-K is provided for bf16 and fp16 inputs")
@@ -346,14 +349,18 @@ def mm(x, w, x_scale=None, w_scale=None, out=None, stream=None, out_dtype=None, 
                           0, 0, 0, 0, workspace.data_ptr(), ws_bytes, stream)
             return out
         h = _handle(kind, dev, ytypes[out_dtype], 0, wt)  # raises BigemmError for a combination not provided
+        ldw = _ld(w.t()) if wt else _ld(w)
         if mx:
-            for t in (x_scale, w_scale):
+            if tuple(x_scale.shape) != (M, K // 32) or tuple(w_scale.shape) != (K // 32, N):
+                raise ValueError(f"scales must be [M, K/32] and [K/32, N] = [{M}, {K // 32}] and [{K // 32}, {N}]")
+            ws = w_scale.t() if wt else w_scale   # rows: [N, K/32] for W^T, else [K/32, N]
+            for t in (x_scale, ws):
                 if not t.is_cuda or t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
-                    raise ValueError("scales must be 2-D CUDA tensors with contiguous rows")
-            bigemm_run(h, M, N, K, x.data_ptr(), _ld(x), w.data_ptr(), _ld(w), out.data_ptr(), _ld(out),
-                       x_scale.data_ptr(), _ld(x_scale), w_scale.data_ptr(), _ld(w_scale), stream)
+                    raise ValueError("scales must be 2-D CUDA tensors with contiguous rows "
+                                     "(w_scale in the same layout as w)")
+            bigemm_run(h, M, N, K, x.data_ptr(), _ld(x), w.data_ptr(), ldw, out.data_ptr(), _ld(out),
+                       x_scale.data_ptr(), _ld(x_scale), w_scale.data_ptr(), _ld(ws), stream)
         else:
-            ldw = _ld(w.t()) if wt else _ld(w)
             bigemm_run(h, M, N, K, x.data_ptr(), _ld(x), w.data_ptr(), ldw, out.data_ptr(), _ld(out),
                        0, 0, 0, 0, stream)
     return out

@@ -46,12 +46,12 @@ bigemm::Op desc_op(const bigemm_desc* d) {
   return op;
 }
 
-// wt: W is [N, K] with ldw >= K (bf16 / fp16 only) instead of [K, N] with ldw >= N.
+// wt: W is [N, K] with ldw >= K (and for MXFP8 W_scale [N, K/32] with
+// ldws >= K/32) instead of [K, N] with ldw >= N (W_scale [K/32, N], ldws >= N).
 bigemm_status check(bigemm::Op op, int64_t M, int64_t N, int64_t K, const void* X, int64_t ldx,
                     const void* W, int64_t ldw, const void* Y, int64_t ldy, const void* XS,
                     int64_t ldxs, const void* WS, int64_t ldws, bool wt = false) {
   if (op.in == 0) return BIGEMM_ERR_UNSUPPORTED;
-  if (wt && op.in != bigemm::kInBf16 && op.in != bigemm::kInF16) return BIGEMM_ERR_UNSUPPORTED;
   if (M < 0 || N < 1 || K < 1) return BIGEMM_ERR_ARG;
   if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return BIGEMM_ERR_ARG;
   if (((M + 127) / 128) * ((N + 127) / 128) > INT32_MAX) return BIGEMM_ERR_ARG;  // grid size
@@ -68,8 +68,8 @@ bigemm_status check(bigemm::Op op, int64_t M, int64_t N, int64_t K, const void* 
   if (!mx) {
     if (XS != nullptr || WS != nullptr) return BIGEMM_ERR_ARG;
   } else {
-    if (ldxs < K / 32 || ldws < N) return BIGEMM_ERR_ARG;
-    if (128 * ldxs >= kOffsetLimit || (K / 32) * ldws >= kOffsetLimit) return BIGEMM_ERR_ARG;
+    if (ldxs < K / 32 || ldws < (wt ? K / 32 : N)) return BIGEMM_ERR_ARG;
+    if (128 * ldxs >= kOffsetLimit || (wt ? 128 : K / 32) * ldws >= kOffsetLimit) return BIGEMM_ERR_ARG;
   }
   if (M == 0) return BIGEMM_OK;
   if (!X || !W || !Y) return BIGEMM_ERR_ARG;
@@ -130,8 +130,8 @@ hipError_t launch_unsplit(bigemm::Op op, bool wt, int64_t M, int64_t N, int64_t 
                           const void* W, int64_t ldw, void* Y, int64_t ldy, const void* XS, int64_t ldxs,
                           const void* WS, int64_t ldws, hipStream_t stream) {
   if (op.in == bigemm::kInMx)
-    return bigemm::launch_mxfp8(op, X, W, Y, XS, WS, M, N, K, ldx, ldw, ldy, ldxs, ldws, stream);
-  if (op.in == bigemm::kInI8) return bigemm::launch_i8(X, W, Y, M, N, K, ldx, ldw, ldy, stream);
+    return bigemm::launch_mxfp8(op, wt, X, W, Y, XS, WS, M, N, K, ldx, ldw, ldy, ldxs, ldws, stream);
+  if (op.in == bigemm::kInI8) return bigemm::launch_i8(wt, X, W, Y, M, N, K, ldx, ldw, ldy, stream);
   return bigemm::launch_bf16(op, wt, X, W, Y, M, N, K, ldx, ldw, ldy, stream);
 }
 
@@ -300,9 +300,10 @@ bigemm_status bigemm_check_args(const bigemm_desc* desc, int64_t M, int64_t N, i
 
 bigemm_status bigemm_check_args_wt(const bigemm_desc* desc, int64_t M, int64_t N, int64_t K,
                                    const void* X, int64_t ldx, const void* W, int64_t ldw,
-                                   const void* Y, int64_t ldy) {
+                                   const void* Y, int64_t ldy, const void* X_scale, int64_t ldxs,
+                                   const void* W_scale, int64_t ldws) {
   if (!desc) return BIGEMM_ERR_ARG;
-  return check(desc_op(desc), M, N, K, X, ldx, W, ldw, Y, ldy, nullptr, 0, nullptr, 0, true);
+  return check(desc_op(desc), M, N, K, X, ldx, W, ldw, Y, ldy, X_scale, ldxs, W_scale, ldws, true);
 }
 
 bigemm_status bigemm_create(const bigemm_desc* desc, bigemm_t* out) {
@@ -338,8 +339,6 @@ bigemm_status bigemm_create_wt(const bigemm_desc* desc, bigemm_t* out) {
   if (!out) return BIGEMM_ERR_ARG;
   *out = nullptr;
   if (!desc) return BIGEMM_ERR_ARG;
-  const bigemm::Op op = desc_op(desc);
-  if (op.in != bigemm::kInBf16 && op.in != bigemm::kInF16) return BIGEMM_ERR_UNSUPPORTED;
   const bigemm_status st = bigemm_create(desc, out);
   if (st != BIGEMM_OK) return st;
   (*out)->w_trans = true;

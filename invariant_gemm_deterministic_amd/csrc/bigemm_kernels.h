@@ -18,7 +18,8 @@ struct Op {
   int32_t out;
 };
 
-// wt: W is given as its transpose, [N][ldw] with ldw >= K (bf16 / fp16 only).
+// wt (every launcher): W is given as its transpose, [N][ldw] with ldw >= K,
+// and for MXFP8 W_scale as [N][ldws] with ldws >= K/32.
 hipError_t launch_bf16(Op op, bool wt, const void* X, const void* W, void* Y, int64_t M, int64_t N, int64_t K,
                        int64_t ldx, int64_t ldw, int64_t ldy, hipStream_t stream);
 
@@ -27,11 +28,11 @@ hipError_t launch_bf16(Op op, bool wt, const void* X, const void* W, void* Y, in
 hipError_t launch_bf16_split(Op op, int32_t k_chunk, const void* X, const void* W, void* Y, void* P, int64_t M,
                              int64_t N, int64_t K, int64_t ldx, int64_t ldw, int64_t ldy, hipStream_t stream);
 
-hipError_t launch_mxfp8(Op op, const void* X, const void* W, void* Y, const void* XS, const void* WS,
+hipError_t launch_mxfp8(Op op, bool wt, const void* X, const void* W, void* Y, const void* XS, const void* WS,
                         int64_t M, int64_t N, int64_t K, int64_t ldx, int64_t ldw, int64_t ldy,
                         int64_t ldxs, int64_t ldws, hipStream_t stream);
 
-hipError_t launch_i8(const void* X, const void* W, void* Y, int64_t M, int64_t N, int64_t K,
+hipError_t launch_i8(bool wt, const void* X, const void* W, void* Y, int64_t M, int64_t N, int64_t K,
                      int64_t ldx, int64_t ldw, int64_t ldy, hipStream_t stream);
 
 }  // namespace bigemm

@@ -26,7 +26,9 @@
 // per K block. Operand
 // fragments come from LDS with ds_read_b128 (row operand, K contiguous) and
 // the transposing ds_read_b64_tr_b16 / ds_read_b64_tr_b8 (the W operand, which
-// is N-contiguous in memory). Both LDS tiles are XOR-swizzled at 16-byte
+// is N-contiguous in memory). When W is given as [N, K] rows (each kernel's
+// kWT flag) its tile is K-contiguous like X's and its fragments are
+// ds_read_b128 as well. Both LDS tiles are XOR-swizzled at 16-byte
 // granularity so the fragment reads do not collide on LDS banks.
 //
 // Lane layouts used below (checked with exact small-integer products on the
@@ -381,7 +383,11 @@ constexpr int kScaleBufBytes = 128 * 4 * kScaleGroup;  // one operand's scales o
 constexpr int kStagesMx = BIGEMM_MX_STAGES;
 static_assert(kStagesMx >= 3 && kStagesMx <= 4, "LDS holds 3 or 4 stages of 32 KiB");
 
-template <bool kStaged, bool kOutBf16>
+// kWT: W is given as its transpose, [N, K] rows with leading dimension
+// ldw >= K, and W_scale as [N, K/32] with ldws >= K/32 (the layout X and
+// X_scale have). W's tile, fragments and scales are then handled exactly like
+// X's; the MFMA operands and scales are the same as for W [K, N].
+template <bool kStaged, bool kOutBf16, bool kWT = false>
 __global__ __launch_bounds__(kThreads, 1)
 void bigemm_mxfp8_kernel(const uint8_t* __restrict__ X, const uint8_t* __restrict__ W,
                          void* __restrict__ Y, const uint8_t* __restrict__ XS,
@@ -421,19 +427,24 @@ void bigemm_mxfp8_kernel(const uint8_t* __restrict__ X, const uint8_t* __restric
     const int r = p >> 3, s = p & 7, c = s ^ swz_x(r);
     xoff[i] = (uint32_t)(r * ldx + c * 16);
     xk[i] = r < rows_valid ? c * 16 : 0x7FFFFFFF;
-    const int kr = p >> 3, cw = s ^ swz_w8(kr);
-    woff[i] = (uint32_t)(kr * ldw + cw * 16);
-    wk[i] = cw * 16 < cols_valid ? kr : 0x7FFFFFFF;
+    if constexpr (kWT) {  // W^T tile: rows of W^T (output columns), swizzled like X
+      woff[i] = (uint32_t)(r * ldw + c * 16);
+      wk[i] = r < cols_valid ? c * 16 : 0x7FFFFFFF;
+    } else {
+      const int kr = p >> 3, cw = s ^ swz_w8(kr);
+      woff[i] = (uint32_t)(kr * ldw + cw * 16);
+      wk[i] = cw * 16 < cols_valid ? kr : 0x7FFFFFFF;
+    }
   }
   const uint8_t* Xt = X + (int64_t)row0 * ldx;
-  const uint8_t* Wt = W + col0;
+  const uint8_t* Wt = kWT ? W + (int64_t)col0 * ldw : W + col0;
 
   auto issue = [&](int kb, uint8_t* stage) {
     const bool live = kb < nkb;
     const int k0 = live ? kb * kBkMx : 0;
     const int kleft = live ? K - k0 : 0;
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(Xt + k0);
-    const __amdgpu_buffer_rsrc_t rw = make_rsrc(Wt + (int64_t)k0 * ldw);
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(kWT ? Wt + k0 : Wt + (int64_t)k0 * ldw);
     uint8_t* sx = stage;
     uint8_t* sw = stage + kTileBytes;
 #pragma unroll
@@ -452,8 +463,10 @@ void bigemm_mxfp8_kernel(const uint8_t* __restrict__ X, const uint8_t* __restric
   const int g = lane >> 5;   // which 16-wide K quarter of a 64-wide MFMA step this lane holds
   // A fragment: two 16-byte reads per (fm, kk): k = kk*64 + g*16 and kk*64 + 32 + g*16
   int a_addr[2][2][2];   // [fm][kk][half]
-  // B fragment: four 8-byte transposing reads per (fn, kk)
+  // B fragment: four 8-byte transposing reads per (fn, kk); for W^T two
+  // 16-byte reads addressed like A's (bt_addr)
   int b_addr[2][2][4];   // [fn][kk][read]
+  int bt_addr[2][2][2];  // [fn][kk][half]
 #pragma unroll
   for (int f = 0; f < 2; ++f) {
 #pragma unroll
@@ -463,6 +476,14 @@ void bigemm_mxfp8_kernel(const uint8_t* __restrict__ X, const uint8_t* __restric
       for (int h = 0; h < 2; ++h) {
         const int c = kk * 4 + h * 2 + g;
         a_addr[f][kk][h] = r * 128 + ((c ^ swz_x(r)) << 4);
+      }
+      if constexpr (kWT) {
+        const int n = wn * 64 + f * 32 + (lane & 31);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int c = kk * 4 + h * 2 + g;
+          bt_addr[f][kk][h] = kTileBytes + n * 128 + ((c ^ swz_x(n)) << 4);
+        }
       }
       const int G = lane >> 4, j = lane & 15;
       const int col = wn * 64 + f * 32 + (G & 1) * 16 + (j & 1) * 8;
@@ -478,7 +499,7 @@ void bigemm_mxfp8_kernel(const uint8_t* __restrict__ X, const uint8_t* __restric
   // kb*4 + kk*2 + g. Out-of-range rows, columns or K blocks read as 0 (2^-127,
   // multiplying zero data).
   const __amdgpu_buffer_rsrc_t rxs = make_rsrc(XS + (int64_t)row0 * ldxs);
-  const __amdgpu_buffer_rsrc_t rws = make_rsrc(WS + col0);
+  const __amdgpu_buffer_rsrc_t rws = make_rsrc(kWT ? WS + (int64_t)col0 * ldws : WS + col0);
   // xs_base/ws_base: the lane's offset for K block 0; xs_lim/ws_lim: the
   // number of K blocks it may read (0 for rows/columns outside the matrix).
   uint32_t xs_base[2], ws_base[2];
@@ -489,7 +510,7 @@ void bigemm_mxfp8_kernel(const uint8_t* __restrict__ X, const uint8_t* __restric
     xs_base[f] = (uint32_t)(r * ldxs);
     xs_lim[f] = r < rows_valid ? nsb : 0;
     const int c = wn * 64 + f * 32 + (lane & 31);
-    ws_base[f] = (uint32_t)c;
+    ws_base[f] = kWT ? (uint32_t)(c * ldws) : (uint32_t)c;
     ws_lim[f] = c < cols_valid ? nsb : 0;
   }
 
@@ -508,7 +529,7 @@ void bigemm_mxfp8_kernel(const uint8_t* __restrict__ X, const uint8_t* __restric
       const int blk = kb * 4 + kk * 2 + g;
 #pragma unroll
       for (int f = 0; f < 2; ++f) {
-        const uint32_t ob = blk < ws_lim[f] ? ws_base[f] + (uint32_t)(blk * ldws) : kOob;
+        const uint32_t ob = blk < ws_lim[f] ? ws_base[f] + (uint32_t)(kWT ? blk : blk * ldws) : kOob;
         sb[f][kk] = __builtin_amdgcn_raw_buffer_load_b8(rws, ob, 0, 0);
       }
     }
@@ -542,8 +563,14 @@ void bigemm_mxfp8_kernel(const uint8_t* __restrict__ X, const uint8_t* __restric
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rxs, LDS(void, buf + j * 1024), 16, ox, 0, 0, 0);
       } else {
         const int p = (j - kXLoads) * 64 + lane;
-        const int kr = q * 4 * kScaleGroup + (p >> 3), cw = (p & 7) * 16;
-        const uint32_t ow = (kr < nsb && cw < cols_valid) ? (uint32_t)(kr * ldws + cw) : kOob;
+        uint32_t ow;
+        if constexpr (kWT) {  // W^T scales: laid out like the X part
+          const int n = p / (kScaleGroup / 4), cx = q * 4 * kScaleGroup + (p % (kScaleGroup / 4)) * 16;
+          ow = (n < cols_valid && cx < nsb) ? (uint32_t)(n * ldws + cx) : kOob;
+        } else {
+          const int kr = q * 4 * kScaleGroup + (p >> 3), cw = (p & 7) * 16;
+          ow = (kr < nsb && cw < cols_valid) ? (uint32_t)(kr * ldws + cw) : kOob;
+        }
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rws, LDS(void, buf + kScaleBufBytes + (j - kXLoads) * 1024), 16, ow,
                                                  0, 0, 0);
       }
@@ -558,10 +585,15 @@ void bigemm_mxfp8_kernel(const uint8_t* __restrict__ X, const uint8_t* __restric
       const int r = wm * 64 + f * 32 + (lane & 31);
       const int d = *LDS(const int, buf + r * 4 * kScaleGroup + b * 4);
       const int c = wn * 64 + f * 32 + (lane & 31);
+      int dw = 0;
+      if constexpr (kWT) dw = *LDS(const int, buf + kScaleBufBytes + c * 4 * kScaleGroup + b * 4);
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         sa_[f][kk] = (d >> (8 * (kk * 2 + g))) & 0xFF;
-        sb_[f][kk] = *LDS(const uint8_t, buf + kScaleBufBytes + (b * 4 + kk * 2 + g) * 128 + c);
+        if constexpr (kWT)
+          sb_[f][kk] = (dw >> (8 * (kk * 2 + g))) & 0xFF;
+        else
+          sb_[f][kk] = *LDS(const uint8_t, buf + kScaleBufBytes + (b * 4 + kk * 2 + g) * 128 + c);
       }
     }
   };
@@ -608,11 +640,17 @@ void bigemm_mxfp8_kernel(const uint8_t* __restrict__ X, const uint8_t* __restric
         const i32x4 a0 = *LDS(const i32x4, st + a_addr[f][kk][0]);
         const i32x4 a1 = *LDS(const i32x4, st + a_addr[f][kk][1]);
         a[f] = i32x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-        i32x2 bv[4];
+        if constexpr (kWT) {
+          const i32x4 b0 = *LDS(const i32x4, st + bt_addr[f][kk][0]);
+          const i32x4 b1 = *LDS(const i32x4, st + bt_addr[f][kk][1]);
+          b[f] = i32x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+        } else {
+          i32x2 bv[4];
 #pragma unroll
-        for (int rd = 0; rd < 4; ++rd)
-          bv[rd] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(LDS(i32x2, st + b_addr[f][kk][rd]));
-        b[f] = i32x8{bv[0][0], bv[0][1], bv[1][0], bv[1][1], bv[2][0], bv[2][1], bv[3][0], bv[3][1]};
+          for (int rd = 0; rd < 4; ++rd)
+            bv[rd] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(LDS(i32x2, st + b_addr[f][kk][rd]));
+          b[f] = i32x8{bv[0][0], bv[0][1], bv[1][0], bv[1][1], bv[2][0], bv[2][1], bv[3][0], bv[3][1]};
+        }
       }
 #pragma unroll
       for (int fm = 0; fm < 2; ++fm)
@@ -689,6 +727,9 @@ typedef int i32x16 __attribute__((ext_vector_type(16)));
 constexpr int kBkI8 = 128;
 constexpr int kStagesI8 = 3;
 
+// kWT: W given as [N, K] rows (ldw >= K); its tile and fragments are then
+// handled like X's.
+template <bool kWT = false>
 __global__ __launch_bounds__(kThreads, 1)
 void bigemm_i8_kernel(const uint8_t* __restrict__ X, const uint8_t* __restrict__ W,
                       int32_t* __restrict__ Y, int M, int N, int K,
@@ -718,12 +759,17 @@ void bigemm_i8_kernel(const uint8_t* __restrict__ X, const uint8_t* __restrict__
     const int r = p >> 3, s = p & 7, c = s ^ swz_x(r);
     xoff[i] = (uint32_t)(r * ldx + c * 16);
     xk[i] = r < rows_valid ? c * 16 : 0x7FFFFFFF;
-    const int kr = p >> 3, cw = s ^ swz_w8(kr);
-    woff[i] = (uint32_t)(kr * ldw + cw * 16);
-    wk[i] = cw * 16 < cols_valid ? kr : 0x7FFFFFFF;
+    if constexpr (kWT) {
+      woff[i] = (uint32_t)(r * ldw + c * 16);
+      wk[i] = r < cols_valid ? c * 16 : 0x7FFFFFFF;
+    } else {
+      const int kr = p >> 3, cw = s ^ swz_w8(kr);
+      woff[i] = (uint32_t)(kr * ldw + cw * 16);
+      wk[i] = cw * 16 < cols_valid ? kr : 0x7FFFFFFF;
+    }
   }
   const uint8_t* Xt = X + (int64_t)row0 * ldx;
-  const uint8_t* Wt = W + col0;
+  const uint8_t* Wt = kWT ? W + (int64_t)col0 * ldw : W + col0;
 
   // The 8 LDS-DMA loads of K block kb (blocks past the end load zeros).
   auto issue = [&](int kb, uint8_t* stage) {
@@ -731,7 +777,7 @@ void bigemm_i8_kernel(const uint8_t* __restrict__ X, const uint8_t* __restrict__
     const int k0 = live ? kb * kBkI8 : 0;
     const int kleft = live ? K - k0 : 0;
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(Xt + k0);
-    const __amdgpu_buffer_rsrc_t rw = make_rsrc(Wt + (int64_t)k0 * ldw);
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(kWT ? Wt + k0 : Wt + (int64_t)k0 * ldw);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t o = xk[i] < kleft ? xoff[i] : kOob;
@@ -746,10 +792,12 @@ void bigemm_i8_kernel(const uint8_t* __restrict__ X, const uint8_t* __restrict__
   };
 
   // Fragment addresses per 32-wide K step kk: A one 16-byte read, B two
-  // transposing 8-byte reads (K values 0..7 and 8..15 of the lane's 16).
+  // transposing 8-byte reads (K values 0..7 and 8..15 of the lane's 16), or
+  // for W^T one 16-byte read addressed like A's.
   const int wm = wave >> 1, wn = wave & 1;
   int a_addr[2][4];      // [f][kk]
   int b_addr[2][4][2];   // [f][kk][half]
+  int bt_addr[2][4];     // [f][kk]
 #pragma unroll
   for (int f = 0; f < 2; ++f) {
 #pragma unroll
@@ -757,6 +805,10 @@ void bigemm_i8_kernel(const uint8_t* __restrict__ X, const uint8_t* __restrict__
       const int r = wm * 64 + f * 32 + (lane & 31);
       const int c = kk * 2 + (lane >> 5);
       a_addr[f][kk] = r * 128 + ((c ^ swz_x(r)) << 4);
+      if constexpr (kWT) {
+        const int n = wn * 64 + f * 32 + (lane & 31);
+        bt_addr[f][kk] = kTileBytes + n * 128 + ((c ^ swz_x(n)) << 4);
+      }
       const int G = lane >> 4, j = lane & 15;
       const int col = wn * 64 + f * 32 + (G & 1) * 16 + (j & 1) * 8;
 #pragma unroll
@@ -785,9 +837,13 @@ void bigemm_i8_kernel(const uint8_t* __restrict__ X, const uint8_t* __restrict__
 #pragma unroll
       for (int f = 0; f < 2; ++f) {
         a[f] = *LDS(const i32x4, st + a_addr[f][kk]);
-        const i32x2 lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32(LDS(i32x2, st + b_addr[f][kk][0]));
-        const i32x2 hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32(LDS(i32x2, st + b_addr[f][kk][1]));
-        b[f] = i32x4{lo[0], lo[1], hi[0], hi[1]};
+        if constexpr (kWT) {
+          b[f] = *LDS(const i32x4, st + bt_addr[f][kk]);
+        } else {
+          const i32x2 lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32(LDS(i32x2, st + b_addr[f][kk][0]));
+          const i32x2 hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32(LDS(i32x2, st + b_addr[f][kk][1]));
+          b[f] = i32x4{lo[0], lo[1], hi[0], hi[1]};
+        }
       }
 #pragma unroll
       for (int fm = 0; fm < 2; ++fm)
@@ -901,7 +957,7 @@ hipError_t launch_bf16_split(Op op, int32_t k_chunk, const void* X, const void* 
   return hipGetLastError();
 }
 
-hipError_t launch_mxfp8(Op op, const void* X, const void* W, void* Y, const void* XS, const void* WS,
+hipError_t launch_mxfp8(Op op, bool wt, const void* X, const void* W, void* Y, const void* XS, const void* WS,
                         int64_t M, int64_t N, int64_t K, int64_t ldx, int64_t ldw, int64_t ldy,
                         int64_t ldxs, int64_t ldws, hipStream_t stream) {
   const int tiles_m = (int)((M + 127) / 128);
@@ -911,19 +967,21 @@ hipError_t launch_mxfp8(Op op, const void* X, const void* W, void* Y, const void
   const bool staged = K % 512 == 0 && ((uintptr_t)XS & 15) == 0 && ldxs % 16 == 0 && ((uintptr_t)WS & 15) == 0 &&
                       ldws % 16 == 0;
   const bool obf = op.out == 1 /* BIGEMM_BF16 */;
-  auto kern = staged ? (obf ? bigemm_mxfp8_kernel<true, true> : bigemm_mxfp8_kernel<true, false>)
-                     : (obf ? bigemm_mxfp8_kernel<false, true> : bigemm_mxfp8_kernel<false, false>);
+  auto kern = wt ? (staged ? (obf ? bigemm_mxfp8_kernel<true, true, true> : bigemm_mxfp8_kernel<true, false, true>)
+                          : (obf ? bigemm_mxfp8_kernel<false, true, true> : bigemm_mxfp8_kernel<false, false, true>))
+                 : (staged ? (obf ? bigemm_mxfp8_kernel<true, true> : bigemm_mxfp8_kernel<true, false>)
+                          : (obf ? bigemm_mxfp8_kernel<false, true> : bigemm_mxfp8_kernel<false, false>));
   hipLaunchKernelGGL(kern, dim3(tiles_m * tiles_n), dim3(kThreads), 0, stream, (const uint8_t*)X,
                      (const uint8_t*)W, Y, (const uint8_t*)XS, (const uint8_t*)WS, (int)M, (int)N, (int)K, ldx, ldw,
                      ldy, ldxs, ldws, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
-hipError_t launch_i8(const void* X, const void* W, void* Y, int64_t M, int64_t N, int64_t K, int64_t ldx,
+hipError_t launch_i8(bool wt, const void* X, const void* W, void* Y, int64_t M, int64_t N, int64_t K, int64_t ldx,
                      int64_t ldw, int64_t ldy, hipStream_t stream) {
   const int tiles_m = (int)((M + 127) / 128);
   const int tiles_n = (int)((N + 127) / 128);
-  hipLaunchKernelGGL(bigemm_i8_kernel, dim3(tiles_m * tiles_n), dim3(kThreads), 0, stream, (const uint8_t*)X,
+  hipLaunchKernelGGL(wt ? bigemm_i8_kernel<true> : bigemm_i8_kernel<false>, dim3(tiles_m * tiles_n), dim3(kThreads), 0, stream, (const uint8_t*)X,
                      (const uint8_t*)W, (int32_t*)Y, (int)M, (int)N, (int)K, ldx, ldw, ldy, tiles_m, tiles_n);
   return hipGetLastError();
 }

@@ -53,7 +53,7 @@ def test_null_handle_paths():
     assert lib.bigemm_create_wt(None, None) == bg.BIGEMM_ERR_ARG
     h = ctypes.c_void_p(1)
     assert lib.bigemm_create_wt(None, ctypes.byref(h)) == bg.BIGEMM_ERR_ARG and h.value is None
-    assert lib.bigemm_check_args_wt(None, 1, 8, 8, A, 8, A, 8, A, 8) == bg.BIGEMM_ERR_ARG
+    assert lib.bigemm_check_args_wt(None, 1, 8, 8, A, 8, A, 8, A, 8, None, 0, None, 0) == bg.BIGEMM_ERR_ARG
     assert bg.bigemm_run_ws(0, 1, 8, 8, A, 8, A, 8, A, 8, check=False) == bg.BIGEMM_ERR_ARG
     n = ctypes.c_uint64()
     assert lib.bigemm_workspace_size(None, 1, 8, 8, ctypes.byref(n)) == bg.BIGEMM_ERR_ARG
@@ -134,9 +134,10 @@ def test_check_args_other_types():
     assert chk(I8, 16, 64, 64, XS=A, ldxs=2) == bg.BIGEMM_ERR_ARG
 
 
-def chk_wt(desc, M, N, K, X=A, ldx=None, W=A, ldw=None, Y=A, ldy=None):
-    return bg.bigemm_check_args_wt(desc[0], desc[1], desc[2], M, N, K, X, K if ldx is None else ldx,
-                                   W, K if ldw is None else ldw, Y, N if ldy is None else ldy)
+def chk_wt(desc, M, N, K, X=A, ldx=None, W=A, ldw=None, Y=A, ldy=None, XS=0, ldxs=0, WS=0, ldws=0):
+    return bg.bigemm_check_args_wt(*desc, M, N, K, X, K if ldx is None else ldx,
+                                   W, K if ldw is None else ldw, Y, N if ldy is None else ldy,
+                                   XS, ldxs, WS, ldws)
 
 
 def test_check_args_w_transposed():
@@ -156,10 +157,23 @@ def test_check_args_w_transposed():
     assert chk_wt(BF, 0, 64, 64, X=0, W=0, Y=0) == bg.BIGEMM_OK
     assert chk_wt(F16, 16, 64, 64) == bg.BIGEMM_OK
     assert chk_wt(BF_OUT_BF, 16, 64, 64) == bg.BIGEMM_OK
-    # bf16 and fp16 only
-    assert chk_wt(MX, 16, 64, 128) == bg.BIGEMM_ERR_UNSUPPORTED
-    assert chk_wt(I8, 16, 64, 64) == bg.BIGEMM_ERR_UNSUPPORTED
+    assert chk_wt(BF, 16, 64, 64, XS=A, ldxs=2) == bg.BIGEMM_ERR_ARG        # no scales for bf16
+    # int8: the same rules with ldw >= K
+    assert chk_wt(I8, 16, 64, 64) == bg.BIGEMM_OK
+    assert chk_wt(I8, 16, 64, 64, ldw=48) == bg.BIGEMM_ERR_ARG
+    # MXFP8: W_scale is [N, K/32], so ldws is checked against K/32 and 128 * ldws < 2^31
+    ok = dict(XS=A, ldxs=4, WS=A, ldws=4)
+    assert chk_wt(MX, 16, 64, 128, **ok) == bg.BIGEMM_OK
+    assert chk(MX, 16, 64, 128, ldw=64, **ok) == bg.BIGEMM_ERR_ARG           # ldws = 4 < N for [K, N]
+    assert chk_wt(MX, 16, 64, 128, XS=A, ldxs=4, WS=A, ldws=3) == bg.BIGEMM_ERR_ARG
+    assert chk_wt(MX, 16, 64, 128, XS=A, ldxs=4, WS=A + 1, ldws=5) == bg.BIGEMM_OK   # scales unaligned ok
+    assert chk_wt(MX, 16, 64, 128, XS=A, ldxs=4, WS=A, ldws=(1 << 24) - 1) == bg.BIGEMM_OK
+    assert chk_wt(MX, 16, 64, 128, XS=A, ldxs=4, WS=A, ldws=1 << 24) == bg.BIGEMM_ERR_ARG
+    assert chk_wt(MX, 16, 64, 128, ldw=112, **ok) == bg.BIGEMM_ERR_ARG      # ldw < K
+    assert chk_wt(MX, 16, 64, 128, XS=A, ldxs=4, WS=0, ldws=4) == bg.BIGEMM_ERR_ARG
+    # descriptors that are not provided at all
     assert chk_wt((bg.BIGEMM_BF16, bg.BIGEMM_F16, bg.BIGEMM_F32, 0), 4, 64, 64) == bg.BIGEMM_ERR_UNSUPPORTED
+    assert chk_wt((bg.BIGEMM_E4M3, bg.BIGEMM_E4M3, bg.BIGEMM_F32, 16), 4, 64, 64) == bg.BIGEMM_ERR_UNSUPPORTED
 
 
 def test_rmsnorm_check_args():

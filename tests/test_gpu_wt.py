@@ -1,10 +1,12 @@
-"""W given as its transpose ([N, K] rows, as a linear layer stores its weight).
+"""W given as its transpose ([N, K] rows, as a linear layer stores its weight;
+for MXFP8 with W_scale as [N, K/32]).
 
-The W-transposed handle stages W's tile differently but feeds the MFMA chain
-the same operands in the same order, so its output must carry exactly the
-bytes of the [K, N] handle for the same logical W (compared as raw bits) at
-every shape, ragged tails included; one direct oracle comparison per input
-type ties it to the gate of the other parity tests as well.
+The W-transposed handle stages W's tile (and scales) differently but feeds
+the MFMA chain the same operands and scales in the same order, so its output
+must carry exactly the bytes of the [K, N] handle for the same logical W
+(compared as raw bits) at every shape, ragged tails included, for every input
+family and both MXFP8 scale-load paths; direct oracle comparisons tie it to
+the gate of the other parity tests as well.
 """
 import ctypes
 
@@ -13,8 +15,8 @@ import pytest
 import torch
 
 import oracle
-from bigemm_inputs import SEED_W, SEED_X, normal_bf16
-from gpu_util import DEV, dev_bf16, require_gpu
+from bigemm_inputs import SEED_W, SEED_X, e8m0_scales, int_i8, normal_bf16, normal_e4m3
+from gpu_util import DEV, dev_bf16, dev_u8, require_gpu
 import invariant_gemm_deterministic_amd as bg
 
 pytestmark = pytest.mark.gpu
@@ -122,17 +124,18 @@ def test_wt_handle_rejects_kn_leading_dimension_rules():
     assert bg.bigemm_run(h, 0, N, K, 0, K, 0, K, 0, N, check=False) == bg.BIGEMM_OK
 
 
-def test_wt_create_refuses_other_families():
-    for t, sb in ((bg.BIGEMM_E4M3, 32), (bg.BIGEMM_I8, 0)):
+def test_wt_create_refuses_descriptors_not_provided():
+    for d in (bg.bigemm_desc(bg.BIGEMM_BF16, bg.BIGEMM_F16, bg.BIGEMM_F32, 0),
+              bg.bigemm_desc(bg.BIGEMM_E4M3, bg.BIGEMM_E4M3, bg.BIGEMM_F32, 16),
+              bg.bigemm_desc(bg.BIGEMM_I8, bg.BIGEMM_I8, bg.BIGEMM_F32, 0)):
         h = ctypes.c_void_p()
-        d = bg.bigemm_desc(t, t, bg.BIGEMM_I32 if t == bg.BIGEMM_I8 else bg.BIGEMM_F32, sb)
         assert bg.load().bigemm_create_wt(ctypes.byref(d), ctypes.byref(h)) == bg.BIGEMM_ERR_UNSUPPORTED
         assert h.value is None
 
 
 def test_mm_transposed_w_limits():
-    """The binding takes a transposed w only for bf16 / fp16 without split-K, and never a w with no
-    contiguous dimension."""
+    """The binding takes no transposed w for split-K, no w with no contiguous dimension, and no MXFP8
+    w_scale in a layout other than w's."""
     xd = dev_bf16(normal_bf16(9, (8, 64)))
     wt = dev_bf16(normal_bf16(10, (128, 64)))
     with pytest.raises(ValueError):
@@ -140,7 +143,79 @@ def test_mm_transposed_w_limits():
     w_strided = dev_bf16(normal_bf16(11, (64, 256)))[:, ::2]
     with pytest.raises(ValueError):
         bg.mm(xd, w_strided)
-    x8 = torch.zeros((8, 64), dtype=torch.int8, device=DEV)
-    w8 = torch.zeros((128, 64), dtype=torch.int8, device=DEV)
+    M, N, K = 8, 64, 128
+    x = dev_u8(normal_e4m3(1, (M, K)))
+    xs = dev_u8(e8m0_scales(2, (M, K // 32), "var"))
+    w_nk = dev_u8(normal_e4m3(3, (N, K)))
+    ws_kn = dev_u8(e8m0_scales(4, (K // 32, N), "var"))
     with pytest.raises(ValueError):
-        bg.mm(x8, w8.t())
+        bg.mm(x, w_nk.t(), xs, ws_kn)          # w as [N, K] rows, w_scale as [K/32, N] rows
+
+
+def _mx_case(M, N, K, seed=0):
+    X, W = normal_e4m3(40 + seed, (M, K)), normal_e4m3(41 + seed, (K, N))
+    XS = e8m0_scales(42 + seed, (M, K // 32), "var")
+    WS = e8m0_scales(43 + seed, (K // 32, N), "var")
+    return X, W, XS, WS
+
+
+# K = 160 and 96: byte-path scales; K a multiple of 512 with packed scale rows: staged scales
+MX_SHAPES = [(1, 64, 128), (33, 256, 160), (300, 64, 96), (130, 272, 1024), (64, 512, 2048),
+             (1024, 4096, 4096)]
+
+
+@pytest.mark.parametrize("M,N,K", MX_SHAPES)
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_wt_bytes_equal_kn_mxfp8(M, N, K, out_dtype):
+    X, W, XS, WS = _mx_case(M, N, K)
+    xd, xs = dev_u8(X), dev_u8(XS)
+    a = bg.mm(xd, dev_u8(W), xs, dev_u8(WS), out_dtype=out_dtype)
+    b = bg.mm(xd, dev_u8(W.T).t(), xs, dev_u8(WS.T).t(), out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(a), _bits(b))
+
+
+@pytest.mark.parametrize("K", [1024, 2048])
+def test_wt_mxfp8_scale_load_paths(K):
+    """W^T scale rows packed (staged through LDS), padded to a length that is not a multiple of 16,
+    or one byte past an aligned base (byte path): all give the bytes of the [K, N] call."""
+    M, N = 200, 256
+    X, W, XS, WS = _mx_case(M, N, K, seed=7)
+    xd, xs = dev_u8(X), dev_u8(XS)
+    ref = bg.mm(xd, dev_u8(W), xs, dev_u8(WS))
+    w_t = dev_u8(W.T).t()
+    nsb = K // 32
+    wide = torch.zeros((N, nsb + 5), dtype=torch.uint8, device=DEV)
+    outs = []
+    wide[:, :nsb] = dev_u8(WS.T)
+    outs.append(bg.mm(xd, w_t, xs, wide[:, :nsb].t()))
+    torch.cuda.synchronize()
+    wide.zero_()
+    wide[:, 1:1 + nsb] = dev_u8(WS.T)
+    outs.append(bg.mm(xd, w_t, xs, wide[:, 1:1 + nsb].t()))
+    outs.append(bg.mm(xd, w_t, xs, dev_u8(WS.T).t()))
+    torch.cuda.synchronize()
+    for y in outs:
+        assert torch.equal(_bits(y), _bits(ref))
+
+
+@pytest.mark.parametrize("M,N,K", [(33, 256, 160), (130, 272, 1024)])
+def test_wt_mxfp8_oracle_parity(M, N, K):
+    X, W, XS, WS = _mx_case(M, N, K, seed=3)
+    y = bg.mm(dev_u8(X), dev_u8(W.T).t(), dev_u8(XS), dev_u8(WS.T).t())
+    torch.cuda.synchronize()
+    Y, S = oracle.gemm_mxfp8(X, W, XS, WS)
+    assert oracle.max_normalized_error(y.cpu().numpy(), Y, S) <= TOL
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 16, 16), (5, 48, 32), (130, 272, 1040), (1024, 4096, 4096)])
+def test_wt_int8_exact(M, N, K):
+    """int8 with W as [N, K] rows: the [K, N] call's bytes, and the exact integer product."""
+    X, W = int_i8(50, (M, K)), int_i8(51, (K, N))
+    xd = torch.from_numpy(X).to(DEV)
+    a = bg.mm(xd, torch.from_numpy(W).to(DEV))
+    b = bg.mm(xd, torch.from_numpy(np.ascontiguousarray(W.T)).to(DEV).t())
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    if M * N * K <= 1 << 26:
+        assert np.array_equal(b.cpu().numpy().astype(np.int64), X.astype(np.int64) @ W.astype(np.int64))
