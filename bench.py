@@ -10,7 +10,8 @@ ABI with inputs resident in HBM. Also reported:
   last-level cache, so W is read from HBM; ``us_warm_llc`` is the same call on
   one buffer set), with achieved algorithmic HBM GB/s and % of the roofline
   bound max(flops / MFMA peak, algorithmic bytes / HBM peak);
-* ``other_types_k4096_n4096``: the MXFP8 kernel (E4M3, K-varying E8M0 scales),
+* ``other_types_k4096_n4096``: the MXFP8 kernel (E4M3, K-varying E8M0 scales;
+  also with W and its scales given as [N, K] and [N, K/32] rows),
   fp16 inputs, bf16 output, bf16 with W given as [N, K] rows, and int8 inputs
   at M = 1024 and 4096, each against its dense MFMA peak (context, not the
   metric); ``w_transposed_byte_diffs`` compares the [N, K]-row call at
@@ -308,14 +309,17 @@ def main():
         Wm = torch.from_numpy(normal_e4m3(SEED_W, (K, N))).to(dev)
         XS = torch.from_numpy(e8m0_scales(SEED_X + SCALE_SEED_OFFSET, (4096, K // 32), "var")).to(dev)
         WS = torch.from_numpy(e8m0_scales(SEED_W + SCALE_SEED_OFFSET, (K // 32, N), "var")).to(dev)
-        for m in (1024, 4096):
-            for _ in range(5):
-                bg.mm(Xm[:m], Wm, XS[:m], WS, out=Y[:m])
-            t = _events(torch, stream, lambda i: bg.mm(Xm[:m], Wm, XS[:m], WS, out=Y[:m]), 20)
-            f = 2.0 * m * N * K
-            mx.append({"kind": "mxfp8", "M": m, "us": round(t * 1e3, 2), "tflops": round(f / (t * 1e-3) / 1e12, 1),
-                       "pct_peak": round(100 * f / (t * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 1)})
-        del Xm, Wm, XS, WS
+        WmT, WST = Wm.t().contiguous(), WS.t().contiguous()   # W and its scales as [N, K] and [N, K/32] rows
+        for kind, fn in (("mxfp8", lambda m: bg.mm(Xm[:m], Wm, XS[:m], WS, out=Y[:m])),
+                         ("mxfp8_w_transposed", lambda m: bg.mm(Xm[:m], WmT.t(), XS[:m], WST.t(), out=Y[:m]))):
+            for m in (1024, 4096):
+                for _ in range(5):
+                    fn(m)
+                t = _events(torch, stream, lambda i: fn(m), 20)
+                f = 2.0 * m * N * K
+                mx.append({"kind": kind, "M": m, "us": round(t * 1e3, 2), "tflops": round(f / (t * 1e-3) / 1e12, 1),
+                           "pct_peak": round(100 * f / (t * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 1)})
+        del Xm, Wm, XS, WS, WmT, WST
         # fp16 inputs and int8 inputs on the same tile skeleton, and bf16 output (context)
         from bigemm_inputs import int_i8, normal_f16
         X16 = torch.from_numpy(normal_f16(SEED_X, (4096, K))).view(torch.float16).to(dev)
