@@ -167,6 +167,16 @@ BIGEMM_API bigemm_status bigemm_run(bigemm_t h, int64_t M, int64_t N, int64_t K,
 BIGEMM_API bigemm_status bigemm_create_split_k(const bigemm_desc* desc, int32_t k_chunk, bigemm_t* out);
 
 /*
+ * The split-K handle above with W given as [N, K] rows (ldw >= K), as for
+ * bigemm_create_wt: the same chunks, chunk sums and ordered merge, with W's
+ * tile staged from the transposed layout, so the bytes equal those of a
+ * bigemm_create_split_k handle with the same k_chunk given W as [K, N].
+ * bf16 and fp16 inputs; errors as bigemm_create_split_k. Run with
+ * bigemm_run_ws.
+ */
+BIGEMM_API bigemm_status bigemm_create_split_k_wt(const bigemm_desc* desc, int32_t k_chunk, bigemm_t* out);
+
+/*
  * Handle whose W is given as its transpose: an [N, K] row-major array with
  * leading dimension ldw >= K (the layout in which a linear layer keeps its
  * weight), so such a weight needs no copy. For MXFP8, W_scale is then
@@ -182,7 +192,8 @@ BIGEMM_API bigemm_status bigemm_create_split_k(const bigemm_desc* desc, int32_t 
  * Run it with bigemm_run or bigemm_run_ws (no workspace). The requirements of
  * bigemm_run hold with ldw >= K in place of ldw >= N and, for MXFP8,
  * ldws >= K/32 in place of ldws >= N and 128 * ldws below 2^31. Devices other
- * than gfx950 return BIGEMM_ERR_UNSUPPORTED; there is no split-K form.
+ * than gfx950 return BIGEMM_ERR_UNSUPPORTED. bigemm_create_split_k_wt is its
+ * split-K form (bf16 and fp16).
  * *out is NULL on failure.
  */
 BIGEMM_API bigemm_status bigemm_create_wt(const bigemm_desc* desc, bigemm_t* out);

@@ -17,10 +17,12 @@ import threading
 
 __all__ = [
     "BIGEMM_OK", "BIGEMM_ERR_ARG", "BIGEMM_ERR_UNSUPPORTED", "BIGEMM_ERR_DEVICE", "BIGEMM_ERR_NOMEM",
-    "BIGEMM_BF16", "BIGEMM_F32", "BIGEMM_E4M3", "BIGEMM_E8M0",
+    "BIGEMM_BF16", "BIGEMM_F32", "BIGEMM_E4M3", "BIGEMM_E8M0", "BIGEMM_F16", "BIGEMM_I8", "BIGEMM_I32",
     "BigemmError", "bigemm_desc", "library_path", "load",
     "bigemm_create", "bigemm_run", "bigemm_destroy", "bigemm_status_str", "bigemm_get_config",
     "bigemm_check_args", "bigemm_abi_version", "mm", "bigemm_create_wt", "bigemm_check_args_wt",
+    "bigemm_create_split_k", "bigemm_create_split_k_wt", "bigemm_workspace_size", "bigemm_run_ws",
+    "bigemm_rmsnorm", "bigemm_rmsnorm_check_args", "rmsnorm",
     "bigemm_kv_layout", "bigemm_kv_cache_write", "bigemm_attn_workspace_size", "bigemm_paged_attention",
     "bigemm_paged_attention_check_args", "kv_cache_write", "paged_attention", "ATTN_SPLIT",
 ]
@@ -103,6 +105,8 @@ def load():
         lib.bigemm_rmsnorm_check_args.argtypes = [i32, i64, i64, vp, i64, vp, vp, i64]
         lib.bigemm_create_split_k.restype = ctypes.c_int
         lib.bigemm_create_split_k.argtypes = [ctypes.POINTER(bigemm_desc), i32, ctypes.POINTER(vp)]
+        lib.bigemm_create_split_k_wt.restype = ctypes.c_int
+        lib.bigemm_create_split_k_wt.argtypes = [ctypes.POINTER(bigemm_desc), i32, ctypes.POINTER(vp)]
         lib.bigemm_workspace_size.restype = ctypes.c_int
         lib.bigemm_workspace_size.argtypes = [vp, i64, i64, i64, ctypes.POINTER(ctypes.c_uint64)]
         lib.bigemm_run_ws.restype = ctypes.c_int
@@ -159,6 +163,16 @@ def bigemm_create_split_k(x_type: int, w_type: int, y_type: int, k_chunk: int) -
     st = load().bigemm_create_split_k(ctypes.byref(d), int(k_chunk), ctypes.byref(h))
     if st != BIGEMM_OK:
         raise BigemmError(st, "bigemm_create_split_k")
+    return int(h.value)
+
+
+def bigemm_create_split_k_wt(x_type: int, w_type: int, y_type: int, k_chunk: int) -> int:
+    """Create an opt-in split-K handle whose W is given as [N, K] (bf16 / fp16). Raises BigemmError."""
+    h = ctypes.c_void_p()
+    d = _desc(x_type, w_type, y_type, 0)
+    st = load().bigemm_create_split_k_wt(ctypes.byref(d), int(k_chunk), ctypes.byref(h))
+    if st != BIGEMM_OK:
+        raise BigemmError(st, "bigemm_create_split_k_wt")
     return int(h.value)
 
 
@@ -254,7 +268,7 @@ def _handle(kind: str, device_index: int, y_type: int = BIGEMM_F32, k_chunk: int
         t, sb = _FAMILIES[kind]
         with torch.cuda.device(device_index):
             if k_chunk:
-                h = bigemm_create_split_k(t, t, y_type, k_chunk)
+                h = (bigemm_create_split_k_wt if wt else bigemm_create_split_k)(t, t, y_type, k_chunk)
             elif wt:
                 h = bigemm_create_wt(t, t, y_type, sb)
             else:
@@ -286,7 +300,7 @@ def mm(x, w, x_scale=None, w_scale=None, out=None, stream=None, out_dtype=None, 
     [M, N] tensor of ``out_dtype`` (float32 or bfloat16 for floating inputs,
     default float32; int32 for int8).
     ``k_chunk`` (bf16 / fp16 only) selects the opt-in split-K handle with that
-    K chunk; its workspace is ``workspace`` (a CUDA tensor of at least
+    K chunk (for either layout of ``w``); its workspace is ``workspace`` (a CUDA tensor of at least
     ``bigemm_workspace_size`` bytes) or a fresh torch allocation.
     """
     import torch
@@ -335,17 +349,16 @@ def mm(x, w, x_scale=None, w_scale=None, out=None, stream=None, out_dtype=None, 
         stream = torch.cuda.current_stream(x.device).cuda_stream
     # The handle belongs to x's device, and the library runs a handle only on its own device.
     with torch.cuda.device(dev):
-        if wt and k_chunk:
-            raise ValueError("split-K takes w as [K, N] with contiguous rows")
         if k_chunk:
             if kind not in ("bf16", "f16"):
                 raise ValueError("split-K is provided for bf16 and fp16 inputs")
-            h = _handle(kind, dev, ytypes[out_dtype], int(k_chunk))
+            h = _handle(kind, dev, ytypes[out_dtype], int(k_chunk), wt)
             need = bigemm_workspace_size(h, M, N, K)
             if workspace is None:
                 workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
             ws_bytes = workspace.numel() * workspace.element_size()
-            bigemm_run_ws(h, M, N, K, x.data_ptr(), _ld(x), w.data_ptr(), _ld(w), out.data_ptr(), _ld(out),
+            bigemm_run_ws(h, M, N, K, x.data_ptr(), _ld(x), w.data_ptr(), _ld(w.t()) if wt else _ld(w),
+                          out.data_ptr(), _ld(out),
                           0, 0, 0, 0, workspace.data_ptr(), ws_bytes, stream)
             return out
         h = _handle(kind, dev, ytypes[out_dtype], 0, wt)  # raises BigemmError for a combination not provided

@@ -358,6 +358,13 @@ bigemm_status bigemm_create_split_k(const bigemm_desc* desc, int32_t k_chunk, bi
   return BIGEMM_OK;
 }
 
+bigemm_status bigemm_create_split_k_wt(const bigemm_desc* desc, int32_t k_chunk, bigemm_t* out) {
+  const bigemm_status st = bigemm_create_split_k(desc, k_chunk, out);
+  if (st != BIGEMM_OK) return st;
+  (*out)->w_trans = true;
+  return BIGEMM_OK;
+}
+
 bigemm_status bigemm_workspace_size(bigemm_t h, int64_t M, int64_t N, int64_t K, uint64_t* bytes) {
   if (!h || !bytes || M < 0 || N < 0 || K < 0) return BIGEMM_ERR_ARG;
   *bytes = 0;
@@ -387,8 +394,8 @@ bigemm_status bigemm_run_ws(bigemm_t h, int64_t M, int64_t N, int64_t K, const v
   if (!workspace || !aligned16(workspace) || workspace_bytes < need) return BIGEMM_ERR_ARG;
   if ((K + h->k_chunk - 1) / h->k_chunk * ((M + 127) / 128) * ((N + 127) / 128) > INT32_MAX) return BIGEMM_ERR_ARG;
   if (M * N > (int64_t)INT32_MAX * 4) return BIGEMM_ERR_ARG;  // merge grid
-  const hipError_t e = bigemm::launch_bf16_split(h->op, h->k_chunk, X, W, Y, workspace, M, N, K, ldx, ldw, ldy,
-                                                 (hipStream_t)stream);
+  const hipError_t e = bigemm::launch_bf16_split(h->op, h->w_trans, h->k_chunk, X, W, Y, workspace, M, N, K, ldx,
+                                                 ldw, ldy, (hipStream_t)stream);
   return e == hipSuccess ? BIGEMM_OK : BIGEMM_ERR_DEVICE;
 }
 

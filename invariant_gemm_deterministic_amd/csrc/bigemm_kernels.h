@@ -25,8 +25,9 @@ hipError_t launch_bf16(Op op, bool wt, const void* X, const void* W, void* Y, in
 
 // Opt-in split-K (bf16 / fp16 inputs): chunk sums of k_chunk K values into P
 // ([ceil(K/k_chunk)][M][N] fp32, 16-byte aligned), then their ordered sum into Y.
-hipError_t launch_bf16_split(Op op, int32_t k_chunk, const void* X, const void* W, void* Y, void* P, int64_t M,
-                             int64_t N, int64_t K, int64_t ldx, int64_t ldw, int64_t ldy, hipStream_t stream);
+hipError_t launch_bf16_split(Op op, bool wt, int32_t k_chunk, const void* X, const void* W, void* Y, void* P,
+                             int64_t M, int64_t N, int64_t K, int64_t ldx, int64_t ldw, int64_t ldy,
+                             hipStream_t stream);
 
 hipError_t launch_mxfp8(Op op, bool wt, const void* X, const void* W, void* Y, const void* XS, const void* WS,
                         int64_t M, int64_t N, int64_t K, int64_t ldx, int64_t ldw, int64_t ldy,

@@ -937,14 +937,16 @@ hipError_t launch_bf16(Op op, bool wt, const void* X, const void* W, void* Y, in
   return hipGetLastError();
 }
 
-hipError_t launch_bf16_split(Op op, int32_t k_chunk, const void* X, const void* W, void* Y, void* P, int64_t M,
-                             int64_t N, int64_t K, int64_t ldx, int64_t ldw, int64_t ldy, hipStream_t stream) {
+hipError_t launch_bf16_split(Op op, bool wt, int32_t k_chunk, const void* X, const void* W, void* Y, void* P,
+                             int64_t M, int64_t N, int64_t K, int64_t ldx, int64_t ldw, int64_t ldy,
+                             hipStream_t stream) {
   const int tiles_m = (int)((M + 127) / 128);
   const int tiles_n = (int)((N + 127) / 128);
   const int nsplit = (int)((K + k_chunk - 1) / k_chunk);
   const int64_t stride = M * N;
   const bool f16 = op.in == kInF16, obf = op.out == 1 /* BIGEMM_BF16 */;
-  auto kern = f16 ? bigemm_bf16_kernel<true, false, true> : bigemm_bf16_kernel<false, false, true>;
+  auto kern = wt ? (f16 ? bigemm_bf16_kernel<true, false, true, true> : bigemm_bf16_kernel<false, false, true, true>)
+                 : (f16 ? bigemm_bf16_kernel<true, false, true> : bigemm_bf16_kernel<false, false, true>);
   hipLaunchKernelGGL(kern, dim3(tiles_m * tiles_n * nsplit), dim3(kThreadsBf16), 0, stream, (const uint16_t*)X,
                      (const uint16_t*)W, P, (int)M, (int)N, (int)K, ldx, ldw, N, tiles_m, tiles_n,
                      k_chunk / kBkBf16, stride);

@@ -26,7 +26,7 @@ def test_header_declares_the_boundary():
                  "bigemm_create_split_k", "bigemm_workspace_size", "bigemm_run_ws",
                  "bigemm_rmsnorm", "bigemm_rmsnorm_check_args", "bigemm_kv_cache_write",
                  "bigemm_attn_workspace_size", "bigemm_paged_attention", "bigemm_paged_attention_check_args",
-                 "bigemm_create_wt", "bigemm_check_args_wt"):
+                 "bigemm_create_wt", "bigemm_check_args_wt", "bigemm_create_split_k_wt"):
         assert name in fns
 
 
@@ -51,6 +51,7 @@ def test_null_handle_paths():
     assert lib.bigemm_create(None, None) == bg.BIGEMM_ERR_ARG
     assert lib.bigemm_create_split_k(None, 512, None) == bg.BIGEMM_ERR_ARG
     assert lib.bigemm_create_wt(None, None) == bg.BIGEMM_ERR_ARG
+    assert lib.bigemm_create_split_k_wt(None, 512, None) == bg.BIGEMM_ERR_ARG
     h = ctypes.c_void_p(1)
     assert lib.bigemm_create_wt(None, ctypes.byref(h)) == bg.BIGEMM_ERR_ARG and h.value is None
     assert lib.bigemm_check_args_wt(None, 1, 8, 8, A, 8, A, 8, A, 8, None, 0, None, 0) == bg.BIGEMM_ERR_ARG

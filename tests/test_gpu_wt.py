@@ -133,13 +133,47 @@ def test_wt_create_refuses_descriptors_not_provided():
         assert h.value is None
 
 
+@pytest.mark.parametrize("M,N,K,k_chunk", [(1, 136, 1000, 256), (5, 264, 520, 512), (129, 4096, 4096, 512),
+                                             (300, 1000, 1096, 2048), (64, 1024, 16384, 2048)])
+@pytest.mark.parametrize("dtype,out_dtype", [("bf16", torch.float32), ("bf16", torch.bfloat16),
+                                             ("f16", torch.float32)])
+def test_wt_split_k_bytes_equal_kn(M, N, K, k_chunk, dtype, out_dtype):
+    """Split-K with W as [N, K] rows: the bytes of the [K, N] split-K call with the same k_chunk (a
+    ragged last chunk, a single chunk, many chunks)."""
+    if dtype == "bf16":
+        X, W = normal_bf16(SEED_X + 2, (M, K)), normal_bf16(SEED_W + 2, (K, N))
+        xd, w_kn, w_nk = dev_bf16(X), dev_bf16(W), dev_bf16(np.ascontiguousarray(W.T))
+    else:
+        g = torch.Generator().manual_seed(M + K)
+        Xf = torch.randn(M, K, generator=g).to(torch.float16)
+        Wf = torch.randn(K, N, generator=g).to(torch.float16)
+        xd, w_kn, w_nk = Xf.to(DEV), Wf.to(DEV), Wf.t().contiguous().to(DEV)
+    a = bg.mm(xd, w_kn, out_dtype=out_dtype, k_chunk=k_chunk)
+    b = bg.mm(xd, w_nk.t(), out_dtype=out_dtype, k_chunk=k_chunk)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(a), _bits(b))
+    if K <= k_chunk:   # one chunk: the unsplit kernel's bytes
+        c = bg.mm(xd, w_nk.t(), out_dtype=out_dtype)
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(c), _bits(b))
+
+
+def test_wt_split_k_create_refuses_other_families():
+    for d in (bg.bigemm_desc(bg.BIGEMM_E4M3, bg.BIGEMM_E4M3, bg.BIGEMM_F32, 32),
+              bg.bigemm_desc(bg.BIGEMM_I8, bg.BIGEMM_I8, bg.BIGEMM_I32, 0)):
+        h = ctypes.c_void_p()
+        assert bg.load().bigemm_create_split_k_wt(ctypes.byref(d), 512, ctypes.byref(h)) == \
+            bg.BIGEMM_ERR_UNSUPPORTED
+        assert h.value is None
+    h = ctypes.c_void_p()
+    d = bg.bigemm_desc(bg.BIGEMM_BF16, bg.BIGEMM_BF16, bg.BIGEMM_F32, 0)
+    assert bg.load().bigemm_create_split_k_wt(ctypes.byref(d), 100, ctypes.byref(h)) == bg.BIGEMM_ERR_ARG
+
+
 def test_mm_transposed_w_limits():
-    """The binding takes no transposed w for split-K, no w with no contiguous dimension, and no MXFP8
-    w_scale in a layout other than w's."""
+    """The binding takes no w with no contiguous dimension, and no MXFP8 w_scale in a layout other
+    than w's."""
     xd = dev_bf16(normal_bf16(9, (8, 64)))
-    wt = dev_bf16(normal_bf16(10, (128, 64)))
-    with pytest.raises(ValueError):
-        bg.mm(xd, wt.t(), k_chunk=64)
     w_strided = dev_bf16(normal_bf16(11, (64, 256)))[:, ::2]
     with pytest.raises(ValueError):
         bg.mm(xd, w_strided)
