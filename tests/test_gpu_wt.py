@@ -253,3 +253,49 @@ def test_wt_int8_exact(M, N, K):
     assert torch.equal(a, b)
     if M * N * K <= 1 << 26:
         assert np.array_equal(b.cpu().numpy().astype(np.int64), X.astype(np.int64) @ W.astype(np.int64))
+
+
+def _padded(a, pad):
+    """Device copy of a 2-D numpy array in rows of a.shape[1] + pad elements (a view of the logical part)."""
+    t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16) if a.dtype == np.uint16
+                         else np.ascontiguousarray(a))
+    buf = torch.zeros((a.shape[0], a.shape[1] + pad), dtype=t.dtype)
+    buf[:, :a.shape[1]] = t
+    return buf.to(DEV)[:, :a.shape[1]]
+
+
+@pytest.mark.parametrize("family", ["bf16", "mx", "i8"])
+def test_wt_random_shapes_and_padding(family):
+    """40 seeded random shapes per family (ragged in M, N and K) with random row padding of X, W^T,
+    Y and the scales: the [N, K] call's bytes equal the [K, N] call's."""
+    rng = np.random.default_rng({"bf16": 11, "mx": 12, "i8": 13}[family])
+    kq, nq = {"bf16": (8, 8), "mx": (32, 16), "i8": (16, 16)}[family]
+    ypad = 4  # fp32 / int32 output rows stay 16-byte aligned
+    for case in range(40):
+        M = int(rng.integers(1, 300))
+        N = nq * int(rng.integers(1, 640 // nq))
+        K = kq * int(rng.integers(1, 1100 // kq))
+        pad = int(rng.choice([0, 16, 48]))   # keeps every row 16-byte aligned for 1- and 2-byte elements
+        if family == "bf16":
+            X, W = normal_bf16(100 + case, (M, K)), normal_bf16(200 + case, (K, N))
+            args_kn, args_nk = (), ()
+        elif family == "mx":
+            X, W, XS, WS = _mx_case(M, N, K, seed=case)
+            spad = int(rng.choice([0, 3, 16]))
+            xs = _padded(XS, spad)
+            args_kn = (xs, _padded(WS, spad))
+            args_nk = (xs, _padded(WS.T, spad).t())
+        else:
+            X, W = int_i8(300 + case, (M, K)), int_i8(400 + case, (K, N))
+            args_kn, args_nk = (), ()
+        xd = _padded(X, pad)
+        w_kn = _padded(W, pad)
+        w_nk = _padded(W.T, pad).t()
+        odt = torch.int32 if family == "i8" else torch.float32
+        ya = torch.full((M, N + ypad), -1, dtype=odt, device=DEV)
+        yb = torch.full((M, N + ypad), -1, dtype=odt, device=DEV)
+        bg.mm(xd, w_kn, *args_kn, out=ya[:, :N])
+        bg.mm(xd, w_nk, *args_nk, out=yb[:, :N])
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(ya) if odt == torch.float32 else ya, _bits(yb) if odt == torch.float32 else yb), \
+            (family, case, M, N, K, pad)
