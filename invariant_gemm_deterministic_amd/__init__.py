@@ -300,8 +300,9 @@ def mm(x, w, x_scale=None, w_scale=None, out=None, stream=None, out_dtype=None, 
     [M, N] tensor of ``out_dtype`` (float32 or bfloat16 for floating inputs,
     default float32; int32 for int8).
     ``k_chunk`` (bf16 / fp16 only) selects the opt-in split-K handle with that
-    K chunk (for either layout of ``w``); its workspace is ``workspace`` (a CUDA tensor of at least
-    ``bigemm_workspace_size`` bytes) or a fresh torch allocation.
+    K chunk (for either layout of ``w``); its workspace is ``workspace`` (a
+    CUDA tensor of at least ``bigemm_workspace_size`` bytes) or a fresh torch
+    allocation.
     """
     import torch
 
@@ -347,6 +348,7 @@ def mm(x, w, x_scale=None, w_scale=None, out=None, stream=None, out_dtype=None, 
         raise ValueError("out must be [M, N] with contiguous rows")
     if stream is None:
         stream = torch.cuda.current_stream(x.device).cuda_stream
+    ldw = _ld(w.t()) if wt else _ld(w)
     # The handle belongs to x's device, and the library runs a handle only on its own device.
     with torch.cuda.device(dev):
         if k_chunk:
@@ -357,15 +359,13 @@ def mm(x, w, x_scale=None, w_scale=None, out=None, stream=None, out_dtype=None, 
             if workspace is None:
                 workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
             ws_bytes = workspace.numel() * workspace.element_size()
-            bigemm_run_ws(h, M, N, K, x.data_ptr(), _ld(x), w.data_ptr(), _ld(w.t()) if wt else _ld(w),
-                          out.data_ptr(), _ld(out),
+            bigemm_run_ws(h, M, N, K, x.data_ptr(), _ld(x), w.data_ptr(), ldw, out.data_ptr(), _ld(out),
                           0, 0, 0, 0, workspace.data_ptr(), ws_bytes, stream)
             return out
         h = _handle(kind, dev, ytypes[out_dtype], 0, wt)  # raises BigemmError for a combination not provided
-        ldw = _ld(w.t()) if wt else _ld(w)
         if mx:
             if tuple(x_scale.shape) != (M, K // 32) or tuple(w_scale.shape) != (K // 32, N):
-                raise ValueError(f"scales must be [M, K/32] and [K/32, N] = [{M}, {K // 32}] and [{K // 32}, {N}]")
+                raise ValueError(f"scales must be [M, K/32] = [{M}, {K // 32}] and [K/32, N] = [{K // 32}, {N}]")
             ws = w_scale.t() if wt else w_scale   # rows: [N, K/32] for W^T, else [K/32, N]
             for t in (x_scale, ws):
                 if not t.is_cuda or t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):

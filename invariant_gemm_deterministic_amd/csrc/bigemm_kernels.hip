@@ -140,8 +140,10 @@ __device__ __forceinline__ void store_out(__amdgpu_buffer_rsrc_t ry, bool ok, ui
 template <bool kF16>
 __device__ __forceinline__ f32x16 mfma_16bit(i32x4 a, i32x4 b, f32x16 c) {
   if (kF16)
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                  0, 0);
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                 0, 0);
 }
 
 // ------------------------------------------------------------------------ bf16
@@ -923,15 +925,22 @@ void bigemm_split_merge_kernel(const float* __restrict__ P, void* __restrict__ Y
 
 // ------------------------------------------------------------------ launchers
 
+typedef void (*Bf16KernelFn)(const uint16_t*, const uint16_t*, void*, int, int, int, int64_t, int64_t, int64_t, int,
+                             int, int, int64_t);
+// The bf16 / fp16 kernel instance for W given as [K, N] (wt false) or [N, K].
+template <bool kF16, bool kOutBf16, bool kSplit>
+Bf16KernelFn bf16_kernel_for(bool wt) {
+  return wt ? bigemm_bf16_kernel<kF16, kOutBf16, kSplit, true> : bigemm_bf16_kernel<kF16, kOutBf16, kSplit, false>;
+}
+
 hipError_t launch_bf16(Op op, bool wt, const void* X, const void* W, void* Y, int64_t M, int64_t N, int64_t K,
                        int64_t ldx, int64_t ldw, int64_t ldy, hipStream_t stream) {
   const int tiles_m = (int)((M + 127) / 128);
   const int tiles_n = (int)((N + 127) / 128);
   const bool f16 = op.in == kInF16, obf = op.out == 1 /* BIGEMM_BF16 */;
-  auto kern = wt ? (f16 ? (obf ? bigemm_bf16_kernel<true, true, false, true> : bigemm_bf16_kernel<true, false, false, true>)
-                        : (obf ? bigemm_bf16_kernel<false, true, false, true> : bigemm_bf16_kernel<false, false, false, true>))
-                 : (f16 ? (obf ? bigemm_bf16_kernel<true, true, false> : bigemm_bf16_kernel<true, false, false>)
-                        : (obf ? bigemm_bf16_kernel<false, true, false> : bigemm_bf16_kernel<false, false, false>));
+  const Bf16KernelFn kern =
+      f16 ? (obf ? bf16_kernel_for<true, true, false>(wt) : bf16_kernel_for<true, false, false>(wt))
+          : (obf ? bf16_kernel_for<false, true, false>(wt) : bf16_kernel_for<false, false, false>(wt));
   hipLaunchKernelGGL(kern, dim3(tiles_m * tiles_n), dim3(kThreadsBf16), 0, stream, (const uint16_t*)X,
                      (const uint16_t*)W, Y, (int)M, (int)N, (int)K, ldx, ldw, ldy, tiles_m, tiles_n, 0, (int64_t)0);
   return hipGetLastError();
@@ -945,8 +954,7 @@ hipError_t launch_bf16_split(Op op, bool wt, int32_t k_chunk, const void* X, con
   const int nsplit = (int)((K + k_chunk - 1) / k_chunk);
   const int64_t stride = M * N;
   const bool f16 = op.in == kInF16, obf = op.out == 1 /* BIGEMM_BF16 */;
-  auto kern = wt ? (f16 ? bigemm_bf16_kernel<true, false, true, true> : bigemm_bf16_kernel<false, false, true, true>)
-                 : (f16 ? bigemm_bf16_kernel<true, false, true> : bigemm_bf16_kernel<false, false, true>);
+  const Bf16KernelFn kern = f16 ? bf16_kernel_for<true, false, true>(wt) : bf16_kernel_for<false, false, true>(wt);
   hipLaunchKernelGGL(kern, dim3(tiles_m * tiles_n * nsplit), dim3(kThreadsBf16), 0, stream, (const uint16_t*)X,
                      (const uint16_t*)W, P, (int)M, (int)N, (int)K, ldx, ldw, N, tiles_m, tiles_n,
                      k_chunk / kBkBf16, stride);
@@ -970,9 +978,9 @@ hipError_t launch_mxfp8(Op op, bool wt, const void* X, const void* W, void* Y, c
                       ldws % 16 == 0;
   const bool obf = op.out == 1 /* BIGEMM_BF16 */;
   auto kern = wt ? (staged ? (obf ? bigemm_mxfp8_kernel<true, true, true> : bigemm_mxfp8_kernel<true, false, true>)
-                          : (obf ? bigemm_mxfp8_kernel<false, true, true> : bigemm_mxfp8_kernel<false, false, true>))
+                           : (obf ? bigemm_mxfp8_kernel<false, true, true> : bigemm_mxfp8_kernel<false, false, true>))
                  : (staged ? (obf ? bigemm_mxfp8_kernel<true, true> : bigemm_mxfp8_kernel<true, false>)
-                          : (obf ? bigemm_mxfp8_kernel<false, true> : bigemm_mxfp8_kernel<false, false>));
+                           : (obf ? bigemm_mxfp8_kernel<false, true> : bigemm_mxfp8_kernel<false, false>));
   hipLaunchKernelGGL(kern, dim3(tiles_m * tiles_n), dim3(kThreads), 0, stream, (const uint8_t*)X,
                      (const uint8_t*)W, Y, (const uint8_t*)XS, (const uint8_t*)WS, (int)M, (int)N, (int)K, ldx, ldw,
                      ldy, ldxs, ldws, tiles_m, tiles_n);
@@ -983,8 +991,9 @@ hipError_t launch_i8(bool wt, const void* X, const void* W, void* Y, int64_t M, 
                      int64_t ldw, int64_t ldy, hipStream_t stream) {
   const int tiles_m = (int)((M + 127) / 128);
   const int tiles_n = (int)((N + 127) / 128);
-  hipLaunchKernelGGL(wt ? bigemm_i8_kernel<true> : bigemm_i8_kernel<false>, dim3(tiles_m * tiles_n), dim3(kThreads), 0, stream, (const uint8_t*)X,
-                     (const uint8_t*)W, (int32_t*)Y, (int)M, (int)N, (int)K, ldx, ldw, ldy, tiles_m, tiles_n);
+  hipLaunchKernelGGL(wt ? bigemm_i8_kernel<true> : bigemm_i8_kernel<false>, dim3(tiles_m * tiles_n), dim3(kThreads), 0,
+                     stream, (const uint8_t*)X, (const uint8_t*)W, (int32_t*)Y, (int)M, (int)N, (int)K, ldx, ldw, ldy,
+                     tiles_m, tiles_n);
   return hipGetLastError();
 }
 
