@@ -310,9 +310,10 @@ def main():
         XS = torch.from_numpy(e8m0_scales(SEED_X + SCALE_SEED_OFFSET, (4096, K // 32), "var")).to(dev)
         WS = torch.from_numpy(e8m0_scales(SEED_W + SCALE_SEED_OFFSET, (K // 32, N), "var")).to(dev)
         WmT, WST = Wm.t().contiguous(), WS.t().contiguous()   # W and its scales as [N, K] and [N, K/32] rows
-        for kind, fn in (("mxfp8", lambda m: bg.mm(Xm[:m], Wm, XS[:m], WS, out=Y[:m])),
-                         ("mxfp8_w_transposed", lambda m: bg.mm(Xm[:m], WmT.t(), XS[:m], WST.t(), out=Y[:m]))):
-            for m in (1024, 4096):
+        # Layouts interleaved per M, so that both see the same thermal state of the chip.
+        for m in (1024, 4096):
+            for kind, fn in (("mxfp8", lambda m: bg.mm(Xm[:m], Wm, XS[:m], WS, out=Y[:m])),
+                             ("mxfp8_w_transposed", lambda m: bg.mm(Xm[:m], WmT.t(), XS[:m], WST.t(), out=Y[:m]))):
                 for _ in range(5):
                     fn(m)
                 t = _events(torch, stream, lambda i: fn(m), 20)
@@ -334,11 +335,11 @@ def main():
             bg.mm(X, WT.t(), out=Y)
         torch.cuda.synchronize()
         wt_byte_diffs = int((Y.view(torch.int32) != Yfull.view(torch.int32)).sum().item()) if M == 4096 else None
-        for name, fn, peak in (("f16", lambda m: bg.mm(X16[:m], W16, out=Y[:m]), PEAK_BF16_TFLOPS),
-                               ("bf16_out", lambda m: bg.mm(X[:m], W, out=Yb[:m]), PEAK_BF16_TFLOPS),
-                               ("bf16_w_transposed", lambda m: bg.mm(X[:m], WT.t(), out=Y[:m]), PEAK_BF16_TFLOPS),
-                               ("i8", lambda m: bg.mm(Xi[:m], Wi, out=Yi[:m]), PEAK_I8_TOPS)):
-            for m in (1024, 4096):
+        for m in (1024, 4096):
+            for name, fn, peak in (("f16", lambda m: bg.mm(X16[:m], W16, out=Y[:m]), PEAK_BF16_TFLOPS),
+                                   ("bf16_out", lambda m: bg.mm(X[:m], W, out=Yb[:m]), PEAK_BF16_TFLOPS),
+                                   ("bf16_w_transposed", lambda m: bg.mm(X[:m], WT.t(), out=Y[:m]), PEAK_BF16_TFLOPS),
+                                   ("i8", lambda m: bg.mm(Xi[:m], Wi, out=Yi[:m]), PEAK_I8_TOPS)):
                 for _ in range(5):
                     fn(m)
                 t = _events(torch, stream, lambda i: fn(m), 20)
