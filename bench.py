@@ -10,12 +10,13 @@ ABI with inputs resident in HBM. Also reported:
   last-level cache, so W is read from HBM; ``us_warm_llc`` is the same call on
   one buffer set), with achieved algorithmic HBM GB/s and % of the roofline
   bound max(flops / MFMA peak, algorithmic bytes / HBM peak);
-* ``other_types_k4096_n4096``: the MXFP8 kernel (E4M3, K-varying E8M0 scales;
-  also with W and its scales given as [N, K] and [N, K/32] rows),
-  fp16 inputs, bf16 output, bf16 with W given as [N, K] rows, and int8 inputs
-  at M = 1024 and 4096, each against its dense MFMA peak (context, not the
-  metric); ``w_transposed_byte_diffs`` compares the [N, K]-row call at
-  M = 4096 with the headline output bit for bit (must be 0);
+* ``other_types_k4096_n4096``: the MXFP8 kernel (E4M3, K-varying E8M0 scales),
+  fp16 inputs, bf16 output and int8 inputs at M = 1024 and 4096, each against
+  its dense MFMA peak (context, not the metric); for bf16, MXFP8 and int8 also
+  W given as [N, K] rows (MXFP8 scales [N, K/32]), timed in launches
+  alternating with the [K, N] call (median per launch, each launch between
+  its own events); ``w_transposed_byte_diffs`` compares the [N, K]-row bf16
+  call at M = 4096 with the headline output bit for bit (must be 0);
 * ``split_k_context``: the opt-in pinned-chunk split-K handle at small M (cold
   LLC) and on the long-K workload, against the unsplit kernel (context);
 * ``rmsnorm_bf16_context``: the batch-invariant RMSNorm (bf16, D = 4096) against
@@ -62,6 +63,22 @@ def _events(torch, stream, fn, reps):
     e.record(stream)
     e.synchronize()
     return s.elapsed_time(e) / reps  # ms per call
+
+
+def _events_ab(torch, stream, fa, fb, reps):
+    """Launches of fa and fb alternated, each between its own pair of events on the launch stream, so
+    that both see the same clock and thermal state; returns the median ms per call of each."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * reps + 1)]
+    ev[0].record(stream)
+    for i in range(reps):
+        fa(i)
+        ev[2 * i + 1].record(stream)
+        fb(i)
+        ev[2 * i + 2].record(stream)
+    ev[-1].synchronize()
+    ta = sorted(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(reps))
+    tb = sorted(ev[2 * i + 1].elapsed_time(ev[2 * i + 2]) for i in range(reps))
+    return ta[reps // 2], tb[reps // 2]
 
 
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "bigemm_bf16_kernel_m4096_k4096_n4096_traffic.md")
@@ -310,14 +327,16 @@ def main():
         XS = torch.from_numpy(e8m0_scales(SEED_X + SCALE_SEED_OFFSET, (4096, K // 32), "var")).to(dev)
         WS = torch.from_numpy(e8m0_scales(SEED_W + SCALE_SEED_OFFSET, (K // 32, N), "var")).to(dev)
         WmT, WST = Wm.t().contiguous(), WS.t().contiguous()   # W and its scales as [N, K] and [N, K/32] rows
-        # Layouts interleaved per M, so that both see the same thermal state of the chip.
+        # The two W layouts in alternating launches, so that both see the same thermal state of the chip.
         for m in (1024, 4096):
-            for kind, fn in (("mxfp8", lambda m: bg.mm(Xm[:m], Wm, XS[:m], WS, out=Y[:m])),
-                             ("mxfp8_w_transposed", lambda m: bg.mm(Xm[:m], WmT.t(), XS[:m], WST.t(), out=Y[:m]))):
-                for _ in range(5):
-                    fn(m)
-                t = _events(torch, stream, lambda i: fn(m), 20)
-                f = 2.0 * m * N * K
+            fa = lambda i: bg.mm(Xm[:m], Wm, XS[:m], WS, out=Y[:m])
+            fb = lambda i: bg.mm(Xm[:m], WmT.t(), XS[:m], WST.t(), out=Y[:m])
+            for i in range(5):
+                fa(i)
+                fb(i)
+            ta, tb = _events_ab(torch, stream, fa, fb, 20)
+            f = 2.0 * m * N * K
+            for kind, t in (("mxfp8", ta), ("mxfp8_w_transposed", tb)):
                 mx.append({"kind": kind, "M": m, "us": round(t * 1e3, 2), "tflops": round(f / (t * 1e-3) / 1e12, 1),
                            "pct_peak": round(100 * f / (t * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 1)})
         del Xm, Wm, XS, WS, WmT, WST
@@ -335,18 +354,31 @@ def main():
             bg.mm(X, WT.t(), out=Y)
         torch.cuda.synchronize()
         wt_byte_diffs = int((Y.view(torch.int32) != Yfull.view(torch.int32)).sum().item()) if M == 4096 else None
+        WiT = Wi.t().contiguous()
         for m in (1024, 4096):
             for name, fn, peak in (("f16", lambda m: bg.mm(X16[:m], W16, out=Y[:m]), PEAK_BF16_TFLOPS),
-                                   ("bf16_out", lambda m: bg.mm(X[:m], W, out=Yb[:m]), PEAK_BF16_TFLOPS),
-                                   ("bf16_w_transposed", lambda m: bg.mm(X[:m], WT.t(), out=Y[:m]), PEAK_BF16_TFLOPS),
-                                   ("i8", lambda m: bg.mm(Xi[:m], Wi, out=Yi[:m]), PEAK_I8_TOPS)):
+                                   ("bf16_out", lambda m: bg.mm(X[:m], W, out=Yb[:m]), PEAK_BF16_TFLOPS)):
                 for _ in range(5):
                     fn(m)
                 t = _events(torch, stream, lambda i: fn(m), 20)
                 f = 2.0 * m * N * K
                 mx.append({"kind": name, "M": m, "us": round(t * 1e3, 2), "tflops": round(f / (t * 1e-3) / 1e12, 1),
                            "pct_peak": round(100 * f / (t * 1e-3) / 1e12 / peak, 1)})
-        del X16, W16, Xi, Wi, Yi, Yb, WT
+            # each W layout against the other in alternating launches (bf16, int8)
+            for names, fa, fb, peak in ((("bf16", "bf16_w_transposed"), lambda i: bg.mm(X[:m], W, out=Y[:m]),
+                                         lambda i: bg.mm(X[:m], WT.t(), out=Y[:m]), PEAK_BF16_TFLOPS),
+                                        (("i8", "i8_w_transposed"), lambda i: bg.mm(Xi[:m], Wi, out=Yi[:m]),
+                                         lambda i: bg.mm(Xi[:m], WiT.t(), out=Yi[:m]), PEAK_I8_TOPS)):
+                for i in range(5):
+                    fa(i)
+                    fb(i)
+                ta, tb = _events_ab(torch, stream, fa, fb, 20)
+                f = 2.0 * m * N * K
+                for name, t in zip(names, (ta, tb)):
+                    mx.append({"kind": name, "M": m, "us": round(t * 1e3, 2),
+                               "tflops": round(f / (t * 1e-3) / 1e12, 1),
+                               "pct_peak": round(100 * f / (t * 1e-3) / 1e12 / peak, 1)})
+        del X16, W16, Xi, Wi, WiT, Yi, Yb, WT
 
     line = {
         "metric": "TFLOP/s vs M (1-4096) at K=N=4096, % MFMA peak; invariance byte-diffs=0",
