@@ -10,10 +10,11 @@
  * every shape uses. This library is that recipe on CDNA4: one fixed tile
  * configuration per input type, the K blocks walked in ascending order by a
  * single workgroup, one MFMA shape at every M, no atomics, no workspace.
- * The same rules give the other entry points below: an opt-in split-K whose
- * split count follows K only, a batch-invariant RMSNorm, and batch-invariant
- * paged decode attention (a KV-cache write plus attention with a fixed split
- * size); each states its own invariance guarantee.
+ * The same rules give the other entry points below: handles that take W as
+ * [N, K] rows (a linear layer's weight layout) with the same output bytes, an
+ * opt-in split-K whose split count follows K only, a batch-invariant RMSNorm,
+ * and batch-invariant paged decode attention (a KV-cache write plus attention
+ * with a fixed split size); each states its own invariance guarantee.
  *
  * Consequences the caller can rely on for the matrix multiply (per handle,
  * device and library build):
