@@ -35,7 +35,7 @@
 extern "C" {
 #endif
 
-#define BIGEMM_ABI_VERSION 6
+#define BIGEMM_ABI_VERSION 7
 
 /* Exported entry points (the library is built with hidden visibility by default). */
 #if defined(__GNUC__)
@@ -223,7 +223,11 @@ BIGEMM_API bigemm_status bigemm_workspace_size(bigemm_t h, int64_t M, int64_t N,
  * library allocates nothing. The workspace is scratch for the duration of the
  * call on `stream`: calls that share a workspace must be ordered (same stream)
  * or they race. For a handle without split-K this is bigemm_run. Errors as
- * bigemm_run, plus BIGEMM_ERR_ARG for a missing, misaligned or short workspace.
+ * bigemm_run, plus BIGEMM_ERR_ARG when the run splits K (K > k_chunk) and
+ *   - the workspace is missing, misaligned or short, or
+ *   - 128 * N * 4 >= 2^31 (the chunk sums are fp32 rows of N values, addressed
+ *     through 32-bit offsets within a 128-row tile, whatever the output type),
+ *     or N % 4 != 0 (the merge reads four sums at a time).
  */
 BIGEMM_API bigemm_status bigemm_run_ws(bigemm_t h, int64_t M, int64_t N, int64_t K,
                             const void* X, int64_t ldx,
@@ -233,6 +237,20 @@ BIGEMM_API bigemm_status bigemm_run_ws(bigemm_t h, int64_t M, int64_t N, int64_t
                             const void* W_scale, int64_t ldws,
                             void* workspace, uint64_t workspace_bytes,
                             void* stream);
+
+/*
+ * The argument checks of bigemm_run_ws on a split-K handle created from
+ * (desc, k_chunk), W given as [K, N], as a pure host function (no HIP call):
+ * those of bigemm_check_args plus the workspace and size limits listed under
+ * bigemm_run_ws. BIGEMM_ERR_UNSUPPORTED for descriptors that have no split-K
+ * form, BIGEMM_ERR_ARG for a bad k_chunk.
+ */
+BIGEMM_API bigemm_status bigemm_check_args_split_k(const bigemm_desc* desc, int32_t k_chunk,
+                                                   int64_t M, int64_t N, int64_t K,
+                                                   const void* X, int64_t ldx,
+                                                   const void* W, int64_t ldw,
+                                                   const void* Y, int64_t ldy,
+                                                   const void* workspace, uint64_t workspace_bytes);
 
 /*
  * Batch-invariant RMSNorm, the blog's section "batch-invariant RMSNorm":

@@ -22,6 +22,7 @@ __all__ = [
     "bigemm_create", "bigemm_run", "bigemm_destroy", "bigemm_status_str", "bigemm_get_config",
     "bigemm_check_args", "bigemm_abi_version", "mm", "bigemm_create_wt", "bigemm_check_args_wt",
     "bigemm_create_split_k", "bigemm_create_split_k_wt", "bigemm_workspace_size", "bigemm_run_ws",
+    "bigemm_check_args_split_k",
     "bigemm_rmsnorm", "bigemm_rmsnorm_check_args", "rmsnorm",
     "bigemm_kv_layout", "bigemm_kv_cache_write", "bigemm_attn_workspace_size", "bigemm_paged_attention",
     "bigemm_paged_attention_check_args", "kv_cache_write", "paged_attention", "ATTN_SPLIT",
@@ -109,6 +110,9 @@ def load():
         lib.bigemm_create_split_k_wt.argtypes = [ctypes.POINTER(bigemm_desc), i32, ctypes.POINTER(vp)]
         lib.bigemm_workspace_size.restype = ctypes.c_int
         lib.bigemm_workspace_size.argtypes = [vp, i64, i64, i64, ctypes.POINTER(ctypes.c_uint64)]
+        lib.bigemm_check_args_split_k.restype = ctypes.c_int
+        lib.bigemm_check_args_split_k.argtypes = [ctypes.POINTER(bigemm_desc), i32, i64, i64, i64, vp, i64, vp, i64,
+                                                  vp, i64, vp, ctypes.c_uint64]
         lib.bigemm_run_ws.restype = ctypes.c_int
         lib.bigemm_run_ws.argtypes = [vp, i64, i64, i64, vp, i64, vp, i64, vp, i64, vp, i64, vp, i64, vp,
                                       ctypes.c_uint64, vp]
@@ -248,6 +252,15 @@ def bigemm_check_args_wt(x_type: int, w_type: int, y_type: int, scale_block: int
     d = _desc(x_type, w_type, y_type, scale_block)
     return int(load().bigemm_check_args_wt(ctypes.byref(d), M, N, K, X or None, ldx, W or None, ldw,
                                            Y or None, ldy, X_scale or None, ldxs, W_scale or None, ldws))
+
+
+def bigemm_check_args_split_k(x_type: int, w_type: int, y_type: int, k_chunk: int, M: int, N: int, K: int,
+                              X: int, ldx: int, W: int, ldw: int, Y: int, ldy: int, workspace: int = 0,
+                              workspace_bytes: int = 0) -> int:
+    """Argument validation of bigemm_run_ws on a split-K handle (pure host function); returns the status."""
+    d = _desc(x_type, w_type, y_type, 0)
+    return int(load().bigemm_check_args_split_k(ctypes.byref(d), int(k_chunk), M, N, K, X or None, ldx, W or None,
+                                                ldw, Y or None, ldy, workspace or None, int(workspace_bytes)))
 
 
 # ------------------------------------------------------------------ torch wrapper

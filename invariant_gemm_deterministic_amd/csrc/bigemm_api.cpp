@@ -89,6 +89,29 @@ bigemm_status rmsnorm_check(int32_t dtype, int64_t M, int64_t D, const void* X, 
   return BIGEMM_OK;
 }
 
+// Workspace bytes of a split-K run: ceil(K / k_chunk) chunk sums of M x N fp32,
+// or 0 when there is no split (no k_chunk, or a single chunk).
+uint64_t split_need(int32_t k_chunk, int64_t M, int64_t N, int64_t K) {
+  if (k_chunk <= 0 || K <= k_chunk || M <= 0 || N <= 0) return 0;
+  return (uint64_t)((K + k_chunk - 1) / k_chunk) * (uint64_t)M * (uint64_t)N * 4u;
+}
+
+// The limits a split-K run adds to check(): the chunk sums are stored through
+// the partial kernel's 32-bit tile offsets with row stride N (128 rows of N
+// fp32 must stay below 2^31 bytes, whatever the output type), the merge kernel
+// reads four sums at a time (N % 4 == 0, and M * N / 4 threads in its grid),
+// the (chunk, tile) grid must fit in int32, and the workspace must be present,
+// 16-byte aligned and large enough.
+bigemm_status split_check(int32_t k_chunk, int64_t M, int64_t N, int64_t K, const void* ws, uint64_t ws_bytes) {
+  const uint64_t need = split_need(k_chunk, M, N, K);
+  if (need == 0) return BIGEMM_OK;
+  if (128 * N * 4 >= kOffsetLimit || N % 4 != 0) return BIGEMM_ERR_ARG;
+  if ((K + k_chunk - 1) / k_chunk * ((M + 127) / 128) * ((N + 127) / 128) > INT32_MAX) return BIGEMM_ERR_ARG;
+  if (M * (N / 4) > (int64_t)INT32_MAX * 256) return BIGEMM_ERR_ARG;  // merge grid
+  if (!ws || !aligned16(ws) || ws_bytes < need) return BIGEMM_ERR_ARG;
+  return BIGEMM_OK;
+}
+
 // gfx950 check for the current device, done once per device (0 unknown, 1 yes, 2 no).
 std::atomic<int> g_arch_ok[64];
 
@@ -367,12 +390,20 @@ bigemm_status bigemm_create_split_k_wt(const bigemm_desc* desc, int32_t k_chunk,
 
 bigemm_status bigemm_workspace_size(bigemm_t h, int64_t M, int64_t N, int64_t K, uint64_t* bytes) {
   if (!h || !bytes || M < 0 || N < 0 || K < 0) return BIGEMM_ERR_ARG;
-  *bytes = 0;
-  if (h->k_chunk > 0 && K > h->k_chunk) {
-    const uint64_t nsplit = (uint64_t)((K + h->k_chunk - 1) / h->k_chunk);
-    *bytes = nsplit * (uint64_t)M * (uint64_t)N * 4u;
-  }
+  *bytes = split_need(h->k_chunk, M, N, K);
   return BIGEMM_OK;
+}
+
+bigemm_status bigemm_check_args_split_k(const bigemm_desc* desc, int32_t k_chunk, int64_t M, int64_t N, int64_t K,
+                                        const void* X, int64_t ldx, const void* W, int64_t ldw, const void* Y,
+                                        int64_t ldy, const void* workspace, uint64_t workspace_bytes) {
+  if (!desc) return BIGEMM_ERR_ARG;
+  const bigemm::Op op = desc_op(desc);
+  if (op.in != bigemm::kInBf16 && op.in != bigemm::kInF16) return BIGEMM_ERR_UNSUPPORTED;
+  if (k_chunk < bigemm::kTileKBf16 || k_chunk % bigemm::kTileKBf16 != 0) return BIGEMM_ERR_ARG;
+  const bigemm_status st = check(op, M, N, K, X, ldx, W, ldw, Y, ldy, nullptr, 0, nullptr, 0);
+  if (st != BIGEMM_OK || M == 0) return st;
+  return split_check(k_chunk, M, N, K, workspace, workspace_bytes);
 }
 
 bigemm_status bigemm_run_ws(bigemm_t h, int64_t M, int64_t N, int64_t K, const void* X, int64_t ldx,
@@ -382,18 +413,15 @@ bigemm_status bigemm_run_ws(bigemm_t h, int64_t M, int64_t N, int64_t K, const v
   if (!h) return BIGEMM_ERR_ARG;
   const bigemm_status st = check(h->op, M, N, K, X, ldx, W, ldw, Y, ldy, X_scale, ldxs, W_scale, ldws, h->w_trans);
   if (st != BIGEMM_OK || M == 0) return st;
+  const bigemm_status sst = split_check(h->k_chunk, M, N, K, workspace, workspace_bytes);
+  if (sst != BIGEMM_OK) return sst;
   const bigemm_status dv = handle_device_current(h);
   if (dv != BIGEMM_OK) return dv;
-  uint64_t need = 0;
-  bigemm_workspace_size(h, M, N, K, &need);
-  if (need == 0) {  // unsplit handle, or a single chunk: the one fixed kernel
+  if (split_need(h->k_chunk, M, N, K) == 0) {  // unsplit handle, or a single chunk: the one fixed kernel
     const hipError_t e = launch_unsplit(h->op, h->w_trans, M, N, K, X, ldx, W, ldw, Y, ldy, X_scale, ldxs,
                                         W_scale, ldws, (hipStream_t)stream);
     return e == hipSuccess ? BIGEMM_OK : BIGEMM_ERR_DEVICE;
   }
-  if (!workspace || !aligned16(workspace) || workspace_bytes < need) return BIGEMM_ERR_ARG;
-  if ((K + h->k_chunk - 1) / h->k_chunk * ((M + 127) / 128) * ((N + 127) / 128) > INT32_MAX) return BIGEMM_ERR_ARG;
-  if (M * N > (int64_t)INT32_MAX * 4) return BIGEMM_ERR_ARG;  // merge grid
   const hipError_t e = bigemm::launch_bf16_split(h->op, h->w_trans, h->k_chunk, X, W, Y, workspace, M, N, K, ldx,
                                                  ldw, ldy, (hipStream_t)stream);
   return e == hipSuccess ? BIGEMM_OK : BIGEMM_ERR_DEVICE;

@@ -26,7 +26,8 @@ def test_header_declares_the_boundary():
                  "bigemm_create_split_k", "bigemm_workspace_size", "bigemm_run_ws",
                  "bigemm_rmsnorm", "bigemm_rmsnorm_check_args", "bigemm_kv_cache_write",
                  "bigemm_attn_workspace_size", "bigemm_paged_attention", "bigemm_paged_attention_check_args",
-                 "bigemm_create_wt", "bigemm_check_args_wt", "bigemm_create_split_k_wt"):
+                 "bigemm_create_wt", "bigemm_check_args_wt", "bigemm_create_split_k_wt",
+                 "bigemm_check_args_split_k"):
         assert name in fns
 
 
@@ -37,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert bg.bigemm_abi_version() == 6
+    assert bg.bigemm_abi_version() == 7
     for s in range(5):
         assert bg.bigemm_status_str(s)
     assert "unknown" in bg.bigemm_status_str(99)
@@ -258,3 +259,31 @@ def test_bench_refuses_more_than_one_gpu():
                        text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU only" in r.stderr and r.stdout == ""
+
+
+def test_check_args_split_k():
+    """The split-K run's own limits: workspace present, aligned and large enough, and the fp32
+    chunk sums addressable through 32-bit offsets within a 128-row tile (128 * N * 4 < 2^31)
+    whatever the output type; a single chunk (K <= k_chunk) needs no workspace."""
+    BFO = (bg.BIGEMM_BF16, bg.BIGEMM_BF16, bg.BIGEMM_BF16)
+
+    def sk(M, N, K, kc=512, ws=A, wsb=None, desc=(bg.BIGEMM_BF16, bg.BIGEMM_BF16, bg.BIGEMM_F32), ldy=None):
+        need = -(-K // kc) * M * N * 4 if K > kc else 0
+        return bg.bigemm_check_args_split_k(*desc, kc, M, N, K, A, K, A, N, A, N if ldy is None else ldy, ws,
+                                            need if wsb is None else wsb)
+
+    assert sk(64, 4096, 4096) == bg.BIGEMM_OK
+    assert sk(64, 4096, 512, ws=0, wsb=0) == bg.BIGEMM_OK               # one chunk: no workspace needed
+    assert sk(0, 4096, 4096, ws=0, wsb=0) == bg.BIGEMM_OK               # M = 0 is a no-op
+    assert sk(64, 4096, 4096, ws=0) == bg.BIGEMM_ERR_ARG                # missing
+    assert sk(64, 4096, 4096, ws=A + 4) == bg.BIGEMM_ERR_ARG            # misaligned
+    assert sk(64, 4096, 4096, wsb=8 * 64 * 4096 * 4 - 1) == bg.BIGEMM_ERR_ARG  # one byte short
+    assert sk(64, 4096, 4096, kc=100) == bg.BIGEMM_ERR_ARG              # k_chunk not a multiple of 64
+    assert bg.bigemm_check_args_split_k(*MX[:3], 512, 1, 64, 1024, A, 1024, A, 64, A, 64, A, 1 << 20) == \
+        bg.BIGEMM_ERR_UNSUPPORTED
+    # 128 * N * 4 just below and at 2^31: with a bf16 output the caller's ldy alone would allow both
+    n_ok, n_bad = (1 << 22) - 8, 1 << 22
+    assert sk(1, n_ok, 1024, desc=BFO) == bg.BIGEMM_OK
+    assert sk(1, n_bad, 1024, desc=BFO) == bg.BIGEMM_ERR_ARG
+    assert chk((bg.BIGEMM_BF16, bg.BIGEMM_BF16, bg.BIGEMM_BF16, 0), 1, n_bad, 1024) == bg.BIGEMM_OK
+    assert sk(1, n_bad, 512, desc=BFO, ws=0, wsb=0) == bg.BIGEMM_OK    # unsplit: the ordinary limits only
