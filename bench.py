@@ -29,8 +29,18 @@ ABI with inputs resident in HBM. Also reported:
   same row of the M = 4096 result (must be 0);
 * ``roofline``: the kernel's algorithmic flops per launch over its average
   launch time (HIP events on the launch stream) against the datasheet peak;
-* ``cpu_baseline``: the CPU oracle timed on a bounded sample of rows of the
-  same workload (rank 0, one GPU only).
+* ``cpu_baseline``: the CPU oracle timed on the same workload (rank 0, one
+  GPU only), and ``cpu_oracle_m_sweep`` at M = 1, 64, 1024, 4096.
+
+Timing method (``timing`` in the line), the same for every GPU figure: each
+point is first warmed for a fixed time (launches back to back for at least
+WARM_S seconds, whatever --warmup says, so that the engine clock has settled
+at its sustained, power-limited value), then timed as back-to-back blocks of
+launches, each block between two HIP events recorded on the launch stream with
+no host synchronisation between blocks; a point's time per call is the median
+over its blocks. The headline times exactly --steps launches that way (one
+bracketed region, split into blocks), and ``value`` is computed from the whole
+region (total time / steps); the median block is reported beside it.
 """
 from __future__ import annotations
 
@@ -54,25 +64,54 @@ M_SWEEP = [1, 16, 64, 128, 256, 512, 1024, 2048, 4096]
 K = N = 4096
 
 
-def _events(torch, stream, fn, reps):
-    s = torch.cuda.Event(enable_timing=True)
-    e = torch.cuda.Event(enable_timing=True)
-    s.record(stream)
-    for i in range(reps):
-        fn(i)
-    e.record(stream)
-    e.synchronize()
-    return s.elapsed_time(e) / reps  # ms per call
+WARM_S = 0.3          # seconds of back-to-back launches before any point is timed
+BLOCKS = 5            # timed blocks per point (median taken)
 
 
-def _events_ab(torch, stream, fa, fb, rounds=4, block=10):
-    """fa and fb timed in alternating blocks of back-to-back launches (each block between two events on
-    the launch stream, as _events), so that both see the same clock and thermal state; returns the
-    median over the rounds of each one's ms per call."""
+def _warm(torch, fn, seconds=WARM_S):
+    """Launch fn back to back for at least `seconds` (synchronising every 20 launches)."""
+    t0 = time.perf_counter()
+    i = 0
+    while True:
+        for _ in range(20):
+            fn(i)
+            i += 1
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            return
+
+
+def _blocks(torch, stream, fn, reps, blocks=BLOCKS):
+    """`blocks` back-to-back blocks of `reps` launches, each between two events on the launch
+    stream (no host synchronisation between blocks). Returns (median ms per call over the
+    blocks, total ms of the whole region, number of launches)."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(blocks + 1)]
+    ev[0].record(stream)
+    i = 0
+    for b in range(blocks):
+        for _ in range(reps):
+            fn(i)
+            i += 1
+        ev[b + 1].record(stream)
+    ev[-1].synchronize()
+    per = sorted(ev[b].elapsed_time(ev[b + 1]) / reps for b in range(blocks))
+    return per[blocks // 2], ev[0].elapsed_time(ev[-1]), blocks * reps
+
+
+def _time_point(torch, stream, fn, reps, warm_s=WARM_S):
+    """One figure of the bench: warm for warm_s seconds, then the median of BLOCKS blocks."""
+    _warm(torch, fn, warm_s)
+    return _blocks(torch, stream, fn, reps)[0]
+
+
+def _time_ab(torch, stream, fa, fb, reps=10, rounds=BLOCKS):
+    """fa and fb in alternating blocks (same clock and thermal state for both), after warming
+    both; returns the median ms per call of each."""
+    _warm(torch, lambda i: (fa(i), fb(i)))
     ta, tb = [], []
     for _ in range(rounds):
-        ta.append(_events(torch, stream, fa, block))
-        tb.append(_events(torch, stream, fb, block))
+        ta.append(_blocks(torch, stream, fa, reps, 1)[0])
+        tb.append(_blocks(torch, stream, fb, reps, 1)[0])
     return sorted(ta)[rounds // 2], sorted(tb)[rounds // 2]
 
 
@@ -95,22 +134,41 @@ def measured_traffic():
     return int(float(vals["traffic_bytes_per_launch"]))
 
 
-def cpu_baseline(X, W, target_s: float = 15.0):
-    """The oracle (fp64, OpenMP) timed on a bounded sample of rows of the workload."""
+def _cpu_model() -> str:
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_oracle_sweep(X, W, ms=(1, 64, 1024, 4096)):
+    """The oracle (fp64 accumulate, OpenMP over rows, as built) on the first M rows of the
+    workload at each M: median of three runs below M = 4096, one run at M = 4096."""
     import oracle
     threads = oracle.set_threads(0)
-    probe_rows = 32
-    t0 = time.perf_counter()
-    oracle.gemm_bf16(X[:probe_rows], W, want_s=False)
-    dt = time.perf_counter() - t0
-    rows = int(min(X.shape[0], max(probe_rows, probe_rows * target_s / max(dt, 1e-6))))
-    t0 = time.perf_counter()
-    oracle.gemm_bf16(X[:rows], W, want_s=False)
-    dt = time.perf_counter() - t0
-    flops = 2.0 * rows * W.shape[0] * W.shape[1]
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{rows} of {X.shape[0]} rows of the M=4096 K=N=4096 bf16 workload "
-                      f"({flops / 1e9:.1f} GFLOP in {dt:.1f} s, fp64 accumulate)"}
+    out = []
+    for m in ms:
+        ts = []
+        for _ in range(1 if m >= 4096 else 3):
+            t0 = time.perf_counter()
+            oracle.gemm_bf16(X[:m], W, want_s=False)
+            ts.append(time.perf_counter() - t0)
+        dt = sorted(ts)[len(ts) // 2]
+        f = 2.0 * m * W.shape[0] * W.shape[1]
+        out.append({"M": m, "s": round(dt, 4), "gflops": round(f / dt / 1e9, 2)})
+    return out, threads
+
+
+def cpu_baseline(sweep, threads, N, K):
+    """The headline workload (M = 4096) on the oracle, from the sweep's last point."""
+    last = sweep[-1]
+    f = 2.0 * last["M"] * N * K
+    return {"value": round(f / last["s"] / 1e12, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"the whole M=4096 K=N=4096 bf16 workload, all rows ({f / 1e9:.1f} GFLOP of fp64 "
+                      f"accumulation in {last['s']:.1f} s on {threads} threads of {_cpu_model()})"}
 
 
 def cpu_baseline_one_thread(X, W, rows: int = 16):
@@ -170,13 +228,18 @@ def main():
     M = args.m
     assert 1 <= M <= 4096
     Xm, Ym = X[:M], Y[:M]
-    for _ in range(args.warmup):
-        bg.mm(Xm, W, out=Ym)
+    head = lambda i: bg.mm(Xm, W, out=Ym)
+    for i in range(args.warmup):
+        head(i)
+    _warm(torch, head)                     # the sustained clock, whatever --warmup is
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ms = _events(torch, stream, lambda i: bg.mm(Xm, W, out=Ym), args.steps)
+    nblk = BLOCKS if args.steps % BLOCKS == 0 and args.steps >= BLOCKS else 1
+    med_ms, total_ms, n = _blocks(torch, stream, head, args.steps // nblk, nblk)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    assert n == args.steps
+    ms = total_ms / args.steps
     flops = 2.0 * M * N * K
     tflops = flops / (ms * 1e-3) / 1e12
     Yfull = Y.clone()
@@ -192,10 +255,8 @@ def main():
             Ws = [W] + [W.clone() for _ in range(nsets - 1)]
             Xs = [X[:m]] + [X[:m].clone() for _ in range(nsets - 1)]
             Ys = [torch.empty((m, N), dtype=torch.float32, device=dev) for _ in range(nsets)]
-            for i in range(2 * nsets):
-                bg.mm(Xs[i % nsets], Ws[i % nsets], out=Ys[i % nsets])
             reps = max(20, 2 * nsets)
-            t = _events(torch, stream, lambda i: bg.mm(Xs[i % nsets], Ws[i % nsets], out=Ys[i % nsets]), reps)
+            t = _time_point(torch, stream, lambda i: bg.mm(Xs[i % nsets], Ws[i % nsets], out=Ys[i % nsets]), reps)
             torch.cuda.synchronize()
             if M == 4096:
                 for y in Ys:
@@ -211,9 +272,7 @@ def main():
                      "cold_llc": nsets > 1}
             if nsets > 1:
                 # the same call with one buffer set, W warm in the last-level cache
-                for _ in range(3):
-                    bg.mm(Xs[0], Ws[0], out=Ys[0])
-                tw = _events(torch, stream, lambda i: bg.mm(Xs[0], Ws[0], out=Ys[0]), 20)
+                tw = _time_point(torch, stream, lambda i: bg.mm(Xs[0], Ws[0], out=Ys[0]), 20, 0.1)
                 entry["us_warm_llc"] = round(tw * 1e3, 2)
             sweep.append(entry)
             del Ws, Xs, Ys
@@ -234,26 +293,32 @@ def main():
             Ys = [torch.empty((m, N), dtype=torch.float32, device=dev) for _ in range(nsets)]
             ws = torch.empty(bg.bigemm_workspace_size(bg._handle("bf16", 0, bg.BIGEMM_F32, kc), m, N, K),
                              dtype=torch.uint8, device=dev)
-            for i in range(2 * nsets):
-                bg.mm(X[:m], Ws[i % nsets], out=Ys[i % nsets], k_chunk=kc, workspace=ws)
-            t = _events(torch, stream, lambda i: bg.mm(X[:m], Ws[i % nsets], out=Ys[i % nsets], k_chunk=kc,
-                                                       workspace=ws), max(20, 2 * nsets))
+            xm = X[:m]
+            t = _time_point(torch, stream, lambda i: bg.mm(xm, Ws[i % nsets], out=Ys[i % nsets], k_chunk=kc,
+                                                           workspace=ws), max(20, 2 * nsets), 0.1)
             f = 2.0 * m * N * K
             byts = 2 * m * K + 2 * K * N + 4 * m * N
+            t_roof = max(f / (PEAK_BF16_TFLOPS * 1e12), byts / (PEAK_HBM_GBS * 1e9))
             split.append({"M": m, "K": K, "N": N, "k_chunk": kc, "us": round(t * 1e3, 2),
                           "tflops": round(f / (t * 1e-3) / 1e12, 1),
-                          "hbm_gbs_algorithmic": round(byts / (t * 1e-3) / 1e9, 0), "cold_llc": True})
+                          "hbm_gbs_algorithmic": round(byts / (t * 1e-3) / 1e9, 0),
+                          "pct_roofline": round(100 * t_roof / (t * 1e-3), 1), "cold_llc": True})
             del Ws, Ys, ws
         XL = torch.from_numpy(normal_bf16(SEED_X, (1024, 16384)).view(np.int16)).to(dev)
         WL = torch.from_numpy(normal_bf16(SEED_W, (16384, 1024)).view(np.int16)).to(dev)
         YL = torch.empty((1024, 1024), dtype=torch.float32, device=dev)
+        wsl = torch.empty(bg.bigemm_workspace_size(bg._handle("bf16", 0, bg.BIGEMM_F32, 2048), 1024, 1024, 16384),
+                          dtype=torch.uint8, device=dev)
         for kcl in (None, 2048):
-            for _ in range(3):
-                bg.mm(XL, WL, out=YL, k_chunk=kcl)
-            t = _events(torch, stream, lambda i: bg.mm(XL, WL, out=YL, k_chunk=kcl), 20)
+            t = _time_point(torch, stream, lambda i: bg.mm(XL, WL, out=YL, k_chunk=kcl, workspace=wsl if kcl else None),
+                            20, 0.1)
+            f = 2.0 * 1024 * 16384 * 1024
+            byts = 2 * 1024 * 16384 * 2 + 4 * 1024 * 1024
+            t_roof = max(f / (PEAK_BF16_TFLOPS * 1e12), byts / (PEAK_HBM_GBS * 1e9))
             split.append({"M": 1024, "K": 16384, "N": 1024, "k_chunk": kcl, "us": round(t * 1e3, 2),
-                          "tflops": round(2.0 * 1024 * 16384 * 1024 / (t * 1e-3) / 1e12, 1)})
-        del XL, WL, YL
+                          "tflops": round(f / (t * 1e-3) / 1e12, 1),
+                          "pct_roofline": round(100 * t_roof / (t * 1e-3), 1)})
+        del XL, WL, YL, wsl
         torch.cuda.empty_cache()
 
     # ------------------------------------------------ RMSNorm (context)
@@ -266,9 +331,7 @@ def main():
         for m in (1, 128, 4096, 16384):
             XN = torch.from_numpy(normal_bf16(SEED_X + 1, (m, D)).view(np.int16)).to(dev)
             YN = torch.empty_like(XN)
-            for _ in range(3):
-                bg.rmsnorm(XN, G, 1e-6, out=YN)
-            t = _events(torch, stream, lambda i: bg.rmsnorm(XN, G, 1e-6, out=YN), 50)
+            t = _time_point(torch, stream, lambda i: bg.rmsnorm(XN, G, 1e-6, out=YN), 50, 0.1)
             byts = 4 * m * D + 2 * D
             norm.append({"M": m, "D": D, "us": round(t * 1e3, 2), "gbs_algorithmic": round(byts / (t * 1e-3) / 1e9, 0),
                          "pct_hbm_peak": round(100 * byts / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 1)})
@@ -302,9 +365,7 @@ def main():
             def call(i):
                 bg.paged_attention(q, kc, vc, bt, seqs, poss, max_context=L, out=o, workspace=wsa)
 
-            for i in range(3):
-                call(i)
-            t = _events(torch, stream, call, 20)
+            t = _time_point(torch, stream, call, 20, 0.1)
             byts = 4 * B * L * Hkv * D + 2 * B * Hq * D + 4 * B * Hq * D + 2 * need
             attn.append({"B": B, "context": L, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "us": round(t * 1e3, 2),
                          "gbs_algorithmic": round(byts / (t * 1e-3) / 1e9, 0),
@@ -328,10 +389,7 @@ def main():
             xm, xs, ym = Xm[:m], XS[:m], Y[:m]   # views made once: the timed calls do no slicing on the host
             fa = lambda i: bg.mm(xm, Wm, xs, WS, out=ym)
             fb = lambda i: bg.mm(xm, wmt, xs, wst, out=ym)
-            for i in range(5):
-                fa(i)
-                fb(i)
-            ta, tb = _events_ab(torch, stream, fa, fb)
+            ta, tb = _time_ab(torch, stream, fa, fb)
             f = 2.0 * m * N * K
             for kind, t in (("mxfp8", ta), ("mxfp8_w_transposed", tb)):
                 mx.append({"kind": kind, "M": m, "us": round(t * 1e3, 2), "tflops": round(f / (t * 1e-3) / 1e12, 1),
@@ -357,9 +415,7 @@ def main():
             x16, xb, xi, ym, yb, yi = X16[:m], X[:m], Xi[:m], Y[:m], Yb[:m], Yi[:m]
             for name, fn, peak in (("f16", lambda i: bg.mm(x16, W16, out=ym), PEAK_BF16_TFLOPS),
                                    ("bf16_out", lambda i: bg.mm(xb, W, out=yb), PEAK_BF16_TFLOPS)):
-                for i in range(5):
-                    fn(i)
-                t = _events(torch, stream, fn, 20)
+                t = _time_point(torch, stream, fn, 20)
                 f = 2.0 * m * N * K
                 mx.append({"kind": name, "M": m, "us": round(t * 1e3, 2), "tflops": round(f / (t * 1e-3) / 1e12, 1),
                            "pct_peak": round(100 * f / (t * 1e-3) / 1e12 / peak, 1)})
@@ -368,10 +424,7 @@ def main():
                                          lambda i: bg.mm(xb, wt, out=ym), PEAK_BF16_TFLOPS),
                                         (("i8", "i8_w_transposed"), lambda i: bg.mm(xi, Wi, out=yi),
                                          lambda i: bg.mm(xi, wit, out=yi), PEAK_I8_TOPS)):
-                for i in range(5):
-                    fa(i)
-                    fb(i)
-                ta, tb = _events_ab(torch, stream, fa, fb)
+                ta, tb = _time_ab(torch, stream, fa, fb)
                 f = 2.0 * m * N * K
                 for name, t in zip(names, (ta, tb)):
                     mx.append({"kind": name, "M": m, "us": round(t * 1e3, 2),
@@ -387,6 +440,10 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 5),
+        "ms_per_step_median_block": round(med_ms, 5),
+        "timing": f"{WARM_S:g} s of back-to-back launches, then the timed launches in back-to-back blocks "
+                  f"between HIP events on the launch stream; headline: {args.steps} launches in {nblk} "
+                  f"block(s), value = total / steps; every other point: median of {BLOCKS} blocks",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -409,7 +466,9 @@ def main():
         "timed_wall_s": round(wall, 3),
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(Xh, Wh)
+        sweep_cpu, threads = cpu_oracle_sweep(Xh, Wh)
+        line["cpu_baseline"] = cpu_baseline(sweep_cpu, threads, N, K)
+        line["cpu_oracle_m_sweep"] = {"cores": threads, "cpu": _cpu_model(), "k": K, "n": N, "points": sweep_cpu}
         line["cpu_baseline_one_thread"] = cpu_baseline_one_thread(Xh, Wh)
     print(json.dumps(line), flush=True)
 

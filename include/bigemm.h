@@ -117,11 +117,21 @@ BIGEMM_API bigemm_status bigemm_create(const bigemm_desc* desc, bigemm_t* out);
  * Requirements (violations return BIGEMM_ERR_ARG synchronously; nothing is
  * launched and Y is untouched):
  *   M >= 0, N >= 1, K >= 1; M == 0 is a successful no-op;
- *   bf16, fp16: K % 8 == 0, N % 8 == 0;  MXFP8: K % 32 == 0, N % 16 == 0;
+ *   bf16, fp16: any K and N;  MXFP8: K % 32 == 0, N % 16 == 0;
  *   int8: K % 16 == 0, N % 16 == 0;
  *   X, W, Y non-NULL when M > 0, 16-byte aligned; ldx, ldw, ldy such that
  *   every row starts 16-byte aligned (ldx, ldw, ldy times the element size
- *   multiples of 16);
+ *   multiples of 16). The operand tiles move in 16-byte pieces, and this
+ *   alignment is the one rule that keeps every piece inside its row; a
+ *   caller whose K (or N) leaves rows of another length pads the rows (the
+ *   padding values are never used) rather than the library picking a second
+ *   load path by layout;
+ *   bf16, fp16 with K % 8 != 0 (or N % 8 != 0): the last 16-byte piece of a
+ *   row of X (of W) also covers up to 7 padding elements past K (past N).
+ *   Those are read, so the padding must be readable memory (it always is
+ *   within a row of ld elements), and never used: X values past K are set to
+ *   zero before the multiply (W rows past K are never read), and W columns
+ *   past N reach only output columns that are not stored;
  *   MXFP8: X_scale, W_scale non-NULL (no alignment requirement);
  *   other types: X_scale and W_scale NULL;
  *   128 * ldx, 128 * ldw, 128 * ldy times the element size below 2^31.
@@ -191,7 +201,8 @@ BIGEMM_API bigemm_status bigemm_create_split_k_wt(const bigemm_desc* desc, int32
  * a bigemm_create handle given the same logical W as [K, N]. Only the staging
  * of W's tile and scales differs.
  * Run it with bigemm_run or bigemm_run_ws (no workspace). The requirements of
- * bigemm_run hold with ldw >= K in place of ldw >= N and, for MXFP8,
+ * bigemm_run hold with ldw >= K in place of ldw >= N (for bf16 / fp16 with
+ * K % 8 != 0 the padding past K of W's rows is read and zeroed like X's) and, for MXFP8,
  * ldws >= K/32 in place of ldws >= N and 128 * ldws below 2^31. Devices other
  * than gfx950 return BIGEMM_ERR_UNSUPPORTED. bigemm_create_split_k_wt is its
  * split-K form (bf16 and fp16).
@@ -226,8 +237,7 @@ BIGEMM_API bigemm_status bigemm_workspace_size(bigemm_t h, int64_t M, int64_t N,
  * bigemm_run, plus BIGEMM_ERR_ARG when the run splits K (K > k_chunk) and
  *   - the workspace is missing, misaligned or short, or
  *   - 128 * N * 4 >= 2^31 (the chunk sums are fp32 rows of N values, addressed
- *     through 32-bit offsets within a 128-row tile, whatever the output type),
- *     or N % 4 != 0 (the merge reads four sums at a time).
+ *     through 32-bit offsets within a 128-row tile, whatever the output type).
  */
 BIGEMM_API bigemm_status bigemm_run_ws(bigemm_t h, int64_t M, int64_t N, int64_t K,
                             const void* X, int64_t ldx,

@@ -295,6 +295,16 @@ def _ld(t) -> int:
     return int(t.stride(0)) if t.shape[0] > 1 else int(t.shape[1])
 
 
+def _ld_rows(t) -> int:
+    """Leading dimension of an X, W or Y operand. A single row's stride is arbitrary in torch and
+    only that row is ever addressed, so it is given as the row width rounded up to whole
+    16-byte units (the library's row-alignment rule then holds for any width)."""
+    if t.shape[0] > 1:
+        return int(t.stride(0))
+    per = 16 // t.element_size()
+    return -(-int(t.shape[1]) // per) * per
+
+
 def mm(x, w, x_scale=None, w_scale=None, out=None, stream=None, out_dtype=None, k_chunk=None,
        workspace=None):
     """Y = X W on the GPU through libbigemm.
@@ -356,12 +366,15 @@ def mm(x, w, x_scale=None, w_scale=None, out=None, stream=None, out_dtype=None, 
         raise ValueError(f"unsupported output dtype {out_dtype}")
     dev = x.device.index if x.device.index is not None else torch.cuda.current_device()
     if out is None:
-        out = torch.empty((M, N), dtype=out_dtype, device=x.device)
+        # rows start 16-byte aligned: for a width that leaves them short, allocate padded rows
+        per = 16 // torch.empty((), dtype=out_dtype).element_size()
+        ldo = -(-N // per) * per
+        out = torch.empty((M, ldo), dtype=out_dtype, device=x.device)[:, :N]
     if tuple(out.shape) != (M, N) or (N > 1 and out.stride(1) != 1):
         raise ValueError("out must be [M, N] with contiguous rows")
     if stream is None:
         stream = torch.cuda.current_stream(x.device).cuda_stream
-    ldw = _ld(w.t()) if wt else _ld(w)
+    ldw = _ld_rows(w.t()) if wt else _ld_rows(w)
     # The handle belongs to x's device, and the library runs a handle only on its own device.
     with torch.cuda.device(dev):
         if k_chunk:
@@ -372,8 +385,8 @@ def mm(x, w, x_scale=None, w_scale=None, out=None, stream=None, out_dtype=None, 
             if workspace is None:
                 workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
             ws_bytes = workspace.numel() * workspace.element_size()
-            bigemm_run_ws(h, M, N, K, x.data_ptr(), _ld(x), w.data_ptr(), ldw, out.data_ptr(), _ld(out),
-                          0, 0, 0, 0, workspace.data_ptr(), ws_bytes, stream)
+            bigemm_run_ws(h, M, N, K, x.data_ptr(), _ld_rows(x), w.data_ptr(), ldw, out.data_ptr(),
+                          _ld_rows(out), 0, 0, 0, 0, workspace.data_ptr(), ws_bytes, stream)
             return out
         h = _handle(kind, dev, ytypes[out_dtype], 0, wt)  # raises BigemmError for a combination not provided
         if mx:
@@ -384,10 +397,10 @@ def mm(x, w, x_scale=None, w_scale=None, out=None, stream=None, out_dtype=None, 
                 if not t.is_cuda or t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
                     raise ValueError("scales must be 2-D CUDA tensors with contiguous rows "
                                      "(w_scale in the same layout as w)")
-            bigemm_run(h, M, N, K, x.data_ptr(), _ld(x), w.data_ptr(), ldw, out.data_ptr(), _ld(out),
+            bigemm_run(h, M, N, K, x.data_ptr(), _ld_rows(x), w.data_ptr(), ldw, out.data_ptr(), _ld_rows(out),
                        x_scale.data_ptr(), _ld(x_scale), w_scale.data_ptr(), _ld(ws), stream)
         else:
-            bigemm_run(h, M, N, K, x.data_ptr(), _ld(x), w.data_ptr(), ldw, out.data_ptr(), _ld(out),
+            bigemm_run(h, M, N, K, x.data_ptr(), _ld_rows(x), w.data_ptr(), ldw, out.data_ptr(), _ld_rows(out),
                        0, 0, 0, 0, stream)
     return out
 

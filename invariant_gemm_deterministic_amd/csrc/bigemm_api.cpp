@@ -58,7 +58,7 @@ bigemm_status check(bigemm::Op op, int64_t M, int64_t N, int64_t K, const void* 
   const bool mx = op.in == bigemm::kInMx;
   const int64_t es = (op.in == bigemm::kInBf16 || op.in == bigemm::kInF16) ? 2 : 1;
   const int64_t eo = op.out == BIGEMM_BF16 ? 2 : 4;
-  if (es == 2 && (K % 8 != 0 || N % 8 != 0)) return BIGEMM_ERR_ARG;
+  // bf16 / fp16: any K and N; only whole rows must be 16-byte aligned (below).
   if (mx && (K % 32 != 0 || N % 16 != 0)) return BIGEMM_ERR_ARG;
   if (op.in == bigemm::kInI8 && (K % 16 != 0 || N % 16 != 0)) return BIGEMM_ERR_ARG;
   if (ldx < K || ldw < (wt ? K : N) || ldy < N) return BIGEMM_ERR_ARG;
@@ -98,16 +98,15 @@ uint64_t split_need(int32_t k_chunk, int64_t M, int64_t N, int64_t K) {
 
 // The limits a split-K run adds to check(): the chunk sums are stored through
 // the partial kernel's 32-bit tile offsets with row stride N (128 rows of N
-// fp32 must stay below 2^31 bytes, whatever the output type), the merge kernel
-// reads four sums at a time (N % 4 == 0, and M * N / 4 threads in its grid),
-// the (chunk, tile) grid must fit in int32, and the workspace must be present,
-// 16-byte aligned and large enough.
+// fp32 must stay below 2^31 bytes, whatever the output type), the merge grid
+// (at most one thread per output) and the (chunk, tile) grid must fit, and the
+// workspace must be present, 16-byte aligned and large enough.
 bigemm_status split_check(int32_t k_chunk, int64_t M, int64_t N, int64_t K, const void* ws, uint64_t ws_bytes) {
   const uint64_t need = split_need(k_chunk, M, N, K);
   if (need == 0) return BIGEMM_OK;
-  if (128 * N * 4 >= kOffsetLimit || N % 4 != 0) return BIGEMM_ERR_ARG;
+  if (128 * N * 4 >= kOffsetLimit) return BIGEMM_ERR_ARG;
   if ((K + k_chunk - 1) / k_chunk * ((M + 127) / 128) * ((N + 127) / 128) > INT32_MAX) return BIGEMM_ERR_ARG;
-  if (M * (N / 4) > (int64_t)INT32_MAX * 256) return BIGEMM_ERR_ARG;  // merge grid
+  if (M * N > (int64_t)INT32_MAX * 256) return BIGEMM_ERR_ARG;  // merge grid (one thread per output at most)
   if (!ws || !aligned16(ws) || ws_bytes < need) return BIGEMM_ERR_ARG;
   return BIGEMM_OK;
 }

@@ -172,7 +172,13 @@ constexpr int kUnrollBf16 = 8 * kStagesBf16;
 // like the X tile (128 rows of K-contiguous bytes) and the B fragments are
 // plain 16-byte reads; the MFMA chain and its operands are the same as for
 // W [K, N], so the output bytes are too.
-template <bool kF16, bool kOutBf16, bool kSplit, bool kWT = false>
+// kKTail: K is not a multiple of 8 (chosen from K alone). The 16-byte chunk of
+// an X row (and of a W^T row) that holds the last K values also holds up to 7
+// values past K, from the row's padding. W rows past K load as zero, but a
+// padding value may be an infinity or a NaN, and 0 * NaN is NaN, so those
+// fragment elements are set to +0 before they reach the MFMA. Every element
+// then accumulates the same products as with a zero-filled tail.
+template <bool kF16, bool kOutBf16, bool kSplit, bool kWT = false, bool kKTail = false>
 __global__ __launch_bounds__(kThreadsBf16, 1)
 void bigemm_bf16_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
                         void* __restrict__ Y, int M, int N, int K,
@@ -300,12 +306,25 @@ void bigemm_bf16_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
     issue(kb + kStagesBf16 - 1, refill);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
+      // kKTail: keep the fragment's K values below K. The lane holds the 8
+      // values from K offset kk*16 + 8*(lane/32) of this block; dword d holds
+      // values 2d (low half) and 2d + 1. Full blocks keep everything.
+      i32x4 kmask = i32x4{-1, -1, -1, -1};
+      if constexpr (kKTail) {
+        const int n = Kr - kb * kBkBf16 - (kk * 16 + 8 * (lane >> 5));  // values of the 8 below K
+#pragma unroll
+        for (int d = 0; d < 4; ++d) kmask[d] = n >= 2 * d + 2 ? -1 : (n == 2 * d + 1 ? 0xFFFF : 0);
+      }
       i32x4 a[2];
 #pragma unroll
-      for (int f = 0; f < 2; ++f) a[f] = *LDS(const i32x4, st + a_addr[f][kk]);
+      for (int f = 0; f < 2; ++f) {
+        a[f] = *LDS(const i32x4, st + a_addr[f][kk]);
+        if constexpr (kKTail) a[f] &= kmask;
+      }
       i32x4 b;
       if constexpr (kWT) {
         b = *LDS(const i32x4, st + bt_addr[kk]);
+        if constexpr (kKTail) b &= kmask;
       } else {
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS(i16x4, st + b_addr[kk][0]));
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS(i16x4, st + b_addr[kk][1]));
@@ -889,37 +908,53 @@ void bigemm_i8_kernel(const uint8_t* __restrict__ X, const uint8_t* __restrict__
 // ------------------------------------------------------------- split-K merge
 //
 // Y[i, j] = P[0][i, j] + P[1][i, j] + ... + P[S-1][i, j], added in ascending
-// chunk order in fp32 (then rounded once to bf16 for a bf16 output). One
-// thread per four consecutive outputs of a row; P is [S][M][N] fp32.
-template <bool kOutBf16>
+// chunk order in fp32 (then rounded once to bf16 for a bf16 output). P is
+// [S][M][N] fp32. kVec4 (N a multiple of 4): one thread per four consecutive
+// outputs of a row, 16-byte loads; otherwise one thread per output. The sums
+// and their order are the same either way.
+template <bool kOutBf16, bool kVec4>
 __global__ __launch_bounds__(256)
 void bigemm_split_merge_kernel(const float* __restrict__ P, void* __restrict__ Y, int M, int N, int64_t ldy,
                                int nsplit, int64_t split_stride) {
-  const int nq = N / 4;
-  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (q >= (int64_t)M * nq) return;
-  const int i = (int)(q / nq);
-  const int j = (int)(q - (int64_t)i * nq) * 4;
-  const float* p = P + (int64_t)i * N + j;
-  float4 acc = *(const float4*)p;
-  for (int s = 1; s < nsplit; ++s) {
-    const float4 v = *(const float4*)(p + s * split_stride);
-    acc.x += v.x;
-    acc.y += v.y;
-    acc.z += v.z;
-    acc.w += v.w;
-  }
-  if (kOutBf16) {
-    const uint32_t b0 = f32_to_bf16_rne(__builtin_bit_cast(uint32_t, acc.x));
-    const uint32_t b1 = f32_to_bf16_rne(__builtin_bit_cast(uint32_t, acc.y));
-    const uint32_t b2 = f32_to_bf16_rne(__builtin_bit_cast(uint32_t, acc.z));
-    const uint32_t b3 = f32_to_bf16_rne(__builtin_bit_cast(uint32_t, acc.w));
-    uint2 packed;
-    packed.x = b0 | (b1 << 16);
-    packed.y = b2 | (b3 << 16);
-    *(uint2*)((uint16_t*)Y + (int64_t)i * ldy + j) = packed;
+  if constexpr (kVec4) {
+    const int nq = N / 4;
+    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (q >= (int64_t)M * nq) return;
+    const int i = (int)(q / nq);
+    const int j = (int)(q - (int64_t)i * nq) * 4;
+    const float* p = P + (int64_t)i * N + j;
+    float4 acc = *(const float4*)p;
+    for (int s = 1; s < nsplit; ++s) {
+      const float4 v = *(const float4*)(p + s * split_stride);
+      acc.x += v.x;
+      acc.y += v.y;
+      acc.z += v.z;
+      acc.w += v.w;
+    }
+    if (kOutBf16) {
+      const uint32_t b0 = f32_to_bf16_rne(__builtin_bit_cast(uint32_t, acc.x));
+      const uint32_t b1 = f32_to_bf16_rne(__builtin_bit_cast(uint32_t, acc.y));
+      const uint32_t b2 = f32_to_bf16_rne(__builtin_bit_cast(uint32_t, acc.z));
+      const uint32_t b3 = f32_to_bf16_rne(__builtin_bit_cast(uint32_t, acc.w));
+      uint2 packed;
+      packed.x = b0 | (b1 << 16);
+      packed.y = b2 | (b3 << 16);
+      *(uint2*)((uint16_t*)Y + (int64_t)i * ldy + j) = packed;
+    } else {
+      *(float4*)((float*)Y + (int64_t)i * ldy + j) = acc;
+    }
   } else {
-    *(float4*)((float*)Y + (int64_t)i * ldy + j) = acc;
+    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (q >= (int64_t)M * N) return;
+    const int i = (int)(q / N);
+    const int j = (int)(q - (int64_t)i * N);
+    const float* p = P + (int64_t)i * N + j;
+    float acc = *p;
+    for (int s = 1; s < nsplit; ++s) acc += p[s * split_stride];
+    if (kOutBf16)
+      ((uint16_t*)Y)[(int64_t)i * ldy + j] = (uint16_t)f32_to_bf16_rne(__builtin_bit_cast(uint32_t, acc));
+    else
+      ((float*)Y)[(int64_t)i * ldy + j] = acc;
   }
 }
 
@@ -927,9 +962,14 @@ void bigemm_split_merge_kernel(const float* __restrict__ P, void* __restrict__ Y
 
 typedef void (*Bf16KernelFn)(const uint16_t*, const uint16_t*, void*, int, int, int, int64_t, int64_t, int64_t, int,
                              int, int, int64_t);
-// The bf16 / fp16 kernel instance for W given as [K, N] (wt false) or [N, K].
+// The bf16 / fp16 kernel instance for W given as [K, N] (wt false) or [N, K],
+// and for K a multiple of 8 or not (ktail): choices made from the layout and K,
+// never from M.
 template <bool kF16, bool kOutBf16, bool kSplit>
-Bf16KernelFn bf16_kernel_for(bool wt) {
+Bf16KernelFn bf16_kernel_for(bool wt, bool ktail) {
+  if (ktail)
+    return wt ? bigemm_bf16_kernel<kF16, kOutBf16, kSplit, true, true>
+              : bigemm_bf16_kernel<kF16, kOutBf16, kSplit, false, true>;
   return wt ? bigemm_bf16_kernel<kF16, kOutBf16, kSplit, true> : bigemm_bf16_kernel<kF16, kOutBf16, kSplit, false>;
 }
 
@@ -938,9 +978,10 @@ hipError_t launch_bf16(Op op, bool wt, const void* X, const void* W, void* Y, in
   const int tiles_m = (int)((M + 127) / 128);
   const int tiles_n = (int)((N + 127) / 128);
   const bool f16 = op.in == kInF16, obf = op.out == 1 /* BIGEMM_BF16 */;
+  const bool kt = K % 8 != 0;
   const Bf16KernelFn kern =
-      f16 ? (obf ? bf16_kernel_for<true, true, false>(wt) : bf16_kernel_for<true, false, false>(wt))
-          : (obf ? bf16_kernel_for<false, true, false>(wt) : bf16_kernel_for<false, false, false>(wt));
+      f16 ? (obf ? bf16_kernel_for<true, true, false>(wt, kt) : bf16_kernel_for<true, false, false>(wt, kt))
+          : (obf ? bf16_kernel_for<false, true, false>(wt, kt) : bf16_kernel_for<false, false, false>(wt, kt));
   hipLaunchKernelGGL(kern, dim3(tiles_m * tiles_n), dim3(kThreadsBf16), 0, stream, (const uint16_t*)X,
                      (const uint16_t*)W, Y, (int)M, (int)N, (int)K, ldx, ldw, ldy, tiles_m, tiles_n, 0, (int64_t)0);
   return hipGetLastError();
@@ -954,16 +995,21 @@ hipError_t launch_bf16_split(Op op, bool wt, int32_t k_chunk, const void* X, con
   const int nsplit = (int)((K + k_chunk - 1) / k_chunk);
   const int64_t stride = M * N;
   const bool f16 = op.in == kInF16, obf = op.out == 1 /* BIGEMM_BF16 */;
-  const Bf16KernelFn kern = f16 ? bf16_kernel_for<true, false, true>(wt) : bf16_kernel_for<false, false, true>(wt);
+  const bool kt = K % 8 != 0;
+  const Bf16KernelFn kern =
+      f16 ? bf16_kernel_for<true, false, true>(wt, kt) : bf16_kernel_for<false, false, true>(wt, kt);
   hipLaunchKernelGGL(kern, dim3(tiles_m * tiles_n * nsplit), dim3(kThreadsBf16), 0, stream, (const uint16_t*)X,
                      (const uint16_t*)W, P, (int)M, (int)N, (int)K, ldx, ldw, N, tiles_m, tiles_n,
                      k_chunk / kBkBf16, stride);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t threads = M * (N / 4);
+  const bool vec4 = N % 4 == 0;  // (and then ldy keeps output rows 16-byte aligned)
+  const int64_t threads = vec4 ? M * (N / 4) : M * N;
   const int blocks = (int)((threads + 255) / 256);
-  hipLaunchKernelGGL(obf ? bigemm_split_merge_kernel<true> : bigemm_split_merge_kernel<false>, dim3(blocks),
-                     dim3(256), 0, stream, (const float*)P, Y, (int)M, (int)N, ldy, nsplit, stride);
+  auto merge = vec4 ? (obf ? bigemm_split_merge_kernel<true, true> : bigemm_split_merge_kernel<false, true>)
+                    : (obf ? bigemm_split_merge_kernel<true, false> : bigemm_split_merge_kernel<false, false>);
+  hipLaunchKernelGGL(merge, dim3(blocks), dim3(256), 0, stream, (const float*)P, Y, (int)M, (int)N, ldy, nsplit,
+                     stride);
   return hipGetLastError();
 }
 

@@ -72,13 +72,18 @@ def chk(desc, M, N, K, X=A, ldx=None, W=A, ldw=None, Y=A, ldy=None, XS=0, ldxs=0
 
 def test_check_args_accepts_valid_bf16():
     assert chk(BF, 4096, 4096, 4096) == bg.BIGEMM_OK
+    # any K and N once every row is 16-byte aligned (padded rows)
+    assert chk(BF, 4, 129, 4099, ldx=4104, ldw=136, ldy=132) == bg.BIGEMM_OK
+    assert chk(BF, 4, 1, 1, ldx=8, ldw=8, ldy=4) == bg.BIGEMM_OK
+    assert chk(BF, 4, 7, 7, ldx=8, ldw=8, ldy=8) == bg.BIGEMM_OK
     assert chk(BF, 1, 128, 256) == bg.BIGEMM_OK
     assert chk(BF, 0, 128, 256, X=0, W=0, Y=0) == bg.BIGEMM_OK       # M = 0 is a no-op
     assert chk(BF, 5, 16, 8, ldx=64, ldw=32, ldy=20) == bg.BIGEMM_OK  # padded leading dims
 
 
 @pytest.mark.parametrize("kw", [
-    dict(M=-1), dict(N=0), dict(K=0), dict(K=12), dict(N=12),            # shape rules
+    dict(M=-1), dict(N=0), dict(K=0),                                    # shape rules
+    dict(K=12), dict(N=12),                                              # unpadded rows of 24 bytes
     dict(ldx=4), dict(ldw=4), dict(ldy=4),                               # ld < row width
     dict(ldx=12, K=8), dict(ldy=10),                                     # rows not 16-byte aligned
     dict(X=0), dict(W=0), dict(Y=0), dict(X=A + 2), dict(Y=A + 4),      # null / misaligned
@@ -153,8 +158,9 @@ def test_check_args_w_transposed():
     assert chk_wt(BF, 16, 64, 256, ldw=260) == bg.BIGEMM_ERR_ARG         # rows not 16-byte aligned
     assert chk_wt(BF, 16, 64, 256, ldw=(1 << 23) - 8) == bg.BIGEMM_OK    # 128 * ldw * 2 just below 2^31
     assert chk_wt(BF, 16, 64, 256, ldw=1 << 23) == bg.BIGEMM_ERR_ARG
-    assert chk_wt(BF, 16, 64, 12) == bg.BIGEMM_ERR_ARG                   # K % 8
-    assert chk_wt(BF, 16, 12, 64) == bg.BIGEMM_ERR_ARG                   # N % 8
+    assert chk_wt(BF, 16, 64, 12) == bg.BIGEMM_ERR_ARG                   # rows of 12 elements: 24 bytes
+    assert chk_wt(BF, 16, 64, 12, ldx=16, ldw=16) == bg.BIGEMM_OK        # K = 12 in padded rows
+    assert chk_wt(BF, 16, 12, 64) == bg.BIGEMM_OK                        # any N (Y rows of 48 bytes)
     assert chk_wt(BF, 16, 64, 64, W=A + 2) == bg.BIGEMM_ERR_ARG
     assert chk_wt(BF, 0, 64, 64, X=0, W=0, Y=0) == bg.BIGEMM_OK
     assert chk_wt(F16, 16, 64, 64) == bg.BIGEMM_OK

@@ -346,21 +346,33 @@ def test_decode_workload_sampled():
         assert H.byte_diff(P.attend(Q[i:i + 1], seqs[i:i + 1], poss[i:i + 1])[0], o[i]) == 0, i
 
 
-def test_merge_thread_mappings_agree():
+@pytest.mark.parametrize("D,out", [(128, "f32"), (128, "bf16"), (64, "f32"), (64, "bf16")])
+def test_merge_thread_mappings_agree(D, out):
     """The merge spreads each output element over 32 threads when the call has few
-    (token, head) pairs, and over 8 from 2048 workgroups of the narrow mapping on (D = 128,
-    16 heads: from 32 tokens). Both compute the same lane sums and tree: 31 tokens (wide)
-    and the same tokens inside a call of 32 (narrow) give identical bytes."""
+    (token, head) pairs, and over 8 from 2048 workgroups of the narrow mapping on
+    (T * H * D / 32 >= 2048: with 16 heads, from 32 tokens at D = 128 and from 64 at D = 64).
+    Both mappings compute the same lane sums and tree, so the tokens just below the
+    threshold (wide) and the same tokens inside a call at the threshold (narrow) give
+    identical bytes, for each head dimension and output type (each pairing of compiled
+    merge instances)."""
     lens = [3000, 700, 257]
-    P = Paged(470, lens, 4, 128, 32).write_all()
-    rng = np.random.default_rng(471)
-    seqs = rng.integers(0, len(lens), 32).astype(np.int32)
+    P = Paged(470 + D, lens, 4, D, 32).write_all()
+    Hq = 16
+    T = 2048 * 32 // (Hq * D)
+    rng = np.random.default_rng(471 + D)
+    seqs = rng.integers(0, len(lens), T).astype(np.int32)
     poss = np.array([rng.integers(0, lens[s]) for s in seqs], np.int32)
-    Q = normal_bf16(472, (32, 16, 128))
-    wide = P.attend(Q[:31], seqs[:31], poss[:31])
-    narrow = P.attend(Q, seqs, poss)
-    assert H.byte_diff(narrow[:31], wide) == 0
-    assert_parity(narrow, Q, P, seqs, poss)
+    Q = normal_bf16(472 + D, (T, Hq, D))
+    odt = torch.float32 if out == "f32" else torch.bfloat16
+    wide = P.attend(Q[:T - 1], seqs[:T - 1], poss[:T - 1], out_dtype=odt)
+    narrow = P.attend(Q, seqs, poss, out_dtype=odt)
+    assert H.byte_diff(narrow[:T - 1], wide) == 0
+    if out == "f32":
+        assert_parity(narrow, Q, P, seqs, poss)
+    else:
+        from test_gpu_dtypes import rne_bf16_bits
+        n32 = P.attend(Q, seqs, poss)
+        assert np.array_equal(bits(narrow), rne_bf16_bits(n32.cpu().numpy()))
 
 
 @pytest.mark.parametrize("D", [64, 128])

@@ -109,10 +109,10 @@ def test_bf16_m_zero_is_noop_and_bad_args_rejected():
     h = bg._handle("bf16", 0)
     y = torch.full((4, 32), 3.0, device=DEV)
     assert bg.bigemm_run(h, 0, 32, 64, xd.data_ptr(), 64, wd.data_ptr(), 32, y.data_ptr(), 32) == bg.BIGEMM_OK
-    # misaligned X, K not a multiple of 8, scales on a bf16 handle: rejected, nothing written
+    # misaligned X, X rows not 16-byte aligned (ldx = 60), scales on a bf16 handle: rejected, nothing written
     assert bg.bigemm_run(h, 4, 32, 64, xd.data_ptr() + 2, 64, wd.data_ptr(), 32, y.data_ptr(), 32,
                          check=False) == bg.BIGEMM_ERR_ARG
-    assert bg.bigemm_run(h, 4, 32, 60, xd.data_ptr(), 64, wd.data_ptr(), 32, y.data_ptr(), 32,
+    assert bg.bigemm_run(h, 4, 32, 60, xd.data_ptr(), 60, wd.data_ptr(), 32, y.data_ptr(), 32,
                          check=False) == bg.BIGEMM_ERR_ARG
     assert bg.bigemm_run(h, 4, 32, 64, xd.data_ptr(), 64, wd.data_ptr(), 32, y.data_ptr(), 32,
                          xd.data_ptr(), 2, wd.data_ptr(), 32, check=False) == bg.BIGEMM_ERR_ARG
