@@ -35,7 +35,7 @@
 extern "C" {
 #endif
 
-#define BIGEMM_ABI_VERSION 7
+#define BIGEMM_ABI_VERSION 8
 
 /* Exported entry points (the library is built with hidden visibility by default). */
 #if defined(__GNUC__)
@@ -51,7 +51,9 @@ typedef enum {
   BIGEMM_ERR_ARG = 1,          /* invalid argument; nothing was launched                    */
   BIGEMM_ERR_UNSUPPORTED = 2,  /* device is not gfx950, or dtype combination not provided   */
   BIGEMM_ERR_DEVICE = 3,       /* a HIP call or the kernel launch failed                     */
-  BIGEMM_ERR_NOMEM = 4         /* host allocation of the handle failed                       */
+  BIGEMM_ERR_NOMEM = 4,        /* host allocation of the handle failed                       */
+  BIGEMM_ERR_SCRATCH = 5       /* bigemm_run_split_k_static: more scratch than the static
+                                  buffer holds (BIGEMM_STATIC_SCRATCH_BYTES); nothing launched */
 } bigemm_status;
 
 typedef enum {
@@ -247,6 +249,38 @@ BIGEMM_API bigemm_status bigemm_run_ws(bigemm_t h, int64_t M, int64_t N, int64_t
                             const void* W_scale, int64_t ldws,
                             void* workspace, uint64_t workspace_bytes,
                             void* stream);
+
+/* Size of the static device scratch buffer of bigemm_run_split_k_static. */
+#define BIGEMM_STATIC_SCRATCH_BYTES (64ull << 20)
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * bigemm_run_ws call of a split-K handle (bigemm_create_split_k or
+ * bigemm_create_split_k_wt) with the chunk sums kept in the library's own
+ * static device buffer instead of a caller workspace. Same kernels, so Y has
+ * the bytes of bigemm_run_ws on the same handle and inputs.
+ *   - The buffer is a file-scope device array of BIGEMM_STATIC_SCRATCH_BYTES
+ *     (64 MiB); every GPU the library runs on holds its own copy until the
+ *     process ends. Its device address is looked up once per device when a
+ *     split-K handle is created there. This call allocates nothing (no
+ *     hipMalloc, no allocating library routine).
+ *   - The chunk sums need ceil(K / k_chunk) * M * N * 4 bytes (0 when
+ *     K <= k_chunk: then the unsplit kernel runs and the buffer is unused).
+ *     More than BIGEMM_STATIC_SCRATCH_BYTES returns BIGEMM_ERR_SCRATCH and
+ *     launches nothing; use bigemm_run_ws with a workspace for such shapes.
+ *   - Every element the merge reads is written by the same call first, so the
+ *     buffer needs no clearing and the previous call's contents never reach Y.
+ *   - All calls on one GPU share that GPU's buffer: calls that overlap on one
+ *     GPU (different streams, or host threads without ordering) race and may
+ *     return wrong results. Order them on one stream.
+ * Errors as bigemm_run_ws (BIGEMM_ERR_ARG also for a handle without split-K).
+ */
+BIGEMM_API bigemm_status bigemm_run_split_k_static(bigemm_t h, int64_t M, int64_t N, int64_t K,
+                                                   const void* X, int64_t ldx,
+                                                   const void* W, int64_t ldw,
+                                                   void* Y, int64_t ldy,
+                                                   void* stream);
 
 /*
  * The argument checks of bigemm_run_ws on a split-K handle created from

@@ -22,7 +22,7 @@ __all__ = [
     "bigemm_create", "bigemm_run", "bigemm_destroy", "bigemm_status_str", "bigemm_get_config",
     "bigemm_check_args", "bigemm_abi_version", "mm", "bigemm_create_wt", "bigemm_check_args_wt",
     "bigemm_create_split_k", "bigemm_create_split_k_wt", "bigemm_workspace_size", "bigemm_run_ws",
-    "bigemm_check_args_split_k",
+    "bigemm_check_args_split_k", "bigemm_run_split_k_static", "BIGEMM_ERR_SCRATCH", "STATIC_SCRATCH_BYTES",
     "bigemm_rmsnorm", "bigemm_rmsnorm_check_args", "rmsnorm",
     "bigemm_kv_layout", "bigemm_kv_cache_write", "bigemm_attn_workspace_size", "bigemm_paged_attention",
     "bigemm_paged_attention_check_args", "kv_cache_write", "paged_attention", "ATTN_SPLIT",
@@ -33,6 +33,8 @@ BIGEMM_ERR_ARG = 1
 BIGEMM_ERR_UNSUPPORTED = 2
 BIGEMM_ERR_DEVICE = 3
 BIGEMM_ERR_NOMEM = 4
+BIGEMM_ERR_SCRATCH = 5
+STATIC_SCRATCH_BYTES = 64 << 20  # BIGEMM_STATIC_SCRATCH_BYTES
 
 BIGEMM_BF16 = 1
 BIGEMM_F32 = 2
@@ -113,6 +115,8 @@ def load():
         lib.bigemm_check_args_split_k.restype = ctypes.c_int
         lib.bigemm_check_args_split_k.argtypes = [ctypes.POINTER(bigemm_desc), i32, i64, i64, i64, vp, i64, vp, i64,
                                                   vp, i64, vp, ctypes.c_uint64]
+        lib.bigemm_run_split_k_static.restype = ctypes.c_int
+        lib.bigemm_run_split_k_static.argtypes = [vp, i64, i64, i64, vp, i64, vp, i64, vp, i64, vp]
         lib.bigemm_run_ws.restype = ctypes.c_int
         lib.bigemm_run_ws.argtypes = [vp, i64, i64, i64, vp, i64, vp, i64, vp, i64, vp, i64, vp, i64, vp,
                                       ctypes.c_uint64, vp]
@@ -208,6 +212,17 @@ def bigemm_run_ws(h: int, M: int, N: int, K: int, X: int, ldx: int, W: int, ldw:
                               workspace or None, int(workspace_bytes), stream or None)
     if check and st != BIGEMM_OK:
         raise BigemmError(st, "bigemm_run_ws")
+    return int(st)
+
+
+def bigemm_run_split_k_static(h: int, M: int, N: int, K: int, X: int, ldx: int, W: int, ldw: int, Y: int,
+                              ldy: int, stream: int = 0, check: bool = True) -> int:
+    """bigemm_run_ws of a split-K handle with the library's static scratch buffer (allocates nothing).
+    Raises BigemmError unless check=False."""
+    st = load().bigemm_run_split_k_static(ctypes.c_void_p(h) if h else None, M, N, K, X or None, ldx,
+                                          W or None, ldw, Y or None, ldy, stream or None)
+    if check and st != BIGEMM_OK:
+        raise BigemmError(st, "bigemm_run_split_k_static")
     return int(st)
 
 

@@ -308,6 +308,8 @@ const char* bigemm_status_str(bigemm_status s) {
     case BIGEMM_ERR_UNSUPPORTED: return "unsupported device or descriptor (gfx950; bf16, fp16, MXFP8 or int8)";
     case BIGEMM_ERR_DEVICE: return "HIP device error";
     case BIGEMM_ERR_NOMEM: return "out of host memory";
+    case BIGEMM_ERR_SCRATCH:
+      return "the split-K chunk sums need more than the static scratch buffer holds (BIGEMM_STATIC_SCRATCH_BYTES)";
   }
   return "unknown status";
 }
@@ -377,6 +379,15 @@ bigemm_status bigemm_create_split_k(const bigemm_desc* desc, int32_t k_chunk, bi
   const bigemm_status st = bigemm_create(desc, out);
   if (st != BIGEMM_OK) return st;
   (*out)->k_chunk = k_chunk;
+  // Set-up of bigemm_run_split_k_static on this device: the static scratch
+  // array's device address, looked up once per device.
+  void* scratch = nullptr;
+  if (bigemm::static_scratch_address((*out)->device, &scratch) != hipSuccess) {
+    (void)hipGetLastError();
+    delete *out;
+    *out = nullptr;
+    return BIGEMM_ERR_DEVICE;
+  }
   return BIGEMM_OK;
 }
 
@@ -422,6 +433,33 @@ bigemm_status bigemm_run_ws(bigemm_t h, int64_t M, int64_t N, int64_t K, const v
     return e == hipSuccess ? BIGEMM_OK : BIGEMM_ERR_DEVICE;
   }
   const hipError_t e = bigemm::launch_bf16_split(h->op, h->w_trans, h->k_chunk, X, W, Y, workspace, M, N, K, ldx,
+                                                 ldw, ldy, (hipStream_t)stream);
+  return e == hipSuccess ? BIGEMM_OK : BIGEMM_ERR_DEVICE;
+}
+
+bigemm_status bigemm_run_split_k_static(bigemm_t h, int64_t M, int64_t N, int64_t K, const void* X, int64_t ldx,
+                                        const void* W, int64_t ldw, void* Y, int64_t ldy, void* stream) {
+  if (!h) return BIGEMM_ERR_ARG;
+  if (h->k_chunk <= 0) return BIGEMM_ERR_ARG;  // a split-K handle only
+  const bigemm_status st = check(h->op, M, N, K, X, ldx, W, ldw, Y, ldy, nullptr, 0, nullptr, 0, h->w_trans);
+  if (st != BIGEMM_OK || M == 0) return st;
+  const uint64_t need = split_need(h->k_chunk, M, N, K);
+  if (need > bigemm::kStaticScratchBytes) return BIGEMM_ERR_SCRATCH;
+  const bigemm_status dv = handle_device_current(h);
+  if (dv != BIGEMM_OK) return dv;
+  if (need == 0) {  // a single chunk: the one fixed kernel, no scratch
+    const hipError_t e = launch_unsplit(h->op, h->w_trans, M, N, K, X, ldx, W, ldw, Y, ldy, nullptr, 0, nullptr,
+                                        0, (hipStream_t)stream);
+    return e == hipSuccess ? BIGEMM_OK : BIGEMM_ERR_DEVICE;
+  }
+  void* scratch = nullptr;
+  if (bigemm::static_scratch_address(h->device, &scratch) != hipSuccess) {
+    (void)hipGetLastError();
+    return BIGEMM_ERR_DEVICE;
+  }
+  const bigemm_status sst = split_check(h->k_chunk, M, N, K, scratch, bigemm::kStaticScratchBytes);
+  if (sst != BIGEMM_OK) return sst;
+  const hipError_t e = bigemm::launch_bf16_split(h->op, h->w_trans, h->k_chunk, X, W, Y, scratch, M, N, K, ldx,
                                                  ldw, ldy, (hipStream_t)stream);
   return e == hipSuccess ? BIGEMM_OK : BIGEMM_ERR_DEVICE;
 }

@@ -29,6 +29,13 @@ hipError_t launch_bf16_split(Op op, bool wt, int32_t k_chunk, const void* X, con
                              int64_t M, int64_t N, int64_t K, int64_t ldx, int64_t ldw, int64_t ldy,
                              hipStream_t stream);
 
+// Size of the static scratch array used by bigemm_run_split_k_static.
+constexpr uint64_t kStaticScratchBytes = (uint64_t)64 << 20;
+
+// Device address of the static scratch array on `device`, which must be the
+// current device; looked up on the first call per device and cached.
+hipError_t static_scratch_address(int device, void** out);
+
 hipError_t launch_mxfp8(Op op, bool wt, const void* X, const void* W, void* Y, const void* XS, const void* WS,
                         int64_t M, int64_t N, int64_t K, int64_t ldx, int64_t ldw, int64_t ldy,
                         int64_t ldxs, int64_t ldws, hipStream_t stream);

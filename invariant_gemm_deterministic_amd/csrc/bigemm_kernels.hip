@@ -47,6 +47,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "bigemm_kernels.h"
 
 namespace bigemm {
@@ -956,6 +959,44 @@ void bigemm_split_merge_kernel(const float* __restrict__ P, void* __restrict__ Y
     else
       ((float*)Y)[(int64_t)i * ldy + j] = acc;
   }
+}
+
+// ------------------------------------------------------------ static scratch
+//
+// The chunk sums of bigemm_run_split_k_static live in this file-scope device
+// array instead of a caller workspace, for callers that cannot allocate. Each
+// GPU holds its own copy for the life of the process. Its name is a host-side
+// stand-in in host code: the device address comes from hipGetSymbolAddress,
+// looked up once per device with that device current, and only that address
+// is handed to kernels.
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+hipError_t static_scratch_address(int device, void** out) {
+  *out = nullptr;
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch_addr[device].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_addr[device].load(std::memory_order_relaxed);
+    if (!p) {
+      int cur = -1;
+      hipError_t e = hipGetDevice(&cur);
+      if (e != hipSuccess) return e;
+      if (cur != device) return hipErrorInvalidDevice;  // the lookup must run with that device current
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (!p) return hipErrorInvalidSymbol;
+      g_scratch_addr[device].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return hipSuccess;
 }
 
 // ------------------------------------------------------------------ launchers

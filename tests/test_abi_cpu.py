@@ -38,8 +38,8 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert bg.bigemm_abi_version() == 7
-    for s in range(5):
+    assert bg.bigemm_abi_version() == 8
+    for s in range(6):
         assert bg.bigemm_status_str(s)
     assert "unknown" in bg.bigemm_status_str(99)
 
