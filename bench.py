@@ -68,8 +68,11 @@ WARM_S = 0.3          # seconds of back-to-back launches before any point is tim
 BLOCKS = 5            # timed blocks per point (median taken)
 
 
-def _warm(torch, fn, seconds=WARM_S):
-    """Launch fn back to back for at least `seconds` (synchronising every 20 launches)."""
+def _warm(torch, fn, seconds=None):
+    """Launch fn back to back for at least `seconds` (default WARM_S; synchronising every 20 launches)."""
+    seconds = WARM_S if seconds is None else min(seconds, WARM_S)
+    if seconds <= 0:
+        return
     t0 = time.perf_counter()
     i = 0
     while True:
@@ -98,7 +101,7 @@ def _blocks(torch, stream, fn, reps, blocks=BLOCKS):
     return per[blocks // 2], ev[0].elapsed_time(ev[-1]), blocks * reps
 
 
-def _time_point(torch, stream, fn, reps, warm_s=WARM_S):
+def _time_point(torch, stream, fn, reps, warm_s=None):
     """One figure of the bench: warm for warm_s seconds, then the median of BLOCKS blocks."""
     _warm(torch, fn, warm_s)
     return _blocks(torch, stream, fn, reps)[0]
@@ -189,6 +192,7 @@ def cpu_baseline_one_thread(X, W, rows: int = 16):
 
 
 def main():
+    global WARM_S
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
@@ -198,7 +202,14 @@ def main():
     ap.add_argument("--m", type=int, default=4096, help="rows of the timed headline call (profiling other M)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="one 256 MiB device copy before the GEMMs (scale reference for byte counters)")
+    ap.add_argument("--kind", choices=("bf16", "mxfp8"), default="bf16",
+                    help="input family of the headline call (profiling the MXFP8 kernel; the bench line is bf16)")
+    ap.add_argument("--warm-s", type=float, default=WARM_S,
+                    help="seconds of launches before each timed point (profiling runs under counters use 0)")
     args = ap.parse_args()
+    WARM_S = args.warm_s
+    if args.kind != "bf16" and not args.no_sweep:
+        ap.error("--kind mxfp8 profiles the MXFP8 kernel alone: use it with --no-sweep")
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the GEMM would shard by rows "
               f"or columns with no exchange, and no multi-GPU launch is implemented.", file=sys.stderr)
@@ -229,9 +240,19 @@ def main():
     assert 1 <= M <= 4096
     Xm, Ym = X[:M], Y[:M]
     head = lambda i: bg.mm(Xm, W, out=Ym)
+    head_peak = PEAK_BF16_TFLOPS
+    if args.kind == "mxfp8":   # E4M3 with K-varying E8M0 scales on both sides, as in other_types
+        from bigemm_inputs import SCALE_SEED_OFFSET, e8m0_scales, normal_e4m3
+        Xq = torch.from_numpy(normal_e4m3(SEED_X, (M, K))).to(dev)
+        Wq = torch.from_numpy(normal_e4m3(SEED_W, (K, N))).to(dev)
+        XSq = torch.from_numpy(e8m0_scales(SEED_X + SCALE_SEED_OFFSET, (M, K // 32), "var")).to(dev)
+        WSq = torch.from_numpy(e8m0_scales(SEED_W + SCALE_SEED_OFFSET, (K // 32, N), "var")).to(dev)
+        head = lambda i: bg.mm(Xq, Wq, XSq, WSq, out=Ym)
+        head_peak = PEAK_FP8_TFLOPS
     for i in range(args.warmup):
         head(i)
-    _warm(torch, head)                     # the sustained clock, whatever --warmup is
+    if WARM_S > 0:
+        _warm(torch, head)                 # the sustained clock, whatever --warmup is
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     nblk = BLOCKS if args.steps % BLOCKS == 0 and args.steps >= BLOCKS else 1
@@ -447,15 +468,19 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16" if args.kind == "bf16" else "e4m3",
         "data": "synthetic",
-        "config": {"workload": f"bf16 projection GEMM Y[{M},4096] = X[{M},4096] . W[4096,4096], "
-                               "X~N(0,1), W~N(0,0.02), fp32 accumulate and output, batch-invariant fixed tile",
-                   "M": M, "N": N, "K": K, "tile": list(bg.bigemm_get_config(bg._handle("bf16", 0)))},
-        "pct_mfma_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
-        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic() if M == 4096 else None},
+        "config": {"workload": (f"bf16 projection GEMM Y[{M},4096] = X[{M},4096] . W[4096,4096], "
+                                "X~N(0,1), W~N(0,0.02), fp32 accumulate and output, batch-invariant fixed tile")
+                   if args.kind == "bf16" else
+                   (f"MXFP8 GEMM Y[{M},4096] = X[{M},4096] . W[4096,4096], E4M3 from N(0,1) with K-varying "
+                    "E8M0 scales in [-4,4] on both sides, fp32 accumulate and output (profiling run)"),
+                   "M": M, "N": N, "K": K,
+                   "tile": list(bg.bigemm_get_config(bg._handle("bf16" if args.kind == "bf16" else "mx", 0)))},
+        "pct_mfma_peak": round(100 * tflops / head_peak, 2),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": head_peak,
+                     "unit": "TFLOP/s", "frac": round(tflops / head_peak, 4),
+                     "traffic": measured_traffic() if M == 4096 and args.kind == "bf16" else None},
         "m_sweep": sweep,
         "other_types_k4096_n4096": mx,
         "w_transposed_byte_diffs": wt_byte_diffs if mx else None,
