@@ -62,14 +62,18 @@ bigemm_status check(bigemm::Op op, int64_t M, int64_t N, int64_t K, const void* 
   if (mx && (K % 32 != 0 || N % 16 != 0)) return BIGEMM_ERR_ARG;
   if (op.in == bigemm::kInI8 && (K % 16 != 0 || N % 16 != 0)) return BIGEMM_ERR_ARG;
   if (ldx < K || ldw < (wt ? K : N) || ldy < N) return BIGEMM_ERR_ARG;
-  if ((ldx * es) % 16 != 0 || (ldw * es) % 16 != 0 || (ldy * eo) % 16 != 0) return BIGEMM_ERR_ARG;
-  if (128 * ldx * es >= kOffsetLimit || 128 * ldw * es >= kOffsetLimit || 128 * ldy * eo >= kOffsetLimit)
+  // Every row 16-byte aligned (ld times the element size a multiple of 16), and the
+  // 128 rows of a tile inside the 32-bit buffer offsets (128 * ld * element size
+  // below 2^31); both written without products that could overflow.
+  if (ldx % (16 / es) != 0 || ldw % (16 / es) != 0 || ldy % (16 / eo) != 0) return BIGEMM_ERR_ARG;
+  if (ldx >= kOffsetLimit / (128 * es) || ldw >= kOffsetLimit / (128 * es) || ldy >= kOffsetLimit / (128 * eo))
     return BIGEMM_ERR_ARG;
   if (!mx) {
     if (XS != nullptr || WS != nullptr) return BIGEMM_ERR_ARG;
   } else {
     if (ldxs < K / 32 || ldws < (wt ? K / 32 : N)) return BIGEMM_ERR_ARG;
-    if (128 * ldxs >= kOffsetLimit || (wt ? 128 : K / 32) * ldws >= kOffsetLimit) return BIGEMM_ERR_ARG;
+    const int64_t wrows = wt ? 128 : K / 32;  // W_scale rows one tile addresses (K >= 32 here)
+    if (ldxs >= kOffsetLimit / 128 || ldws >= (kOffsetLimit + wrows - 1) / wrows) return BIGEMM_ERR_ARG;
   }
   if (M == 0) return BIGEMM_OK;
   if (!X || !W || !Y) return BIGEMM_ERR_ARG;
@@ -83,7 +87,7 @@ bigemm_status rmsnorm_check(int32_t dtype, int64_t M, int64_t D, const void* X, 
   if (dtype != BIGEMM_BF16 && dtype != BIGEMM_F32) return BIGEMM_ERR_UNSUPPORTED;
   if (M < 0 || M > INT32_MAX || D < 8 || D > 65536 || D % 8 != 0) return BIGEMM_ERR_ARG;
   const int64_t es = dtype == BIGEMM_BF16 ? 2 : 4;
-  if (ldx < D || ldy < D || (ldx * es) % 16 != 0 || (ldy * es) % 16 != 0) return BIGEMM_ERR_ARG;
+  if (ldx < D || ldy < D || ldx % (16 / es) != 0 || ldy % (16 / es) != 0) return BIGEMM_ERR_ARG;
   if (M == 0) return BIGEMM_OK;
   if (!X || !G || !Y || !aligned16(X) || !aligned16(G) || !aligned16(Y)) return BIGEMM_ERR_ARG;
   return BIGEMM_OK;
@@ -91,9 +95,13 @@ bigemm_status rmsnorm_check(int32_t dtype, int64_t M, int64_t D, const void* X, 
 
 // Workspace bytes of a split-K run: ceil(K / k_chunk) chunk sums of M x N fp32,
 // or 0 when there is no split (no k_chunk, or a single chunk).
+// Saturates at UINT64_MAX (the exact product can need up to 2^90 for sizes that
+// other checks reject), so that no size wraps to a small one.
 uint64_t split_need(int32_t k_chunk, int64_t M, int64_t N, int64_t K) {
   if (k_chunk <= 0 || K <= k_chunk || M <= 0 || N <= 0) return 0;
-  return (uint64_t)((K + k_chunk - 1) / k_chunk) * (uint64_t)M * (uint64_t)N * 4u;
+  const unsigned __int128 b =
+      (unsigned __int128)(uint64_t)((K + k_chunk - 1) / k_chunk) * (uint64_t)M * (uint64_t)N * 4u;
+  return b > (unsigned __int128)UINT64_MAX ? UINT64_MAX : (uint64_t)b;
 }
 
 // The limits a split-K run adds to check(): the chunk sums are stored through
@@ -102,10 +110,12 @@ uint64_t split_need(int32_t k_chunk, int64_t M, int64_t N, int64_t K) {
 // (at most one thread per output) and the (chunk, tile) grid must fit, and the
 // workspace must be present, 16-byte aligned and large enough.
 bigemm_status split_check(int32_t k_chunk, int64_t M, int64_t N, int64_t K, const void* ws, uint64_t ws_bytes) {
+  if (M < 0 || N < 0 || K < 0 || M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return BIGEMM_ERR_ARG;
   const uint64_t need = split_need(k_chunk, M, N, K);
   if (need == 0) return BIGEMM_OK;
   if (128 * N * 4 >= kOffsetLimit) return BIGEMM_ERR_ARG;
-  if ((K + k_chunk - 1) / k_chunk * ((M + 127) / 128) * ((N + 127) / 128) > INT32_MAX) return BIGEMM_ERR_ARG;
+  if ((__int128)((K + k_chunk - 1) / k_chunk) * ((M + 127) / 128) * ((N + 127) / 128) > INT32_MAX)
+    return BIGEMM_ERR_ARG;
   if (M * N > (int64_t)INT32_MAX * 256) return BIGEMM_ERR_ARG;  // merge grid (one thread per output at most)
   if (!ws || !aligned16(ws) || ws_bytes < need) return BIGEMM_ERR_ARG;
   return BIGEMM_OK;
@@ -185,7 +195,8 @@ bigemm_status attn_sizes(const bigemm_kv_layout* kv, int64_t T, int32_t H, int32
   if (G < 1 || G > 16) return BIGEMM_ERR_ARG;  // the query heads of a group fill one 16-row MFMA tile
   if (max_context < 1 || (int64_t)max_context > (int64_t)kv->max_blocks * kv->block_size) return BIGEMM_ERR_ARG;
   const int64_t ns = ((int64_t)max_context + bigemm::kAttnSplit - 1) / bigemm::kAttnSplit;
-  if (T * kv->num_kv_heads * ns > INT32_MAX || T * H * (kv->head_dim / 32) > INT32_MAX) return BIGEMM_ERR_ARG;
+  if ((__int128)T * kv->num_kv_heads * ns > INT32_MAX || (__int128)T * H * (kv->head_dim / 32) > INT32_MAX)
+    return BIGEMM_ERR_ARG;
   *nsplit = (int32_t)ns;
   *need = (uint64_t)T * (uint64_t)H * (uint64_t)ns * (uint64_t)(kv->head_dim + 2) * 4u;
   return BIGEMM_OK;
@@ -212,7 +223,7 @@ bigemm_status bigemm_kv_cache_write(const bigemm_kv_layout* kv, int64_t T, const
                                     void* K_cache, void* V_cache, void* stream) {
   const bigemm_status st = kv_layout_check(kv);
   if (st != BIGEMM_OK) return st;
-  if (T < 0 || T * kv->num_kv_heads * (kv->head_dim / 8) >= (int64_t)INT32_MAX) return BIGEMM_ERR_ARG;
+  if (T < 0 || (__int128)T * kv->num_kv_heads * (kv->head_dim / 8) >= (int64_t)INT32_MAX) return BIGEMM_ERR_ARG;
   if (T == 0) return BIGEMM_OK;
   if (!K_new || !V_new || !seq_ids || !positions || !block_table || !K_cache || !V_cache) return BIGEMM_ERR_ARG;
   if (!aligned16(K_new) || !aligned16(V_new) || !aligned16(K_cache) || !aligned16(V_cache)) return BIGEMM_ERR_ARG;
