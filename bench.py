@@ -20,7 +20,9 @@ ABI with inputs resident in HBM. Also reported:
 * ``split_k_context``: the opt-in pinned-chunk split-K handle at small M (cold
   LLC) and on the long-K workload, against the unsplit kernel (context);
 * ``rmsnorm_bf16_context``: the batch-invariant RMSNorm (bf16, D = 4096) against
-  the HBM peak (context);
+  the HBM peak (context), by events around back-to-back Python calls and, as
+  ``us_graph``, around replays of the same calls captured in a HIP graph (the
+  kernels without the host dispatch of each call);
 * ``paged_attention_decode_context``: the batch-invariant paged attention
   (fixed 256-position KV splits, bf16 cache in blocks of 32, one query token
   per sequence at its last position, fp32 output) for several batch / context
@@ -116,6 +118,30 @@ def _time_ab(torch, stream, fa, fb, reps=10, rounds=BLOCKS):
         ta.append(_blocks(torch, stream, fa, reps, 1)[0])
         tb.append(_blocks(torch, stream, fb, reps, 1)[0])
     return sorted(ta)[rounds // 2], sorted(tb)[rounds // 2]
+
+
+def _time_graph(torch, stream, fn, reps, replays=BLOCKS):
+    """fn called `reps` times inside one captured HIP graph (torch.cuda.CUDAGraph), so the host
+    dispatch of each call is out of the timed region; returns the median ms per call over
+    `replays` timed replays (after one untimed replay)."""
+    fn(0)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(reps):
+            fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(replays):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record(stream)
+        g.replay()
+        e.record(stream)
+        e.synchronize()
+        ts.append(s.elapsed_time(e) / reps)
+    del g
+    return sorted(ts)[replays // 2]
 
 
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "bigemm_bf16_kernel_m4096_k4096_n4096_traffic.md")
@@ -353,9 +379,13 @@ def main():
             XN = torch.from_numpy(normal_bf16(SEED_X + 1, (m, D)).view(np.int16)).to(dev)
             YN = torch.empty_like(XN)
             t = _time_point(torch, stream, lambda i: bg.rmsnorm(XN, G, 1e-6, out=YN), 50, 0.1)
+            # the same 50 calls replayed from a captured graph: the kernel without the Python dispatch
+            tg = _time_graph(torch, stream, lambda i: bg.rmsnorm(XN, G, 1e-6, out=YN), 50)
             byts = 4 * m * D + 2 * D
             norm.append({"M": m, "D": D, "us": round(t * 1e3, 2), "gbs_algorithmic": round(byts / (t * 1e-3) / 1e9, 0),
-                         "pct_hbm_peak": round(100 * byts / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 1)})
+                         "pct_hbm_peak": round(100 * byts / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 1),
+                         "us_graph": round(tg * 1e3, 2),
+                         "pct_hbm_peak_graph": round(100 * byts / (tg * 1e-3) / 1e9 / PEAK_HBM_GBS, 1)})
             del XN, YN
 
     # ----------------------------------------- paged attention, decode (context)

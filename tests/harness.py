@@ -85,6 +85,15 @@ def _with_row(batch, i, row):
 
 
 # ---------------------------------------------------------------------- cells
+def sha256_of(arrays) -> str:
+    """sha256 over the bytes of a tuple of arrays (the record of which inputs a cell used)."""
+    import hashlib
+    h = hashlib.sha256()
+    for a in arrays:
+        h.update(np.ascontiguousarray(a).tobytes())
+    return h.hexdigest()
+
+
 def ab_cell(gemm, make_rows, weights, M: int, row: int,
             seed_C: int = SEED_C, seed_A: int = SEED_A, seed_B: int = SEED_B):
     C = make_rows(seed_C, 1)
@@ -94,7 +103,19 @@ def ab_cell(gemm, make_rows, weights, M: int, row: int,
     yB = gemm(XB, weights)[row]
     y1 = gemm(C, weights)[0]
     return {"M": M, "row": row, "ab": byte_diff(yA, yB), "canon": byte_diff(yA, y1),
-            "degenerate": M == 1}
+            "degenerate": M == 1, "seeds": [seed_C, seed_A, seed_B], "sha256_C": sha256_of(C),
+            "sha256_W": sha256_of(weights)}
+
+
+# Every A/B cell the GPU tests ran, one record each: the issue's per-cell byte-diff
+# count (section "ATK integration"), written as JSON lines to $BIGEMM_BI_REPORT at
+# the end of the session and summed in the test summary.
+REPORT = []
+
+
+def report(config: str, cells, **fields):
+    for c in cells:
+        REPORT.append(dict(config=config, **fields, **c))
 
 
 def position_cell(gemm, make_rows, weights, M: int, seed_C: int = SEED_C, seed_fill: int = SEED_A):

@@ -71,6 +71,7 @@ def test_f16_ab_and_position_cells():
     W = (normal_f16(SEED_W, (256, 128)).view(np.float16),)
     make = H.rows_f16(256)
     cells = [H.ab_cell(gemm, make, W, M, r) for M in (1, 4, 8, 16, 32) for r in (0, M // 2, M - 1)]
+    H.report("fp16 X[M,256].W[256,128]", cells, K=256, N=128, dtype="f16")
     assert not [c for c in cells if c["ab"] or c["canon"]]
     for M in (17, 129, 300):
         assert all(v == 0 for v in H.position_cell(gemm, make, W, M).values()), M
@@ -141,6 +142,7 @@ def test_bf16_output_msweep_and_ab():
     gemm = GpuGemm(out_dtype=torch.bfloat16)
     Wn = (normal_bf16(SEED_W, (256, 128)),)
     cells = [H.ab_cell(gemm, H.rows_bf16(256), Wn, M, r) for M in (1, 8, 32) for r in (0, M // 2, M - 1)]
+    H.report("bf16 -> bf16 out X[M,256].W[256,128]", cells, K=256, N=128, dtype="bf16")
     assert not [c for c in cells if c["ab"] or c["canon"]]
 
 
@@ -150,6 +152,7 @@ def test_mxfp8_bf16_output_ab_cells():
     W = (normal_e4m3(SEED_W, (K, N)), e8m0_scales(SEED_W + SCALE_SEED_OFFSET, (K // 32, N), "var"))
     make = H.rows_mx(K, "var")
     cells = [H.ab_cell(gemm, make, W, M, r) for M in (1, 16, 64) for r in (0, M // 2, M - 1)]
+    H.report("MXFP8 -> bf16 out", cells, K=K, N=N, dtype="e4m3")
     assert not [c for c in cells if c["ab"] or c["canon"]]
 
 
@@ -180,6 +183,7 @@ def test_i8_invariance():
     W = (int_i8(SEED_W, (256, 128)),)
     make = H.rows_i8(256)
     cells = [H.ab_cell(gemm, make, W, M, r) for M in (1, 4, 16, 32) for r in (0, M // 2, M - 1)]
+    H.report("int8 X[M,256].W[256,128]", cells, K=256, N=128, dtype="i8")
     assert not [c for c in cells if c["ab"] or c["canon"]]
     xd = dev_i8(int_i8(SEED_X, (1024, 1024)))
     wd = dev_i8(int_i8(SEED_W, (1024, 512)))

@@ -38,6 +38,7 @@ def test_small_bf16_ab_cells():
     W = (normal_bf16(SEED_W, (256, 128)),)
     make = H.rows_bf16(256)
     cells = [H.ab_cell(gemm, make, W, M, r) for M in (1, 4, 8, 16, 32) for r in _ab_rows(M)]
+    H.report("bf16 X[M,256].W[256,128]", cells, K=256, N=128, dtype="bf16")
     assert len(cells) == 15
     bad = [c for c in cells if c["ab"] or c["canon"]]
     assert not bad, bad
@@ -161,6 +162,7 @@ def test_mxfp8_ab_grid(combo):
             for M in g["M_per_rank"]:
                 for r in _ab_rows(M):
                     c = H.ab_cell(gemm, make, W, M, r)
+                    H.report(f"MXFP8 {combo[0]},{combo[1]}", [c], K=K, N=N, dtype="e4m3")
                     n += 1
                     if c["ab"] or c["canon"]:
                         bad.append((K, N, c))

@@ -90,6 +90,7 @@ def test_rmsnorm_ab_position_and_msweep():
     G = (normal_bf16(SEED_W, (4096,)),)
     make = H.rows_bf16(4096)
     cells = [H.ab_cell(norm, make, G, M, r) for M in (1, 4, 8, 16, 32, 300) for r in (0, M // 2, M - 1)]
+    H.report("RMSNorm D=4096", cells, K=4096, N=4096, dtype="bf16")
     assert not [c for c in cells if c["ab"] or c["canon"]]
     for M in (17, 129):
         assert all(v == 0 for v in H.position_cell(norm, make, G, M).values()), M

@@ -76,6 +76,7 @@ def test_split_k_ab_and_position_cells():
     W = (normal_bf16(SEED_W, (1024, 128)),)
     make = H.rows_bf16(1024)
     cells = [H.ab_cell(gemm, make, W, M, r) for M in (1, 4, 16, 32) for r in (0, M // 2, M - 1)]
+    H.report("split-K bf16 X[M,1024].W[1024,128]", cells, K=1024, N=128, dtype="bf16")
     assert not [c for c in cells if c["ab"] or c["canon"]]
     for M in (17, 129):
         assert all(v == 0 for v in H.position_cell(gemm, make, W, M).values()), M

@@ -137,6 +137,7 @@ def test_tail_invariance_cells():
     W = (normal_bf16(SEED_W, (K, N), 0.02),)
     make = H.rows_bf16(K)
     cells = [H.ab_cell(g, make, W, M, r) for M in (1, 4, 33, 130) for r in (0, M // 2, M - 1)]
+    H.report("bf16 tails K=4099 N=129", cells, K=K, N=N, dtype="bf16")
     assert not [c for c in cells if c["ab"] or c["canon"]], cells
     for M in (17, 129):
         assert all(v == 0 for v in H.position_cell(g, make, W, M).values()), M
