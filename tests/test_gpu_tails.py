@@ -143,3 +143,36 @@ def test_tail_invariance_cells():
         assert all(v == 0 for v in H.position_cell(g, make, W, M).values()), M
     sweep = H.msweep_cell(g, (normal_bf16(SEED_X, (300, K)),), W, (1, 7, 128, 129, 257))
     assert all(v["rows"] == 0 and v["alone"] == 0 for v in sweep.values()), sweep
+
+
+def test_tail_random_shapes():
+    """30 seeded random shapes with any K in [1, 1100] and N in [1, 640] (rows padded to
+    a multiple of 8 elements plus a random extra 0, 8 or 24, the padding NaN / infinity):
+    oracle parity of the fp32 output, the W^T call's bytes equal to the [K, N] call's,
+    and the bf16 output equal to the fp32 output rounded once."""
+    from test_gpu_dtypes import rne_bf16_bits
+    rng = np.random.default_rng(2024)
+    for case in range(30):
+        M, N, K = int(rng.integers(1, 300)), int(rng.integers(1, 640)), int(rng.integers(1, 1100))
+        extra = int(rng.choice([0, 8, 24]))
+        X = normal_bf16(500 + case, (M, K))
+        W = normal_bf16(600 + case, (K, N))
+        Xp = np.full((M, -(-K // 8) * 8 + extra), NAN16, np.uint16)
+        Xp[:, :K] = X
+        Wp = np.full((K, -(-N // 8) * 8 + extra), INF16, np.uint16)
+        Wp[:, :N] = W
+        WTp = np.full((N, -(-K // 8) * 8 + extra), INF16, np.uint16)
+        WTp[:, :K] = W.T
+        xd = torch.from_numpy(Xp.view(np.int16)).to(DEV)[:, :K]
+        wd = torch.from_numpy(Wp.view(np.int16)).to(DEV)[:, :N]
+        wtd = torch.from_numpy(WTp.view(np.int16)).to(DEV)[:, :K].t()
+        y = bg.mm(xd, wd)
+        yt = bg.mm(xd, wtd) if N > 1 else y   # one output column: no separate [N, K] layout
+        yb = bg.mm(xd, wd, out_dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+        Y, S = oracle.gemm_bf16(X, W)
+        yh = y.cpu().numpy()
+        assert oracle.max_normalized_error(yh, Y, S) <= TOL, (case, M, N, K)
+        assert H.byte_diff(y, yt) == 0, (case, M, N, K)
+        ybh = yb.cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+        assert np.array_equal(ybh, rne_bf16_bits(np.ascontiguousarray(yh))), (case, M, N, K)
