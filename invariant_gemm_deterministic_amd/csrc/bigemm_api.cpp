@@ -22,6 +22,7 @@
 struct bigemm_s {
   bigemm::Op op;
   int device;
+  int cus;          // the device's compute units
   int32_t k_chunk;  // 0: no split-K
   bool w_trans;     // W given as its transpose, [N, K] (bigemm_create_wt)
 };
@@ -158,13 +159,15 @@ bigemm_status handle_device_current(const bigemm_s* h) {
 }
 
 // The one fixed kernel of the handle's input family (no split).
-hipError_t launch_unsplit(bigemm::Op op, bool wt, int64_t M, int64_t N, int64_t K, const void* X, int64_t ldx,
+hipError_t launch_unsplit(const bigemm_s* h, int64_t M, int64_t N, int64_t K, const void* X, int64_t ldx,
                           const void* W, int64_t ldw, void* Y, int64_t ldy, const void* XS, int64_t ldxs,
                           const void* WS, int64_t ldws, hipStream_t stream) {
+  const bigemm::Op op = h->op;
+  const bool wt = h->w_trans;
   if (op.in == bigemm::kInMx)
     return bigemm::launch_mxfp8(op, wt, X, W, Y, XS, WS, M, N, K, ldx, ldw, ldy, ldxs, ldws, stream);
   if (op.in == bigemm::kInI8) return bigemm::launch_i8(wt, X, W, Y, M, N, K, ldx, ldw, ldy, stream);
-  return bigemm::launch_bf16(op, wt, X, W, Y, M, N, K, ldx, ldw, ldy, stream);
+  return bigemm::launch_bf16(op, wt, X, W, Y, M, N, K, ldx, ldw, ldy, h->cus, stream);
 }
 
 // ------------------------------------------------------------------ attention
@@ -364,6 +367,7 @@ bigemm_status bigemm_create(const bigemm_desc* desc, bigemm_t* out) {
   if (!h) return BIGEMM_ERR_NOMEM;
   h->op = op;
   h->device = dev;
+  h->cus = prop.multiProcessorCount;
   h->k_chunk = 0;
   h->w_trans = false;
   *out = h;
@@ -439,7 +443,7 @@ bigemm_status bigemm_run_ws(bigemm_t h, int64_t M, int64_t N, int64_t K, const v
   const bigemm_status dv = handle_device_current(h);
   if (dv != BIGEMM_OK) return dv;
   if (split_need(h->k_chunk, M, N, K) == 0) {  // unsplit handle, or a single chunk: the one fixed kernel
-    const hipError_t e = launch_unsplit(h->op, h->w_trans, M, N, K, X, ldx, W, ldw, Y, ldy, X_scale, ldxs,
+    const hipError_t e = launch_unsplit(h, M, N, K, X, ldx, W, ldw, Y, ldy, X_scale, ldxs,
                                         W_scale, ldws, (hipStream_t)stream);
     return e == hipSuccess ? BIGEMM_OK : BIGEMM_ERR_DEVICE;
   }
@@ -459,7 +463,7 @@ bigemm_status bigemm_run_split_k_static(bigemm_t h, int64_t M, int64_t N, int64_
   const bigemm_status dv = handle_device_current(h);
   if (dv != BIGEMM_OK) return dv;
   if (need == 0) {  // a single chunk: the one fixed kernel, no scratch
-    const hipError_t e = launch_unsplit(h->op, h->w_trans, M, N, K, X, ldx, W, ldw, Y, ldy, nullptr, 0, nullptr,
+    const hipError_t e = launch_unsplit(h, M, N, K, X, ldx, W, ldw, Y, ldy, nullptr, 0, nullptr,
                                         0, (hipStream_t)stream);
     return e == hipSuccess ? BIGEMM_OK : BIGEMM_ERR_DEVICE;
   }
@@ -513,7 +517,7 @@ bigemm_status bigemm_run(bigemm_t h, int64_t M, int64_t N, int64_t K, const void
   if (st != BIGEMM_OK || M == 0) return st;
   const bigemm_status dv = handle_device_current(h);
   if (dv != BIGEMM_OK) return dv;
-  const hipError_t e = launch_unsplit(h->op, h->w_trans, M, N, K, X, ldx, W, ldw, Y, ldy, X_scale, ldxs,
+  const hipError_t e = launch_unsplit(h, M, N, K, X, ldx, W, ldw, Y, ldy, X_scale, ldxs,
                                       W_scale, ldws, (hipStream_t)stream);
   return e == hipSuccess ? BIGEMM_OK : BIGEMM_ERR_DEVICE;
 }

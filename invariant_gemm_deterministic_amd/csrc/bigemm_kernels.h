@@ -20,8 +20,10 @@ struct Op {
 
 // wt (every launcher): W is given as its transpose, [N][ldw] with ldw >= K,
 // and for MXFP8 W_scale as [N][ldws] with ldws >= K/32.
+// cus: the device's compute units (the grid may be padded with prefetch
+// workgroups up to one per CU; see prefetch_grid).
 hipError_t launch_bf16(Op op, bool wt, const void* X, const void* W, void* Y, int64_t M, int64_t N, int64_t K,
-                       int64_t ldx, int64_t ldw, int64_t ldy, hipStream_t stream);
+                       int64_t ldx, int64_t ldw, int64_t ldy, int cus, hipStream_t stream);
 
 // Opt-in split-K (bf16 / fp16 inputs): chunk sums of k_chunk K values into P
 // ([ceil(K/k_chunk)][M][N] fp32, 16-byte aligned), then their ordered sum into Y.

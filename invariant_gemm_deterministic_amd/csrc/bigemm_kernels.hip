@@ -49,6 +49,7 @@
 
 #include <atomic>
 #include <mutex>
+#include <type_traits>
 
 #include "bigemm_kernels.h"
 
@@ -94,6 +95,29 @@ __device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int
 }
 __device__ __forceinline__ void tile_of(int bid, int nblocks, int tiles_m, int tiles_n, int& tm, int& tn) {
   tile_coords(xcd_order(bid, nblocks), tiles_m, tiles_n, tm, tn);
+}
+
+// A grid padded with prefetch workgroups (prefetch_grid): workgroups 0 ..
+// ntiles - 1 are the tiles, placed exactly as in a grid of ntiles (tile_of);
+// workgroup bid >= ntiles runs on XCD x = bid % kXcds (the same round-robin)
+// and is dealt to one of the cx tiles that XCD holds, round-robin over the
+// XCD's prefetch workgroups. Returns the tile's xcd_order index, with rank /
+// nrank the workgroup's rank among that tile's prefetchers and their number;
+// -1 when the XCD holds no tile.
+__device__ __forceinline__ int prefetch_role(int bid, int nblocks, int ntiles, int& rank, int& nrank) {
+  const int x = bid % kXcds;
+  const int per = ntiles / kXcds, rem = ntiles - per * kXcds;
+  const int cx = per + (x < rem ? 1 : 0);            // tiles on XCD x
+  const int b0 = ntiles + (x - ntiles % kXcds + kXcds) % kXcds;  // first prefetcher on XCD x
+  const int hx = (nblocks - 1 - b0) / kXcds + 1;     // prefetchers on XCD x
+  const int h = (bid - b0) / kXcds;                  // this one's index among them
+  rank = 0;
+  nrank = 0;
+  if (cx == 0) return -1;
+  const int i = h % cx;
+  rank = h / cx;
+  nrank = (hx - 1 - i) / cx + 1;
+  return i < per ? x * per + i : per * kXcds + x;
 }
 
 // 16-byte-chunk swizzle of a 128-byte-row operand tile (X tiles, and the MXFP8
@@ -167,6 +191,76 @@ static_assert(kStagesBf16 >= 3 && kStagesBf16 <= 5, "LDS holds 3 to 5 stages of 
 // K-loop unroll of the bf16 kernel (steps per loop iteration).
 constexpr int kUnrollBf16 = 8 * kStagesBf16;
 
+// A prefetch workgroup of the bf16 / fp16 kernel (prefetch_grid). For the K
+// blocks rank, rank + nrank, ... of its tile it reads one dword of every
+// 128-byte line the tile's own loads of that block touch, so that the line is
+// in the XCD's L2 when the tile's workgroup asks for it; the dwords go to a
+// scratch corner of its LDS and are never read. Slot q = tid: X rows q / 2
+// (q < 256; the block's 128 bytes of a row start 16-byte aligned, so chunks 0
+// and 7 cover its one or two lines), then W: rows (q - 256) / 3 of a [K, N]
+// tile (256 bytes of columns: chunks 0, 8 and 15 cover two or three lines), or
+// rows (q - 256) / 2 of a W^T tile (as X). A chunk is touched only where the
+// tile's own loads read it (row, column and K inside the matrix), so every
+// read stays inside the bytes the tile reads. One load per wave per block.
+//
+// Pacing: block kb is requested no earlier than (kb - kPrefetchLead) block
+// times after the workgroup started (s_memrealtime, 100 MHz), a block time
+// being roughly what the tile's workgroup takes per block when its lines come
+// from L2 (kPrefetchTicks, by the rows the tile multiplies). Running further
+// ahead only evicts lines from the L2 before they are used. The wait is on
+// the clock alone, so it always ends.
+constexpr int kPrefetchLead = 16;
+__device__ __forceinline__ int64_t prefetch_ticks(int rows_valid) {
+  return rows_valid <= 32 ? 24 : (rows_valid <= 64 ? 27 : 33);
+}
+
+template <bool kWT>
+__device__ __forceinline__ void bf16_prefetch(const uint16_t* X, const uint16_t* W, int M, int N, int K,
+                                              int64_t ldx, int64_t ldw, int tiles_m, int tiles_n, uint8_t* scratch,
+                                              int tid) {
+  int rank, nrank, tm, tn;
+  const int t = prefetch_role(blockIdx.x, gridDim.x, tiles_m * tiles_n, rank, nrank);
+  if (t < 0) return;
+  tile_coords(t, tiles_m, tiles_n, tm, tn);
+  const int row0 = tm * 128, col0 = tn * 128;
+  const int rows_valid = min(128, M - row0), cols_valid = min(128, N - col0);
+  const int nkb = (K + kBkBf16 - 1) / kBkBf16;
+  const int wave = __builtin_amdgcn_readfirstlane(tid) >> 6;
+  const bool isx = wave < 4;  // waves 0-3: X lines, waves 4-7: W lines
+  int r, c;                   // row of the tile, 8-element chunk of the block
+  bool ok;                    // the row (and for a [K, N] tile the column chunk) is inside the matrix
+  if (isx || kWT) {
+    r = (tid & 255) >> 1;
+    c = (tid & 1) ? 7 : 0;
+    ok = r < (isx ? rows_valid : cols_valid);
+  } else {
+    const int q = tid - 256;
+    r = q / 3;
+    c = q % 3 == 0 ? 0 : (q % 3 == 1 ? 8 : 15);
+    ok = r < kBkBf16 && c * 8 < cols_valid;
+  }
+  const uint16_t* Xt = X + (int64_t)row0 * ldx;
+  const uint16_t* Wt = kWT ? W + (int64_t)col0 * ldw : W + col0;
+  const int64_t ticks = prefetch_ticks(rows_valid);
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  int j = 0;
+  for (int kb = rank; kb < nkb; kb += nrank, ++j) {
+    const int64_t due = (int64_t)(kb - kPrefetchLead) * ticks;
+    while ((int64_t)(__builtin_amdgcn_s_memrealtime() - t0) < due) __builtin_amdgcn_s_sleep(2);
+    BIGEMM_WAIT_VMCNT(3);  // at most four blocks' loads in flight (the four LDS corners below)
+    const int k0 = kb * kBkBf16;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(isx ? Xt + k0 : (kWT ? Wt + k0 : Wt + (int64_t)k0 * ldw));
+    uint32_t o = kOob;
+    if (isx || kWT) {
+      if (ok && k0 + c * 8 < K) o = (uint32_t)((r * (isx ? ldx : ldw) + c * 8) * 2);
+    } else {
+      if (ok && k0 + r < K) o = (uint32_t)((r * ldw + c * 8) * 2);
+    }
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDS(void, scratch + (j & 3) * 2048 + wave * 256), 4, o, 0, 0, 0);
+  }
+  BIGEMM_WAIT_VMCNT(0);  // no LDS-DMA load may outlive the workgroup
+}
+
 // kSplit: the opt-in split-K variant. The grid is (chunk, tile) pairs; the
 // workgroup runs the same chain over the K blocks of its chunk only
 // (kb_per_split blocks) and stores the fp32 chunk sum at Y + chunk * split_stride.
@@ -200,6 +294,12 @@ void bigemm_bf16_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  if constexpr (!kSplit) {
+    if (__builtin_expect((int)blockIdx.x >= tiles_m * tiles_n, 0)) {  // a prefetch workgroup
+      bf16_prefetch<kWT>(X, W, M, N, K, ldx, ldw, tiles_m, tiles_n, stage0, tid);
+      return;
+    }
+  }
   int tm, tn;
   int kb_first = 0;                               // first K block of this workgroup
   int nkb = (K + kBkBf16 - 1) / kBkBf16;          // K blocks this workgroup accumulates
@@ -212,7 +312,7 @@ void bigemm_bf16_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
     nkb = min(nkb - kb_first, kb_per_split);
     Y = (float*)Y + chunk * split_stride;
   } else {
-    tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+    tile_of(blockIdx.x, tiles_m * tiles_n, tiles_m, tiles_n, tm, tn);
   }
   const int row0 = tm * 128;
   const int col0 = tn * 128;
@@ -302,11 +402,16 @@ void bigemm_bf16_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
 
   // One K block: wait for this stage (kStagesBf16 - 2 younger blocks, 4 loads
   // each, may stay in flight), refill the stage read in the previous block,
-  // then run the MFMA chain on this stage: kk ascending, both fragments per kk.
-  auto step = [&](int kb, const uint8_t* st, uint8_t* refill) {
+  // then run the MFMA chain on this stage: kk ascending, the wave's first kNf
+  // fragments per kk (kNf < 2 only where the tile's rows past M cover whole
+  // 32-row fragments, which are then neither read nor multiplied; every
+  // multiplied fragment runs the same chain as in a full tile).
+  auto step = [&](auto nf, int kb, const uint8_t* st, uint8_t* refill) {
+    constexpr int kNf = decltype(nf)::value;
     BIGEMM_WAIT_VMCNT(4 * (kStagesBf16 - 2));
     BIGEMM_BARRIER();
     issue(kb + kStagesBf16 - 1, refill);
+    if constexpr (kNf == 0) return;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       // kKTail: keep the fragment's K values below K. The lane holds the 8
@@ -320,7 +425,7 @@ void bigemm_bf16_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
       }
       i32x4 a[2];
 #pragma unroll
-      for (int f = 0; f < 2; ++f) {
+      for (int f = 0; f < kNf; ++f) {
         a[f] = *LDS(const i32x4, st + a_addr[f][kk]);
         if constexpr (kKTail) a[f] &= kmask;
       }
@@ -335,7 +440,7 @@ void bigemm_bf16_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
         b = i32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
       }
 #pragma unroll
-      for (int f = 0; f < 2; ++f) acc[f] = mfma_16bit<kF16>(a[f], b, acc[f]);
+      for (int f = 0; f < kNf; ++f) acc[f] = mfma_16bit<kF16>(a[f], b, acc[f]);
     }
   };
 
@@ -352,22 +457,34 @@ void bigemm_bf16_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
   // all of them (vmcnt(0)) before the first step of an iteration; 32 steps
   // make that drain rare (once for K = 2048, twice for K = 4096). The body is
   // about 18 KB of code, inside the instruction cache.
-  for (int kb = 0;;) {
-    bool done = false;
+  auto kloop = [&](auto nf) {
+    for (int kb = 0;;) {
+      bool done = false;
 #pragma unroll
-    for (int u = 0; u < kUnrollBf16; ++u) {
-      step(kb, stg[u % kStagesBf16], stg[(u + kStagesBf16 - 1) % kStagesBf16]);
-      if (++kb == nkb) {
-        done = true;
-        break;
+      for (int u = 0; u < kUnrollBf16; ++u) {
+        step(nf, kb, stg[u % kStagesBf16], stg[(u + kStagesBf16 - 1) % kStagesBf16]);
+        if (++kb == nkb) {
+          done = true;
+          break;
+        }
       }
+      if (done) break;
     }
-    if (done) break;
-  }
+  };
+  // Fragments of the wave that hold a row below M (wave-uniform: the wave
+  // index is read as a scalar). Every wave runs the same loads, waits and
+  // barriers whatever its count.
+  const int wrow0 = (__builtin_amdgcn_readfirstlane(tid) >> 8) * 64;
+  if (rows_valid > wrow0 + 32)
+    kloop(std::integral_constant<int, 2>{});
+  else if (rows_valid > wrow0)
+    kloop(std::integral_constant<int, 1>{});
+  else
+    kloop(std::integral_constant<int, 0>{});
   BIGEMM_WAIT_VMCNT(0);  // no LDS-DMA load may outlive the workgroup
 
   // Epilogue: plain stores (fp32, or its bf16 rounding), masked through the
-  // buffer range check.
+  // buffer range check. Fragments never multiplied hold only rows past M.
   const __amdgpu_buffer_rsrc_t ry =
       make_rsrc((uint8_t*)Y + ((int64_t)row0 * ldy + col0) * (kOutBf16 ? 2 : 4));
 #pragma unroll
@@ -1003,6 +1120,25 @@ hipError_t static_scratch_address(int device, void** out) {
 
 typedef void (*Bf16KernelFn)(const uint16_t*, const uint16_t*, void*, int, int, int, int64_t, int64_t, int64_t, int,
                              int, int, int64_t);
+
+// Prefetch workgroups. With fewer tiles than CUs, each tile's workgroup
+// streams its X and W panels alone, at the rate one CU sustains against HBM
+// latency, while the other CUs idle. When the tiles fill at most half of the
+// CUs and K is long (at least kPrefetchMinBlocks K blocks), the grid is padded
+// to one workgroup per CU: each extra workgroup touches the lines of every
+// nrank-th K block of one tile of its XCD (prefetch_role, bf16_prefetch), a
+// little ahead of the tile's own workgroup, which then finds them in the XCD's
+// L2. They store nothing; the tiles, each tile's arithmetic, and so every
+// output byte are the same as with a grid of the tiles alone. The condition
+// depends on the tile count, which follows M: only which CUs read ahead
+// changes with M, never the work of any output element.
+constexpr int kPrefetchMinBlocks = 32;
+int prefetch_grid(int ntiles, int nkb, int cus) {
+  const int slots = cus / kXcds;
+  if (slots < 2 || 2 * ntiles > slots * kXcds || nkb < kPrefetchMinBlocks) return ntiles;
+  return slots * kXcds;
+}
+
 // The bf16 / fp16 kernel instance for W given as [K, N] (wt false) or [N, K],
 // and for K a multiple of 8 or not (ktail): choices made from the layout and K,
 // never from M.
@@ -1015,16 +1151,18 @@ Bf16KernelFn bf16_kernel_for(bool wt, bool ktail) {
 }
 
 hipError_t launch_bf16(Op op, bool wt, const void* X, const void* W, void* Y, int64_t M, int64_t N, int64_t K,
-                       int64_t ldx, int64_t ldw, int64_t ldy, hipStream_t stream) {
+                       int64_t ldx, int64_t ldw, int64_t ldy, int cus, hipStream_t stream) {
   const int tiles_m = (int)((M + 127) / 128);
   const int tiles_n = (int)((N + 127) / 128);
+  const int ntiles = tiles_m * tiles_n;
+  const int grid = prefetch_grid(ntiles, (int)((K + kBkBf16 - 1) / kBkBf16), cus);
   const bool f16 = op.in == kInF16, obf = op.out == 1 /* BIGEMM_BF16 */;
   const bool kt = K % 8 != 0;
   const Bf16KernelFn kern =
       f16 ? (obf ? bf16_kernel_for<true, true, false>(wt, kt) : bf16_kernel_for<true, false, false>(wt, kt))
           : (obf ? bf16_kernel_for<false, true, false>(wt, kt) : bf16_kernel_for<false, false, false>(wt, kt));
-  hipLaunchKernelGGL(kern, dim3(tiles_m * tiles_n), dim3(kThreadsBf16), 0, stream, (const uint16_t*)X,
-                     (const uint16_t*)W, Y, (int)M, (int)N, (int)K, ldx, ldw, ldy, tiles_m, tiles_n, 0, (int64_t)0);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreadsBf16), 0, stream, (const uint16_t*)X, (const uint16_t*)W, Y,
+                     (int)M, (int)N, (int)K, ldx, ldw, ldy, tiles_m, tiles_n, 0, (int64_t)0);
   return hipGetLastError();
 }
 

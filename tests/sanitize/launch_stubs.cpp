@@ -17,7 +17,7 @@ static hipError_t unreachable(const char* what) {
 
 namespace bigemm {
 hipError_t launch_bf16(Op, bool, const void*, const void*, void*, int64_t, int64_t, int64_t, int64_t, int64_t,
-                       int64_t, hipStream_t) {
+                       int64_t, int, hipStream_t) {
   return unreachable("launch_bf16");
 }
 hipError_t launch_bf16_split(Op, bool, int32_t, const void*, const void*, void*, void*, int64_t, int64_t, int64_t,

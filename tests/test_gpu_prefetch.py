@@ -1,0 +1,141 @@
+"""Products whose grid is padded with prefetch workgroups, through the C ABI.
+
+The bf16 / fp16 kernel pads its grid to one workgroup per CU when the 128 x 128 tiles fill at
+most half of the CUs (at most 128 tiles on the 256-CU MI355X) and K spans at least 32 K blocks
+(K >= 1985). The extra workgroups load K blocks of their XCD's tiles ahead, into their own LDS,
+and store nothing. Checked here, over tile counts from 2 to 128 (XCDs with no tile, XCDs holding
+one tile more than others), K from 32 blocks to 256, K and N not multiples of 8, both W
+layouts, fp16 inputs and bf16 output:
+- parity with the oracle, and integer-exact inputs bit for bit;
+- every row's bytes equal to the same row inside a product of more than 128 tiles (a grid
+  that is not padded), with the rows placed first and last there.
+"""
+import numpy as np
+import pytest
+import torch
+
+import invariant_gemm_deterministic_amd as bg
+import oracle
+from bigemm_inputs import SEED_W, SEED_X, int_bf16, normal_bf16, normal_f16
+from gpu_util import DEV, require_gpu
+
+pytestmark = pytest.mark.gpu
+TOL = oracle.PARITY_TOL
+
+# (M, N, K): tiles
+CASES = [
+    (1, 4096, 4096),     # 32 tiles, 4 per XCD
+    (37, 1000, 2048),    # 8 tiles, one per XCD; 32 K blocks, the fewest that pad
+    (300, 1100, 2112),   # 27 tiles: three XCDs hold one tile more
+    (129, 128, 8192),    # 2 tiles: six XCDs hold none
+    (512, 4096, 4096),   # 128 tiles, the largest padded grid
+    (64, 1024, 16384),   # 8 tiles, 256 K blocks
+    (100, 520, 4099),    # 5 tiles, K not a multiple of 8
+]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def dev_rows(a, dtype=torch.int16):
+    """Device copy of a [R, C] array of 16-bit values in rows of roundup(C, 8) elements
+    (zero padding); returns the [R, C] view."""
+    a = np.ascontiguousarray(a)
+    R, C = a.shape
+    ld = -(-C // 8) * 8
+    buf = torch.zeros((R, ld), dtype=torch.int16, device=DEV)
+    buf[:, :C] = torch.from_numpy(a.view(np.int16)).to(DEV)
+    return buf.view(dtype)[:, :C]
+
+
+def w_operand(W, wt, dtype=torch.int16):
+    """W [K, N] as the kernel operand: [K, N] rows, or the transposed view of [N, K] rows."""
+    return dev_rows(np.ascontiguousarray(W.T), dtype).t() if wt else dev_rows(W, dtype)
+
+
+def unpadded_rows(x, w, out_dtype=None):
+    """The rows of x computed inside a product of more than 128 tiles: x placed first and
+    last among other rows (seeded normal values). Returns the two [M, N] results."""
+    M, K = x.shape
+    N = w.shape[1]
+    tiles_n = -(-N // 128)
+    big = max(128 * (128 // tiles_n + 1), -(-2 * M // 128) * 128)   # tiles_m * tiles_n > 128
+    g = torch.Generator(device=DEV)
+    g.manual_seed(9001)
+    fill = torch.randn((big, K), generator=g, device=DEV)
+    fill = fill.to(torch.bfloat16).view(torch.int16) if x.dtype == torch.int16 else fill.to(x.dtype)
+    buf = torch.zeros((big, x.stride(0)), dtype=x.dtype, device=DEV)
+    buf[:, :K] = fill
+    buf[:M, :K] = x
+    buf[big - M:, :K] = x
+    y = bg.mm(buf[:, :K], w, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return y[:M], y[big - M:]
+
+
+def same_bytes(a, b):
+    if a.dtype == torch.bfloat16:
+        return torch.equal(a.view(torch.int16), b.view(torch.int16))
+    return torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+@pytest.mark.parametrize("M,N,K", CASES)
+def test_prefetch_grid_parity_and_rows(M, N, K):
+    X = normal_bf16(SEED_X, (M, K))
+    W = normal_bf16(SEED_W, (K, N), 0.02)
+    x, w = dev_rows(X), w_operand(W, False)
+    y = bg.mm(x, w)
+    torch.cuda.synchronize()
+    Y, S = oracle.gemm_bf16(X, W)
+    assert oracle.max_normalized_error(y.cpu().numpy(), Y, S) <= TOL
+    first, last = unpadded_rows(x, w)
+    assert same_bytes(y, first) and same_bytes(y, last)
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 1100, 2112), (100, 520, 4099)])
+def test_prefetch_grid_integer_exact(M, N, K):
+    X, W = int_bf16(80, (M, K)), int_bf16(81, (K, N))
+    y = bg.mm(dev_rows(X), w_operand(W, False))
+    torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().numpy().astype(np.float64), oracle.gemm_bf16(X, W, want_s=False))
+
+
+@pytest.mark.parametrize("M,N,K", [(37, 1000, 2048), (100, 520, 4099)])
+def test_prefetch_grid_w_transposed(M, N, K):
+    """W given as [N, K] rows: the same bytes as the [K, N] layout, and as the rows inside
+    an unpadded grid."""
+    X = normal_bf16(82, (M, K))
+    W = normal_bf16(83, (K, N), 0.02)
+    x = dev_rows(X)
+    y = bg.mm(x, w_operand(W, False))
+    yt = bg.mm(x, w_operand(W, True))
+    torch.cuda.synchronize()
+    assert same_bytes(y, yt)
+    first, last = unpadded_rows(x, w_operand(W, True))
+    assert same_bytes(yt, first) and same_bytes(yt, last)
+
+
+@pytest.mark.parametrize("M,N,K", [(129, 128, 8192), (100, 520, 4099)])
+def test_prefetch_grid_f16_and_bf16_out(M, N, K):
+    """fp16 inputs and bf16 output: parity, and rows as in an unpadded grid."""
+    Xh = normal_f16(84, (M, K))
+    Wh = normal_f16(85, (K, N), 0.02)
+    xh, wh = dev_rows(Xh, torch.float16), w_operand(Wh, False, torch.float16)
+    yh = bg.mm(xh, wh)
+    torch.cuda.synchronize()
+    Y, S = oracle.gemm_f16(Xh, Wh)
+    assert oracle.max_normalized_error(yh.cpu().numpy(), Y, S) <= TOL
+    first, last = unpadded_rows(xh, wh)
+    assert same_bytes(yh, first) and same_bytes(yh, last)
+
+    X = normal_bf16(86, (M, K))
+    W = normal_bf16(87, (K, N), 0.02)
+    x, w = dev_rows(X), w_operand(W, False)
+    y16 = bg.mm(x, w, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    Y, S = oracle.gemm_bf16(X, W)
+    assert oracle.max_normalized_error(y16.float().cpu().numpy(), Y, S) <= oracle.PARITY_TOL_BF16_OUT
+    first, last = unpadded_rows(x, w, out_dtype=torch.bfloat16)
+    assert same_bytes(y16, first) and same_bytes(y16, last)
