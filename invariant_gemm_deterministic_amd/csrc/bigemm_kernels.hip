@@ -52,6 +52,7 @@
 #include <type_traits>
 
 #include "bigemm_kernels.h"
+#include "bigemm_tilemap.h"
 
 namespace bigemm {
 
@@ -70,54 +71,9 @@ constexpr int kStageBytes = 2 * kTileBytes;   // X tile + W tile
 constexpr uint32_t kOob = 0x80000000u;        // buffer offset that is always out of range
 constexpr int kNumRecords = 0x7FFFFFFF;       // every in-range offset is below 2^31
 constexpr int kRsrcWord3 = 0x00020000;        // raw buffer, 32-bit data format (CDNA)
-constexpr int kXcds = 8;                      // MI355X dispatches workgroups round-robin over 8 XCDs
-constexpr int kGroupM = 4;                    // tile rows that share W tiles inside one XCD
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, kNumRecords, kRsrcWord3);
-}
-
-// Placement only: undo the round-robin XCD dispatch so that consecutive tiles
-// land on one XCD (its L2 then serves the shared X and W tiles), and walk the
-// tiles in groups of kGroupM tile-rows so that the XCD's concurrent tiles form
-// a compact block.
-__device__ __forceinline__ int xcd_order(int bid, int nblocks) {
-  const int per = nblocks / kXcds;
-  return bid < per * kXcds ? (bid % kXcds) * per + bid / kXcds : bid;
-}
-__device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int& tm, int& tn) {
-  const int group = t / (kGroupM * tiles_n);
-  const int first_m = group * kGroupM;
-  const int gm = min(tiles_m - first_m, kGroupM);
-  const int in = t - group * kGroupM * tiles_n;
-  tm = first_m + in % gm;
-  tn = in / gm;
-}
-__device__ __forceinline__ void tile_of(int bid, int nblocks, int tiles_m, int tiles_n, int& tm, int& tn) {
-  tile_coords(xcd_order(bid, nblocks), tiles_m, tiles_n, tm, tn);
-}
-
-// A grid padded with prefetch workgroups (prefetch_grid): workgroups 0 ..
-// ntiles - 1 are the tiles, placed exactly as in a grid of ntiles (tile_of);
-// workgroup bid >= ntiles runs on XCD x = bid % kXcds (the same round-robin)
-// and is dealt to one of the cx tiles that XCD holds, round-robin over the
-// XCD's prefetch workgroups. Returns the tile's xcd_order index, with rank /
-// nrank the workgroup's rank among that tile's prefetchers and their number;
-// -1 when the XCD holds no tile.
-__device__ __forceinline__ int prefetch_role(int bid, int nblocks, int ntiles, int& rank, int& nrank) {
-  const int x = bid % kXcds;
-  const int per = ntiles / kXcds, rem = ntiles - per * kXcds;
-  const int cx = per + (x < rem ? 1 : 0);            // tiles on XCD x
-  const int b0 = ntiles + (x - ntiles % kXcds + kXcds) % kXcds;  // first prefetcher on XCD x
-  const int hx = (nblocks - 1 - b0) / kXcds + 1;     // prefetchers on XCD x
-  const int h = (bid - b0) / kXcds;                  // this one's index among them
-  rank = 0;
-  nrank = 0;
-  if (cx == 0) return -1;
-  const int i = h % cx;
-  rank = h / cx;
-  nrank = (hx - 1 - i) / cx + 1;
-  return i < per ? x * per + i : per * kXcds + x;
 }
 
 // 16-byte-chunk swizzle of a 128-byte-row operand tile (X tiles, and the MXFP8
@@ -1120,24 +1076,6 @@ hipError_t static_scratch_address(int device, void** out) {
 
 typedef void (*Bf16KernelFn)(const uint16_t*, const uint16_t*, void*, int, int, int, int64_t, int64_t, int64_t, int,
                              int, int, int64_t);
-
-// Prefetch workgroups. With fewer tiles than CUs, each tile's workgroup
-// streams its X and W panels alone, at the rate one CU sustains against HBM
-// latency, while the other CUs idle. When the tiles fill at most half of the
-// CUs and K is long (at least kPrefetchMinBlocks K blocks), the grid is padded
-// to one workgroup per CU: each extra workgroup touches the lines of every
-// nrank-th K block of one tile of its XCD (prefetch_role, bf16_prefetch), a
-// little ahead of the tile's own workgroup, which then finds them in the XCD's
-// L2. They store nothing; the tiles, each tile's arithmetic, and so every
-// output byte are the same as with a grid of the tiles alone. The condition
-// depends on the tile count, which follows M: only which CUs read ahead
-// changes with M, never the work of any output element.
-constexpr int kPrefetchMinBlocks = 32;
-int prefetch_grid(int ntiles, int nkb, int cus) {
-  const int slots = cus / kXcds;
-  if (slots < 2 || 2 * ntiles > slots * kXcds || nkb < kPrefetchMinBlocks) return ntiles;
-  return slots * kXcds;
-}
 
 // The bf16 / fp16 kernel instance for W given as [K, N] (wt false) or [N, K],
 // and for K a multiple of 8 or not (ktail): choices made from the layout and K,
