@@ -307,14 +307,20 @@ void bigemm_bf16_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
   // end (kb >= nkb) is still issued, entirely out of range: it loads zeros
   // into a stage nobody reads again, and keeps every pipeline step the same
   // instruction sequence (so the number of loads in flight is fixed).
-  auto issue = [&](int kb, uint8_t* stage) {
+  // kNx: how many of the wave's two X loads are issued. Load i covers tile rows
+  // 64 i + 8 wave .. + 7; the loop leaves out those whose rows are all past M
+  // (always the last ones). Their LDS rows keep the zeros the prologue's
+  // out-of-range loads wrote into every stage, so the fragments read the same
+  // values as before; the wait counts follow the wave's number of loads.
+  auto issue = [&](auto nx, int kb, uint8_t* stage) {
+    constexpr int kNx = decltype(nx)::value;
     const bool live = kb < nkb;
     const int k0 = live ? kb * kBkBf16 : 0;
     const int kleft = live ? Kr - k0 : 0;
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(Xt + k0);
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(kWT ? Wt + k0 : Wt + (int64_t)k0 * ldw);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < kNx; ++i) {
       const uint32_t o = xk[i] < kleft ? xoff[i] : kOob;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, LDS(void, stage + i * 8192 + wave * 1024), 16, o, 0, 0, 0);
     }
@@ -356,17 +362,18 @@ void bigemm_bf16_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
 
   f32x16 acc[2] = {f32x16{}, f32x16{}};
 
-  // One K block: wait for this stage (kStagesBf16 - 2 younger blocks, 4 loads
-  // each, may stay in flight), refill the stage read in the previous block,
+  // One K block: wait for this stage (kStagesBf16 - 2 younger blocks, 2 + kNx
+  // loads each, may stay in flight), refill the stage read in the previous block,
   // then run the MFMA chain on this stage: kk ascending, the wave's first kNf
   // fragments per kk (kNf < 2 only where the tile's rows past M cover whole
   // 32-row fragments, which are then neither read nor multiplied; every
   // multiplied fragment runs the same chain as in a full tile).
-  auto step = [&](auto nf, int kb, const uint8_t* st, uint8_t* refill) {
+  auto step = [&](auto nf, auto nx, int kb, const uint8_t* st, uint8_t* refill) {
     constexpr int kNf = decltype(nf)::value;
-    BIGEMM_WAIT_VMCNT(4 * (kStagesBf16 - 2));
+    constexpr int kNx = decltype(nx)::value;
+    BIGEMM_WAIT_VMCNT((2 + kNx) * (kStagesBf16 - 2));
     BIGEMM_BARRIER();
-    issue(kb + kStagesBf16 - 1, refill);
+    issue(nx, kb + kStagesBf16 - 1, refill);
     if constexpr (kNf == 0) return;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
@@ -401,24 +408,26 @@ void bigemm_bf16_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
   };
 
   // Prologue: a dummy (entirely out-of-range) fill of the last stage, then
-  // blocks 0 to kStagesBf16 - 2. The dummy makes the loads in flight at the
-  // loop head target the stages in the same order on entry as on every later
-  // iteration.
-  issue(nkb, stg[kStagesBf16 - 1]);
+  // blocks 0 to kStagesBf16 - 2, all with every load (zeros in the rows past M
+  // of every stage). The dummy makes the loads in flight at the loop head
+  // target the stages in the same order on entry as on every later iteration.
+  // A variant issuing fewer loads per block than the prologue only waits for
+  // more than it needs on its first steps.
+  issue(std::integral_constant<int, 2>{}, nkb, stg[kStagesBf16 - 1]);
 #pragma unroll
-  for (int s = 0; s < kStagesBf16 - 1; ++s) issue(s, stg[s]);
+  for (int s = 0; s < kStagesBf16 - 1; ++s) issue(std::integral_constant<int, 2>{}, s, stg[s]);
   // Unrolled by kUnrollBf16 steps (a multiple of kStagesBf16) so that each
   // stage is a fixed LDS object in every step. The compiler cannot track which
   // stage the loads in flight target across the loop back-edge, and waits for
   // all of them (vmcnt(0)) before the first step of an iteration; 32 steps
   // make that drain rare (once for K = 2048, twice for K = 4096). The body is
   // about 18 KB of code, inside the instruction cache.
-  auto kloop = [&](auto nf) {
+  auto kloop = [&](auto nf, auto nx) {
     for (int kb = 0;;) {
       bool done = false;
 #pragma unroll
       for (int u = 0; u < kUnrollBf16; ++u) {
-        step(nf, kb, stg[u % kStagesBf16], stg[(u + kStagesBf16 - 1) % kStagesBf16]);
+        step(nf, nx, kb, stg[u % kStagesBf16], stg[(u + kStagesBf16 - 1) % kStagesBf16]);
         if (++kb == nkb) {
           done = true;
           break;
@@ -427,16 +436,31 @@ void bigemm_bf16_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
       if (done) break;
     }
   };
-  // Fragments of the wave that hold a row below M (wave-uniform: the wave
-  // index is read as a scalar). Every wave runs the same loads, waits and
-  // barriers whatever its count.
-  const int wrow0 = (__builtin_amdgcn_readfirstlane(tid) >> 8) * 64;
-  if (rows_valid > wrow0 + 32)
-    kloop(std::integral_constant<int, 2>{});
-  else if (rows_valid > wrow0)
-    kloop(std::integral_constant<int, 1>{});
-  else
-    kloop(std::integral_constant<int, 0>{});
+  // Per wave (uniform: the wave index is read as a scalar): nf fragments hold
+  // a row below M, nx of its X loads do. Every wave meets the same barriers;
+  // the combinations below are the only ones that occur, and any other would
+  // run the full variant, which is correct for every tile.
+  const int wave_u = __builtin_amdgcn_readfirstlane(tid) >> 6;
+  const int wrow0 = (wave_u >> 2) * 64;
+  const int nf = (rows_valid > wrow0) + (rows_valid > wrow0 + 32);
+  const int nx = (wave_u * 8 < rows_valid) + (64 + wave_u * 8 < rows_valid);
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  const int v = nf * 3 + nx;
+  if (__builtin_expect(v == 8 || (v != 7 && v != 4 && v != 3 && v != 1 && v != 0), 1)) {
+    kloop(I2{}, I2{});  // full tiles (and any other count: all loads, both fragments)
+  } else if (v == 7) {
+    kloop(I2{}, I1{});
+  } else if (v == 4) {
+    kloop(I1{}, I1{});
+  } else if (v == 3) {
+    kloop(I1{}, I0{});
+  } else if (v == 1) {
+    kloop(I0{}, I1{});
+  } else {
+    kloop(I0{}, I0{});
+  }
   BIGEMM_WAIT_VMCNT(0);  // no LDS-DMA load may outlive the workgroup
 
   // Epilogue: plain stores (fp32, or its bf16 rounding), masked through the
