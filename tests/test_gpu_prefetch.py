@@ -1,14 +1,17 @@
-"""Products whose grid is padded with prefetch workgroups, through the C ABI.
+"""Small-M products through the C ABI: grids padded with prefetch workgroups, and tiles whose
+waves skip the fragments and X loads that hold only rows past M.
 
 The bf16 / fp16 kernel pads its grid to one workgroup per CU when the 128 x 128 tiles fill at
 most half of the CUs (at most 128 tiles on the 256-CU MI355X) and K spans at least 32 K blocks
-(K >= 1985). The extra workgroups load K blocks of their XCD's tiles ahead, into their own LDS,
-and store nothing. Checked here, over tile counts from 2 to 128 (XCDs with no tile, XCDs holding
-one tile more than others), K from 32 blocks to 256, K and N not multiples of 8, both W
-layouts, fp16 inputs and bf16 output:
+(K >= 1985). The extra workgroups touch the lines of K blocks of their XCD's tiles ahead and
+store nothing. In a tile with rows past M, each wave runs the K loop for the number of its
+fragments and X loads that hold rows below M. Checked here, over tile counts from 2 to 128 (XCDs
+with no tile, XCDs holding one tile more than others), K from 32 blocks to 256, K and N not
+multiples of 8, every count of rows in a tile from 1 to 130, both W layouts, fp16 inputs and
+bf16 output:
 - parity with the oracle, and integer-exact inputs bit for bit;
 - every row's bytes equal to the same row inside a product of more than 128 tiles (a grid
-  that is not padded), with the rows placed first and last there.
+  that is not padded, every wave on the full-tile loop), with the rows placed first and last.
 """
 import numpy as np
 import pytest
@@ -139,3 +142,47 @@ def test_prefetch_grid_f16_and_bf16_out(M, N, K):
     assert oracle.max_normalized_error(y16.float().cpu().numpy(), Y, S) <= oracle.PARITY_TOL_BF16_OUT
     first, last = unpadded_rows(x, w, out_dtype=torch.bfloat16)
     assert same_bytes(y16, first) and same_bytes(y16, last)
+
+
+def test_every_partial_tile_row_count():
+    """Every count of rows in a tile, 1 to 130 (and 255, 256): the waves choose their K loop from
+    how many of their fragments and X loads hold rows below M (six combinations occur). Each
+    product's rows must equal the same rows of one product of more than 128 tiles (not padded,
+    every wave on the full-tile loop). K = 2048 pads the small grids with prefetch workgroups."""
+    K, N, BIG = 2048, 2048, 1152   # 16 tile columns; 9 x 16 = 144 tiles for the reference
+    X = normal_bf16(90, (BIG, K))
+    W = normal_bf16(91, (K, N), 0.02)
+    x, w = dev_rows(X), w_operand(W, False)
+    ref = bg.mm(x, w)
+    torch.cuda.synchronize()
+    bad = []
+    for m in list(range(1, 131)) + [255, 256]:
+        y = bg.mm(x[:m], w)
+        torch.cuda.synchronize()
+        if not same_bytes(y, ref[:m]):
+            bad.append(m)
+    assert not bad, f"rows differ from the unpadded product at M = {bad}"
+    # the reference itself against the oracle on a sample of rows (every partial count shares them)
+    rows = np.array([0, 1, 31, 32, 33, 63, 64, 65, 96, 97, 127, 128, 129, BIG - 1])
+    Y, S = oracle.gemm_bf16(X[rows], W)
+    assert oracle.max_normalized_error(ref.cpu().numpy()[rows], Y, S) <= TOL
+
+
+@pytest.mark.parametrize("wt,f16", [(True, False), (False, True)])
+def test_partial_tile_row_counts_other_kernels(wt, f16):
+    """The same for W given as [N, K] rows and for fp16 inputs, at the counts where a wave's
+    choice changes (fragment and X-load boundaries)."""
+    K, N, BIG = 2048, 2048, 1152
+    dt = torch.float16 if f16 else torch.int16
+    X = normal_f16(92, (BIG, K)) if f16 else normal_bf16(92, (BIG, K))
+    W = normal_f16(93, (K, N), 0.02) if f16 else normal_bf16(93, (K, N), 0.02)
+    x, w = dev_rows(X, dt), w_operand(W, wt, dt)
+    ref = bg.mm(x, w)
+    torch.cuda.synchronize()
+    bad = []
+    for m in (1, 2, 8, 9, 16, 17, 24, 25, 32, 33, 40, 41, 56, 57, 64, 65, 72, 73, 96, 97, 104, 105, 120, 121, 127, 128):
+        y = bg.mm(x[:m], w)
+        torch.cuda.synchronize()
+        if not same_bytes(y, ref[:m]):
+            bad.append(m)
+    assert not bad, f"rows differ from the unpadded product at M = {bad}"
