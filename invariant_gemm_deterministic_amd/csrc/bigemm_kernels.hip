@@ -167,7 +167,7 @@ constexpr int kUnrollBf16 = 8 * kStagesBf16;
 // the clock alone, so it always ends.
 constexpr int kPrefetchLead = 16;
 __device__ __forceinline__ int64_t prefetch_ticks(int rows_valid) {
-  return rows_valid <= 32 ? 24 : (rows_valid <= 64 ? 27 : 33);
+  return rows_valid <= 32 ? 17 : (rows_valid <= 64 ? 21 : 33);
 }
 
 template <bool kWT>
