@@ -186,3 +186,32 @@ def test_partial_tile_row_counts_other_kernels(wt, f16):
         if not same_bytes(y, ref[:m]):
             bad.append(m)
     assert not bad, f"rows differ from the unpadded product at M = {bad}"
+
+
+def test_random_small_m_shapes():
+    """24 seeded random shapes with few tiles and K of at least 32 blocks (padded grids, every
+    combination of row counts, K and N not multiples of 8, both W layouts, bf16 and fp16 inputs,
+    fp32 and bf16 output): parity with the oracle, and rows equal to the same rows placed first
+    and last in a product of more than 128 tiles."""
+    rng = np.random.default_rng(2026)
+    for case in range(24):
+        M = int(rng.integers(1, 301))
+        N = int(rng.integers(1, 3001))
+        K = int(rng.integers(1985, 6001))
+        wt = bool(rng.integers(0, 2))
+        f16 = bool(rng.integers(0, 2))
+        out_bf16 = bool(rng.integers(0, 2))
+        dt = torch.float16 if f16 else torch.int16
+        gen = normal_f16 if f16 else normal_bf16
+        X = gen(1000 + case, (M, K))
+        W = gen(2000 + case, (K, N), 0.02)
+        x, w = dev_rows(X, dt), w_operand(W, wt, dt)
+        odt = torch.bfloat16 if out_bf16 else None
+        y = bg.mm(x, w, out_dtype=odt)
+        torch.cuda.synchronize()
+        Y, S = (oracle.gemm_f16 if f16 else oracle.gemm_bf16)(X, W)
+        tol = oracle.PARITY_TOL_BF16_OUT if out_bf16 else TOL
+        label = f"case {case}: M={M} N={N} K={K} wt={wt} f16={f16} bf16_out={out_bf16}"
+        assert oracle.max_normalized_error(y.float().cpu().numpy(), Y, S) <= tol, label
+        first, last = unpadded_rows(x, w, out_dtype=odt)
+        assert same_bytes(y, first) and same_bytes(y, last), label
