@@ -10,6 +10,9 @@
  * every shape uses. This library is that recipe on CDNA4: one fixed tile
  * configuration per input type, the K blocks walked in ascending order by a
  * single workgroup, one MFMA shape at every M, no atomics, no workspace.
+ * (When a bf16 / fp16 product has few tiles and a long K, otherwise idle CUs
+ * also run workgroups that only read the tiles' next K blocks into the L2
+ * cache; they store nothing and change no output byte.)
  * The same rules give the other entry points below: handles that take W as
  * [N, K] rows (a linear layer's weight layout) with the same output bytes, an
  * opt-in split-K whose split count follows K only, a batch-invariant RMSNorm,
@@ -171,8 +174,8 @@ BIGEMM_API bigemm_status bigemm_run(bigemm_t h, int64_t M, int64_t N, int64_t K,
  * same call repeated gives the same bytes. The bytes differ from those of an
  * unsplit handle whenever K > k_chunk (another fixed summation tree); with
  * K <= k_chunk they are identical. The point is occupancy: at small M the
- * unsplit kernel has ceil(M/128)*ceil(N/128) workgroups, this one that many
- * times the chunk count.
+ * unsplit kernel has ceil(M/128)*ceil(N/128) tiles, each reduced by one
+ * workgroup, this one that many workgroups times the chunk count.
  * Returns BIGEMM_ERR_ARG for a bad k_chunk, BIGEMM_ERR_UNSUPPORTED for other
  * descriptors or devices. Run it with bigemm_run_ws (bigemm_run returns
  * BIGEMM_ERR_ARG on such a handle: it needs a workspace).
