@@ -560,7 +560,14 @@ void bigemm_mxfp8_kernel(const uint8_t* __restrict__ X, const uint8_t* __restric
   const uint8_t* Xt = X + (int64_t)row0 * ldx;
   const uint8_t* Wt = kWT ? W + (int64_t)col0 * ldw : W + col0;
 
-  auto issue = [&](int kb, uint8_t* stage) {
+  // The 8 LDS-DMA loads of K block kb into `stage` (a block past the end is
+  // issued entirely out of range, as in the bf16 kernel). kNx: how many of the
+  // wave's four X loads are issued. Load i covers tile rows 32 i + 8 wave .. + 7;
+  // the loop leaves out those whose rows are all past M (always the last ones).
+  // Their LDS rows keep the zeros the prologue's out-of-range loads wrote into
+  // every stage; the wait counts follow the wave's number of loads.
+  auto issue = [&](auto nx, int kb, uint8_t* stage) {
+    constexpr int kNx = decltype(nx)::value;
     const bool live = kb < nkb;
     const int k0 = live ? kb * kBkMx : 0;
     const int kleft = live ? K - k0 : 0;
@@ -569,7 +576,7 @@ void bigemm_mxfp8_kernel(const uint8_t* __restrict__ X, const uint8_t* __restric
     uint8_t* sx = stage;
     uint8_t* sw = stage + kTileBytes;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kNx; ++i) {
       const uint32_t o = xk[i] < kleft ? xoff[i] : kOob;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, LDS(void, sx + i * 4096 + wave * 1024), 16, o, 0, 0, 0);
     }
@@ -655,13 +662,15 @@ void bigemm_mxfp8_kernel(const uint8_t* __restrict__ X, const uint8_t* __restric
       }
     }
   };
-  // X scales, byte path: one byte per lane, fragment and step.
-  auto load_xscales = [&](int kb, int (&sa)[2][2]) {
+  // X scales, byte path: one byte per lane, fragment and step, for the first
+  // kNf fragments.
+  auto load_xscales = [&](auto nf, int kb, int (&sa)[2][2]) {
+    constexpr int kNf = decltype(nf)::value;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const int blk = kb * 4 + kk * 2 + g;
 #pragma unroll
-      for (int f = 0; f < 2; ++f) {
+      for (int f = 0; f < kNf; ++f) {
         const uint32_t oa = blk < xs_lim[f] ? xs_base[f] + (uint32_t)blk : kOob;
         sa[f][kk] = __builtin_amdgcn_raw_buffer_load_b8(rxs, oa, 0, 0);
       }
@@ -732,25 +741,39 @@ void bigemm_mxfp8_kernel(const uint8_t* __restrict__ X, const uint8_t* __restric
   // block of a group (its buffer was last read in the previous block, before
   // this step's barrier). Byte path: each block's scale loads are issued just
   // before its LDS-DMA loads, kStagesMx - 1 blocks ahead, so the wait for this
-  // block's DMA also covers its scales. Younger than this block's DMA are the
-  // next kStagesMx - 2 blocks' DMA loads (and byte-path scale loads); a scale
-  // group in flight only makes the wait cover more than it needs to. Then the
-  // stage read in the previous block is refilled and the MFMA chain runs on
-  // this stage: kk ascending. u is the step's position in the unrolled loop.
-  auto step = [&](int kb, int u, const uint8_t* st, uint8_t* refill, int (&sac)[2][2], const int (&sbc)[2][2],
-                  int (&san)[2][2], int (&sbn)[2][2]) {
-    BIGEMM_WAIT_VMCNT((kStaged ? 8 : 16) * (kStagesMx - 2));
+  // block's DMA also covers its scales. Younger than this block's loads are the
+  // next kStagesMx - 2 blocks' loads (4 + kNx DMA loads each, and 8 byte-path
+  // scale loads); a scale group in flight only makes the wait cover more than it
+  // needs to. Then the stage read in the previous block is refilled and the
+  // MFMA chain runs on this stage: kk ascending, the wave's first kNf row
+  // fragments (kNf < 2 only where the tile's rows past M cover whole 32-row
+  // fragments, which are then neither read nor multiplied; every multiplied
+  // fragment runs the same chain as in a full tile). u is the step's position
+  // in the unrolled loop.
+  auto step = [&](auto nf, auto nx, f32x16 (&acc)[2][2], int kb, int u, const uint8_t* st, uint8_t* refill,
+                  int (&sac)[2][2], const int (&sbc)[2][2], int (&san)[2][2],
+                  int (&sbn)[2][2]) __attribute__((always_inline)) {
+    constexpr int kNf = decltype(nf)::value;
+    constexpr int kNx = decltype(nx)::value;
+    // Byte path: only the scale loads whose values the wave multiplies are
+    // issued (an unused load could be dropped by the compiler, and the count
+    // below must be exact): 2 kNf X bytes and 4 W bytes per block, none if
+    // kNf = 0.
+    constexpr int kScaleLoads = kStaged ? 0 : (kNf > 0 ? 4 + 2 * kNf : 0);
+    BIGEMM_WAIT_VMCNT((4 + kNx + kScaleLoads) * (kStagesMx - 2));
     BIGEMM_BARRIER();
     const int nb = kb + kStagesMx - 1;
     // u is a multiple of kScaleGroup exactly where kb is (kUnroll is a multiple
-    // of two groups and the loop starts at kb = 0).
+    // of two groups and the loop starts at kb = 0). Every wave issues its share
+    // of the scale group, whatever it multiplies.
     if (kStaged) {
       if (u % kScaleGroup == 0) issue_scales(kb / kScaleGroup + 1, scl[(u / kScaleGroup + 1) % 2]);
-    } else {
-      load_xscales(nb, san);
+    } else if constexpr (kNf > 0) {
+      load_xscales(nf, nb, san);
       load_wscales(nb, sbn);
     }
-    issue(nb, refill);
+    issue(nx, nb, refill);
+    if constexpr (kNf == 0) return;
     int sal[2][2], sbl[2][2];
     if (kStaged) read_scales(u % kScaleGroup, scl[(u / kScaleGroup) % 2], sal, sbl);
 #pragma unroll
@@ -758,9 +781,11 @@ void bigemm_mxfp8_kernel(const uint8_t* __restrict__ X, const uint8_t* __restric
       i32x8 a[2], b[2];
 #pragma unroll
       for (int f = 0; f < 2; ++f) {
-        const i32x4 a0 = *LDS(const i32x4, st + a_addr[f][kk][0]);
-        const i32x4 a1 = *LDS(const i32x4, st + a_addr[f][kk][1]);
-        a[f] = i32x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+        if (f < kNf) {
+          const i32x4 a0 = *LDS(const i32x4, st + a_addr[f][kk][0]);
+          const i32x4 a1 = *LDS(const i32x4, st + a_addr[f][kk][1]);
+          a[f] = i32x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+        }
         if constexpr (kWT) {
           const i32x4 b0 = *LDS(const i32x4, st + bt_addr[f][kk][0]);
           const i32x4 b1 = *LDS(const i32x4, st + bt_addr[f][kk][1]);
@@ -774,7 +799,7 @@ void bigemm_mxfp8_kernel(const uint8_t* __restrict__ X, const uint8_t* __restric
         }
       }
 #pragma unroll
-      for (int fm = 0; fm < 2; ++fm)
+      for (int fm = 0; fm < kNf; ++fm)
 #pragma unroll
         for (int fn = 0; fn < 2; ++fn)
           acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
@@ -788,51 +813,92 @@ void bigemm_mxfp8_kernel(const uint8_t* __restrict__ X, const uint8_t* __restric
   // their scales. The dummy makes the loads in
   // flight at the loop head target the stages in the same order on entry as on
   // every later iteration.
+  // The prologue issues every load (zeros in the rows past M of every stage); a
+  // variant issuing fewer loads per block only waits for more than it needs on
+  // its first steps.
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I4 = std::integral_constant<int, 4>;
   if (kStaged) issue_scales(0, scl[0]);
-  issue(nkb, stg[kStagesMx - 1]);
+  issue(I4{}, nkb, stg[kStagesMx - 1]);
 #pragma unroll
   for (int s = 0; s < kStagesMx - 1; ++s) {
     if (!kStaged) {
-      load_xscales(s, sa[s]);
+      load_xscales(I2{}, s, sa[s]);
       load_wscales(s, sb[s]);
     }
-    issue(s, stg[s]);
+    issue(I4{}, s, stg[s]);
   }
   // Unrolled by kUnroll so that each stage and scale slot is fixed in every
   // step. (The compiler cannot track which stage the loads in flight
   // target across the loop back-edge and drains them before the first step of
   // an iteration; a longer body makes that the exception.)
-  for (int kb = 0;;) {
-    bool done = false;
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int c = u % kStagesMx, n = (u + kStagesMx - 1) % kStagesMx;
-      step(kb, u, stg[c], stg[n], sa[c], sb[c], sa[n], sb[n]);
-      if (++kb == nkb) {
-        done = true;
-        break;
-      }
-    }
-    if (done) break;
-  }
-  BIGEMM_WAIT_VMCNT(0);  // no LDS-DMA load may outlive the workgroup
-
+  // Each variant holds its own accumulators and stores its own fragments
+  // (plain stores, masked through the buffer range check; a wave with kNf = 0
+  // holds only rows past M and stores nothing).
   const __amdgpu_buffer_rsrc_t ry =
       make_rsrc((uint8_t*)Y + ((int64_t)row0 * ldy + col0) * (kOutBf16 ? 2 : 4));
+  auto kloop = [&](auto nf, auto nx) __attribute__((always_inline)) {
+    constexpr int kNf = decltype(nf)::value;
+    for (int kb = 0;;) {
+      bool done = false;
+      // Keep the accumulators in AGPRs across the back edge: with several K
+      // loops in the kernel the register allocator otherwise carries them in
+      // VGPRs and copies all 64 registers out and back at every iteration.
 #pragma unroll
-  for (int fm = 0; fm < 2; ++fm)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int fn = 0; fn < 2; ++fn)
+        for (int j = 0; j < 2; ++j) asm volatile("" : "+a"(acc[i][j]));
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int rl = wm * 64 + fm * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        const int cl = wn * 64 + fn * 32 + (lane & 31);
-        // Copy the element out first: bit-casting an ext_vector element
-        // expression directly reads element 0 with this compiler.
-        const float v = acc[fm][fn][r];
-        store_out<kOutBf16>(ry, rl < rows_valid && cl < cols_valid, (uint32_t)(rl * ldy + cl),
-                            __builtin_bit_cast(uint32_t, v));
+      for (int u = 0; u < kUnroll; ++u) {
+        const int c = u % kStagesMx, n = (u + kStagesMx - 1) % kStagesMx;
+        step(nf, nx, acc, kb, u, stg[c], stg[n], sa[c], sb[c], sa[n], sb[n]);
+        if (++kb == nkb) {
+          done = true;
+          break;
+        }
       }
+      if (done) break;
+    }
+    BIGEMM_WAIT_VMCNT(0);  // no LDS-DMA load may outlive the workgroup
+#pragma unroll
+    for (int fm = 0; fm < kNf; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < 2; ++fn)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rl = wm * 64 + fm * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+          const int cl = wn * 64 + fn * 32 + (lane & 31);
+          // Copy the element out first: bit-casting an ext_vector element
+          // expression directly reads element 0 with this compiler.
+          const float v = acc[fm][fn][r];
+          store_out<kOutBf16>(ry, rl < rows_valid && cl < cols_valid, (uint32_t)(rl * ldy + cl),
+                              __builtin_bit_cast(uint32_t, v));
+        }
+  };
+  // Per wave (uniform: the wave index is read as a scalar): nf of its row
+  // fragments and nx of its X loads hold a row below M. Only tiles of at most
+  // 64 rows get a reduced loop; a wave may run a variant with more fragments or
+  // loads than it needs (the extra loads read zeros, the extra fragments are
+  // never stored), so six loops cover every count, as in the bf16 kernel.
+  const int wave_u = __builtin_amdgcn_readfirstlane(tid) >> 6;
+  const int wrow0 = (wave_u >> 1) * 64;
+  const int nf = (rows_valid > wrow0) + (rows_valid > wrow0 + 32);
+  const int nx = (wave_u * 8 < rows_valid) + (32 + wave_u * 8 < rows_valid);
+  if (__builtin_expect(rows_valid > 64, 1)) {
+    kloop(I2{}, I4{});  // full tiles (and every tile of more than 64 rows)
+  } else if (nf == 2) {
+    kloop(I2{}, I2{});
+  } else if (nf == 1) {
+    kloop(I1{}, I1{});
+  } else if (nx == 2) {
+    kloop(I0{}, I2{});
+  } else if (nx == 1) {
+    kloop(I0{}, I1{});
+  } else {
+    kloop(I0{}, I0{});
+  }
 }
 
 // ------------------------------------------------------------------------ int8
