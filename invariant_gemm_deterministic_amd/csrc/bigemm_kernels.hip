@@ -958,15 +958,19 @@ void bigemm_i8_kernel(const uint8_t* __restrict__ X, const uint8_t* __restrict__
   const uint8_t* Xt = X + (int64_t)row0 * ldx;
   const uint8_t* Wt = kWT ? W + (int64_t)col0 * ldw : W + col0;
 
-  // The 8 LDS-DMA loads of K block kb (blocks past the end load zeros).
-  auto issue = [&](int kb, uint8_t* stage) {
+  // The LDS-DMA loads of K block kb (blocks past the end load zeros). kNx: how
+  // many of the wave's four X loads are issued; load i covers tile rows
+  // 32 i + 8 wave .. + 7, and those whose rows are all past M are left out
+  // (their LDS rows keep the zeros the prologue wrote), as in the MXFP8 kernel.
+  auto issue = [&](auto nx, int kb, uint8_t* stage) {
+    constexpr int kNx = decltype(nx)::value;
     const bool live = kb < nkb;
     const int k0 = live ? kb * kBkI8 : 0;
     const int kleft = live ? K - k0 : 0;
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(Xt + k0);
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(kWT ? Wt + k0 : Wt + (int64_t)k0 * ldw);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kNx; ++i) {
       const uint32_t o = xk[i] < kleft ? xoff[i] : kOob;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, LDS(void, stage + i * 4096 + wave * 1024), 16, o, 0, 0, 0);
     }
@@ -1012,18 +1016,23 @@ void bigemm_i8_kernel(const uint8_t* __restrict__ X, const uint8_t* __restrict__
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = i32x16{};
 
-  // One K block: wait for this stage (the next block's 8 loads may stay in
-  // flight), refill the stage read in the previous block, MFMA chain kk ascending.
-  auto step = [&](int kb, const uint8_t* st, uint8_t* refill) {
-    BIGEMM_WAIT_VMCNT(8 * (kStagesI8 - 2));
+  // One K block: wait for this stage (the next blocks' 4 + kNx loads each may
+  // stay in flight), refill the stage read in the previous block, MFMA chain kk
+  // ascending over the wave's first kNf row fragments (kNf < 2 only where the
+  // tile's rows past M cover whole 32-row fragments).
+  auto step = [&](auto nf, auto nx, int kb, const uint8_t* st, uint8_t* refill) __attribute__((always_inline)) {
+    constexpr int kNf = decltype(nf)::value;
+    constexpr int kNx = decltype(nx)::value;
+    BIGEMM_WAIT_VMCNT((4 + kNx) * (kStagesI8 - 2));
     BIGEMM_BARRIER();
-    issue(kb + kStagesI8 - 1, refill);
+    issue(nx, kb + kStagesI8 - 1, refill);
+    if constexpr (kNf == 0) return;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       i32x4 a[2], b[2];
 #pragma unroll
       for (int f = 0; f < 2; ++f) {
-        a[f] = *LDS(const i32x4, st + a_addr[f][kk]);
+        if (f < kNf) a[f] = *LDS(const i32x4, st + a_addr[f][kk]);
         if constexpr (kWT) {
           b[f] = *LDS(const i32x4, st + bt_addr[f][kk]);
         } else {
@@ -1033,42 +1042,77 @@ void bigemm_i8_kernel(const uint8_t* __restrict__ X, const uint8_t* __restrict__
         }
       }
 #pragma unroll
-      for (int fm = 0; fm < 2; ++fm)
+      for (int fm = 0; fm < kNf; ++fm)
 #pragma unroll
         for (int fn = 0; fn < 2; ++fn)
           acc[fm][fn] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[fm], b[fn], acc[fm][fn], 0, 0, 0);
     }
   };
 
-  issue(nkb, stg[kStagesI8 - 1]);
+  // Prologue with every load (zeros in the rows past M of every stage).
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I4 = std::integral_constant<int, 4>;
+  issue(I4{}, nkb, stg[kStagesI8 - 1]);
 #pragma unroll
-  for (int s2 = 0; s2 < kStagesI8 - 1; ++s2) issue(s2, stg[s2]);
-  for (int kb = 0;;) {
-    bool done = false;
-#pragma unroll
-    for (int u = 0; u < 2 * kStagesI8; ++u) {
-      step(kb, stg[u % kStagesI8], stg[(u + kStagesI8 - 1) % kStagesI8]);
-      if (++kb == nkb) {
-        done = true;
-        break;
-      }
-    }
-    if (done) break;
-  }
-  BIGEMM_WAIT_VMCNT(0);  // no LDS-DMA load may outlive the workgroup
-
+  for (int s2 = 0; s2 < kStagesI8 - 1; ++s2) issue(I4{}, s2, stg[s2]);
+  // Unrolled 8 times the stage count, so that the compiler's drain of the loads
+  // in flight at the loop head (it cannot tell which stage they target) comes
+  // once per 24 blocks. Each variant stores its own fragments.
   const __amdgpu_buffer_rsrc_t ry = make_rsrc(Y + (int64_t)row0 * ldy + col0);
+  auto kloop = [&](auto nf, auto nx) __attribute__((always_inline)) {
+    constexpr int kNf = decltype(nf)::value;
+    for (int kb = 0;;) {
+      bool done = false;
+      // Keep the accumulators in AGPRs across the back edge (see the MXFP8 kernel).
 #pragma unroll
-  for (int fm = 0; fm < 2; ++fm)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int fn = 0; fn < 2; ++fn)
+        for (int j = 0; j < 2; ++j) asm volatile("" : "+a"(acc[i][j]));
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int rl = wm * 64 + fm * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        const int cl = wn * 64 + fn * 32 + (lane & 31);
-        const int v = acc[fm][fn][r];
-        store_out<false>(ry, rl < rows_valid && cl < cols_valid, (uint32_t)(rl * ldy + cl), (uint32_t)v);
+      for (int u = 0; u < 8 * kStagesI8; ++u) {
+        step(nf, nx, kb, stg[u % kStagesI8], stg[(u + kStagesI8 - 1) % kStagesI8]);
+        if (++kb == nkb) {
+          done = true;
+          break;
+        }
       }
+      if (done) break;
+    }
+    BIGEMM_WAIT_VMCNT(0);  // no LDS-DMA load may outlive the workgroup
+#pragma unroll
+    for (int fm = 0; fm < kNf; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < 2; ++fn)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rl = wm * 64 + fm * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+          const int cl = wn * 64 + fn * 32 + (lane & 31);
+          const int v = acc[fm][fn][r];
+          store_out<false>(ry, rl < rows_valid && cl < cols_valid, (uint32_t)(rl * ldy + cl), (uint32_t)v);
+        }
+  };
+  // Per wave, as in the MXFP8 kernel: tiles of more than 64 rows run the full
+  // loop; in smaller ones each wave runs the smallest of six loops that covers
+  // its fragments and X loads holding a row below M.
+  const int wave_u = __builtin_amdgcn_readfirstlane(tid) >> 6;
+  const int wrow0 = (wave_u >> 1) * 64;
+  const int nf = (rows_valid > wrow0) + (rows_valid > wrow0 + 32);
+  const int nx = (wave_u * 8 < rows_valid) + (32 + wave_u * 8 < rows_valid);
+  if (__builtin_expect(rows_valid > 64, 1)) {
+    kloop(I2{}, I4{});
+  } else if (nf == 2) {
+    kloop(I2{}, I2{});
+  } else if (nf == 1) {
+    kloop(I1{}, I1{});
+  } else if (nx == 2) {
+    kloop(I0{}, I2{});
+  } else if (nx == 1) {
+    kloop(I0{}, I1{});
+  } else {
+    kloop(I0{}, I0{});
+  }
 }
 
 // ------------------------------------------------------------- split-K merge

@@ -1,14 +1,15 @@
-"""MXFP8 products with tiles of at most 64 rows, through the C ABI.
+"""MXFP8 and int8 products with tiles of at most 64 rows, through the C ABI.
 
-In such a tile each wave of the MXFP8 kernel runs the K loop for the number of its 32-row fragments
-and of its X loads that hold a row below M: fragments holding only rows past M are neither read nor
-multiplied, and X loads of rows past M are left out (six loops, chosen per wave; tiles of more than
-64 rows run the full loop). Checked here for every count of rows in a tile from 1 to 130 (and 255),
-for both scale-load paths (staged: scale rows 16-byte aligned and K a multiple of 512; byte loads: any
-other layout), W as [K, N] and as [N, K] rows, fp32 and bf16 output:
-- every row's bytes equal the same row computed inside a full tile;
-- parity with the oracle on the reference rows;
-- seeded random shapes against the oracle and against rows inside a full tile.
+In such a tile each wave of the MXFP8 and int8 kernels (4 waves of 64 x 64 outputs) runs the K loop
+for the number of its 32-row fragments and of its X loads that hold a row below M: fragments holding
+only rows past M are neither read nor multiplied, and X loads of rows past M are left out (six loops,
+chosen per wave; tiles of more than 64 rows run the full loop). Checked here for every count of rows in
+a tile from 1 to 130 (and 255):
+- MXFP8, both scale-load paths (staged: scale rows 16-byte aligned and K a multiple of 512; byte loads:
+  any other layout), W as [K, N] and as [N, K] rows, fp32 and bf16 output: every row's bytes equal the
+  same row computed inside a full tile; parity with the oracle on the reference rows; seeded random
+  shapes against the oracle and against rows inside a full tile;
+- int8, both W layouts: every row equal to numpy's exact int64 product.
 """
 import numpy as np
 import pytest
@@ -135,3 +136,24 @@ def test_mxfp8_random_small_m_shapes():
         Y, S = oracle.gemm_mxfp8(X[:M], W, XS[:M], WS)
         assert oracle.max_normalized_error(y.cpu().numpy(), Y, S) <= TOL, label
         assert same_bytes(y, big[:M]), label
+
+
+@pytest.mark.parametrize("wt", [False, True])
+def test_int8_every_partial_tile_row_count(wt):
+    """int8 -> int32: every count of rows in a tile, 1 to 130 and 255, equal to the exact product
+    (K * 127^2 < 2^31), W as [K, N] and as [N, K] rows; N with a ragged tile column."""
+    K, N, BIG = 2048, 304, 256
+    rng = np.random.default_rng(140)
+    X = rng.integers(-128, 128, size=(BIG, K)).astype(np.int8)
+    W = rng.integers(-128, 128, size=(K, N)).astype(np.int8)
+    exact = X.astype(np.int64) @ W.astype(np.int64)
+    x = rows_u8(X.view(np.uint8), K).view(torch.int8)
+    w = (rows_u8(np.ascontiguousarray(W.T).view(np.uint8), K).view(torch.int8).t() if wt
+         else rows_u8(W.view(np.uint8), up16(N)).view(torch.int8))
+    bad = []
+    for m in list(range(1, 131)) + [255]:
+        y = bg.mm(x[:m], w)
+        torch.cuda.synchronize()
+        if not np.array_equal(y.cpu().numpy().astype(np.int64), exact[:m]):
+            bad.append(m)
+    assert not bad, f"rows differ from the exact product at M = {bad}"
