@@ -742,9 +742,10 @@ void bigemm_mxfp8_kernel(const uint8_t* __restrict__ X, const uint8_t* __restric
   // this step's barrier). Byte path: each block's scale loads are issued just
   // before its LDS-DMA loads, kStagesMx - 1 blocks ahead, so the wait for this
   // block's DMA also covers its scales. Younger than this block's loads are the
-  // next kStagesMx - 2 blocks' loads (4 + kNx DMA loads each, and 8 byte-path
-  // scale loads); a scale group in flight only makes the wait cover more than it
-  // needs to. Then the stage read in the previous block is refilled and the
+  // next kStagesMx - 2 blocks' loads (4 + kNx DMA loads each, and on the byte
+  // path the wave's scale loads); a scale group in flight, or the prologue's
+  // full set of loads, only makes the wait cover more than it needs to. Then
+  // the stage read in the previous block is refilled and the
   // MFMA chain runs on this stage: kk ascending, the wave's first kNf row
   // fragments (kNf < 2 only where the tile's rows past M cover whole 32-row
   // fragments, which are then neither read nor multiplied; every multiplied
