@@ -12,7 +12,9 @@ ABI with inputs resident in HBM. Also reported:
   bound max(flops / MFMA peak, algorithmic bytes / HBM peak);
 * ``other_types_k4096_n4096``: the MXFP8 kernel (E4M3, K-varying E8M0 scales),
   fp16 inputs, bf16 output and int8 inputs at M = 1024 and 4096, each against
-  its dense MFMA peak (context, not the metric); for bf16, MXFP8 and int8 also
+  its dense MFMA peak (context, not the metric); MXFP8 and int8 also at M = 1
+  and 64 with a cold last-level cache (W rotating over copies, as in
+  ``m_sweep``), with algorithmic HBM GB/s; for bf16, MXFP8 and int8 also
   W given as [N, K] rows (MXFP8 scales [N, K/32]), timed in blocks of
   back-to-back launches alternating with blocks of the [K, N] call (median
   over four rounds); ``w_transposed_byte_diffs`` compares the [N, K]-row bf16
@@ -107,6 +109,14 @@ def _time_point(torch, stream, fn, reps, warm_s=None):
     """One figure of the bench: warm for warm_s seconds, then the median of BLOCKS blocks."""
     _warm(torch, fn, warm_s)
     return _blocks(torch, stream, fn, reps)[0]
+
+
+def _small_m_entry(kind, m, N, K, t, byts, peak):
+    """A small-M point of the other types (t in ms per call; byts the algorithmic bytes)."""
+    f = 2.0 * m * N * K
+    return {"kind": kind, "M": m, "us": round(t * 1e3, 2), "tflops": round(f / (t * 1e-3) / 1e12, 1),
+            "pct_peak": round(100 * f / (t * 1e-3) / 1e12 / peak, 2),
+            "hbm_gbs_algorithmic": round(byts / (t * 1e-3) / 1e9, 0), "cold_llc": True}
 
 
 def _time_ab(torch, stream, fa, fb, reps=10, rounds=BLOCKS):
@@ -445,6 +455,17 @@ def main():
             for kind, t in (("mxfp8", ta), ("mxfp8_w_transposed", tb)):
                 mx.append({"kind": kind, "M": m, "us": round(t * 1e3, 2), "tflops": round(f / (t * 1e-3) / 1e12, 1),
                            "pct_peak": round(100 * f / (t * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 1)})
+        # small M with a cold last-level cache (W and its scales rotate over copies, as in the sweep)
+        for m in (1, 64):
+            byts = m * K + K * N + (m * K + K * N) // 32 + 4 * m * N
+            nsets = max(2, int(np.ceil(600e6 / byts)))
+            Wc = [Wm] + [Wm.clone() for _ in range(nsets - 1)]
+            WSc = [WS] + [WS.clone() for _ in range(nsets - 1)]
+            xm, xs, ym = Xm[:m], XS[:m], Y[:m]
+            t = _time_point(torch, stream, lambda i: bg.mm(xm, Wc[i % nsets], xs, WSc[i % nsets], out=ym),
+                            max(20, 2 * nsets))
+            mx.append(_small_m_entry("mxfp8", m, N, K, t, byts, PEAK_FP8_TFLOPS))
+            del Wc, WSc
         del Xm, Wm, XS, WS, WmT, WST
         # fp16 inputs and int8 inputs on the same tile skeleton, and bf16 output (context)
         from bigemm_inputs import int_i8, normal_f16
@@ -481,6 +502,14 @@ def main():
                     mx.append({"kind": name, "M": m, "us": round(t * 1e3, 2),
                                "tflops": round(f / (t * 1e-3) / 1e12, 1),
                                "pct_peak": round(100 * f / (t * 1e-3) / 1e12 / peak, 1)})
+        for m in (1, 64):   # int8 at small M, cold last-level cache
+            byts = m * K + K * N + 4 * m * N
+            nsets = max(2, int(np.ceil(600e6 / byts)))
+            Wc = [Wi] + [Wi.clone() for _ in range(nsets - 1)]
+            xi, yi = Xi[:m], Yi[:m]
+            t = _time_point(torch, stream, lambda i: bg.mm(xi, Wc[i % nsets], out=yi), max(20, 2 * nsets))
+            mx.append(_small_m_entry("i8", m, N, K, t, byts, PEAK_I8_TOPS))
+            del Wc
         del X16, W16, Xi, Wi, WiT, Yi, Yb, WT
 
     line = {
