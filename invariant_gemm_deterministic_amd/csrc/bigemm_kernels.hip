@@ -312,6 +312,7 @@ void bigemm_bf16_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
   // (always the last ones). Their LDS rows keep the zeros the prologue's
   // out-of-range loads wrote into every stage, so the fragments read the same
   // values as before; the wait counts follow the wave's number of loads.
+  const int wave_s = __builtin_amdgcn_readfirstlane(tid) >> 6;  // the LDS-DMA bases (M0) stay scalar
   auto issue = [&](auto nx, int kb, uint8_t* stage) {
     constexpr int kNx = decltype(nx)::value;
     const bool live = kb < nkb;
@@ -322,12 +323,12 @@ void bigemm_bf16_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
 #pragma unroll
     for (int i = 0; i < kNx; ++i) {
       const uint32_t o = xk[i] < kleft ? xoff[i] : kOob;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, LDS(void, stage + i * 8192 + wave * 1024), 16, o, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, LDS(void, stage + i * 8192 + wave_s * 1024), 16, o, 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const uint32_t o = wk[i] < kleft ? woff[i] : kOob;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, LDS(void, stage + kTileBytes + i * 8192 + wave * 1024), 16, o,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, LDS(void, stage + kTileBytes + i * 8192 + wave_s * 1024), 16, o,
                                                 0, 0, 0);
     }
   };
