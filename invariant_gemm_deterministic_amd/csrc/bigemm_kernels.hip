@@ -147,17 +147,20 @@ static_assert(kStagesBf16 >= 3 && kStagesBf16 <= 5, "LDS holds 3 to 5 stages of 
 // K-loop unroll of the bf16 kernel (steps per loop iteration).
 constexpr int kUnrollBf16 = 8 * kStagesBf16;
 
-// A prefetch workgroup of the bf16 / fp16 kernel (prefetch_grid). For the K
-// blocks rank, rank + nrank, ... of its tile it reads one dword of every
-// 128-byte line the tile's own loads of that block touch, so that the line is
-// in the XCD's L2 when the tile's workgroup asks for it; the dwords go to a
-// scratch corner of its LDS and are never read. Slot q = tid: X rows q / 2
-// (q < 256; the block's 128 bytes of a row start 16-byte aligned, so chunks 0
-// and 7 cover its one or two lines), then W: rows (q - 256) / 3 of a [K, N]
-// tile (256 bytes of columns: chunks 0, 8 and 15 cover two or three lines), or
-// rows (q - 256) / 2 of a W^T tile (as X). A chunk is touched only where the
-// tile's own loads read it (row, column and K inside the matrix), so every
-// read stays inside the bytes the tile reads. One load per wave per block.
+// A prefetch workgroup of the bf16 / fp16 kernel (prefetch_grid). The
+// prefetch workgroups of an XCD share out the K blocks of the distinct X
+// panels (tile rows) and W panels (tile columns) of the XCD's tiles
+// (prefetch_units): for each of its panel blocks a workgroup reads one dword of
+// every 128-byte line the tiles' own loads of that block touch, so that the
+// line is in the XCD's L2 when a tile's workgroup asks for it; the dwords go to
+// a scratch corner of its LDS and are never read. Waves 0-3 take the X panel
+// blocks, lane slot q = tid: row q / 2 (the block's 128 bytes of a row start
+// 16-byte aligned, so chunks 0 and 7 cover its one or two lines). Waves 4-7
+// take the W panel blocks: rows (q - 256) / 3 of a [K, N] panel (256 bytes of
+// columns: chunks 0, 8 and 15 cover two or three lines), or rows (q - 256) / 2
+// of a W^T panel (as X). A chunk is touched only where the tiles' own loads
+// read it (row, column and K inside the matrix), so every read stays inside
+// the bytes the tiles read. One load per wave per panel block.
 //
 // Pacing: block kb is requested no earlier than (kb - kPrefetchLead) block
 // times after the workgroup started (s_memrealtime, 100 MHz), a block time
@@ -174,43 +177,68 @@ template <bool kWT>
 __device__ __forceinline__ void bf16_prefetch(const uint16_t* X, const uint16_t* W, int M, int N, int K,
                                               int64_t ldx, int64_t ldw, int tiles_m, int tiles_n, uint8_t* scratch,
                                               int tid) {
-  int rank, nrank, tm, tn;
-  const int t = prefetch_role(blockIdx.x, gridDim.x, tiles_m * tiles_n, rank, nrank);
-  if (t < 0) return;
-  tile_coords(t, tiles_m, tiles_n, tm, tn);
-  const int row0 = tm * 128, col0 = tn * 128;
-  const int rows_valid = min(128, M - row0), cols_valid = min(128, N - col0);
-  const int nkb = (K + kBkBf16 - 1) / kBkBf16;
+  const int ntiles = tiles_m * tiles_n;
+  const int xcd = blockIdx.x % kXcds;
+  const int cx = xcd_tiles(xcd, ntiles);  // at most kPrefetchMaxXcdTiles (prefetch_grid)
+  if (cx == 0) return;
+  int h, nh;
+  prefetch_helper(blockIdx.x, gridDim.x, ntiles, h, nh);
+  const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid) >> 6;
-  const bool isx = wave < 4;  // waves 0-3: X lines, waves 4-7: W lines
-  int r, c;                   // row of the tile, 8-element chunk of the block
-  bool ok;                    // the row (and for a [K, N] tile the column chunk) is inside the matrix
+  // Lane i < cx holds the XCD's i-th tile; a tile row (column) is a unit at
+  // the first lane that has it (prefetch_units is the same rule on the host).
+  int tmi = 0, tni = 0;
+  if (lane < cx) tile_of(xcd + kXcds * lane, ntiles, tiles_m, tiles_n, tmi, tni);
+  bool first_row = lane < cx, first_col = lane < cx;
+  int tm_min = tiles_m;
+  for (int j = 0; j < cx; ++j) {
+    const int tmj = __builtin_amdgcn_readlane(tmi, j), tnj = __builtin_amdgcn_readlane(tni, j);
+    if (j < lane) {
+      first_row = first_row && tmj != tmi;
+      first_col = first_col && tnj != tni;
+    }
+    tm_min = tmj < tm_min ? tmj : tm_min;
+  }
+  const bool isx = wave < 4;  // waves 0-3: the X panels' lines, waves 4-7: the W panels'
+  const uint64_t units = __builtin_amdgcn_ballot_w64(isx ? first_row : first_col);
+  const int nu = __builtin_popcountll(units);
+  int r, c;   // row of the panel block, 8-element chunk of that row touched by this lane
   if (isx || kWT) {
     r = (tid & 255) >> 1;
     c = (tid & 1) ? 7 : 0;
-    ok = r < (isx ? rows_valid : cols_valid);
   } else {
     const int q = tid - 256;
     r = q / 3;
     c = q % 3 == 0 ? 0 : (q % 3 == 1 ? 8 : 15);
-    ok = r < kBkBf16 && c * 8 < cols_valid;
   }
-  const uint16_t* Xt = X + (int64_t)row0 * ldx;
-  const uint16_t* Wt = kWT ? W + (int64_t)col0 * ldw : W + col0;
-  const int64_t ticks = prefetch_ticks(rows_valid);
+  const int nkb = (K + kBkBf16 - 1) / kBkBf16;
+  // Pace: a row's X panel at that row's tiles' rate; a W panel at the rate of
+  // the XCD's fullest tile row, the slowest tiles that read it.
+  const int64_t col_ticks = prefetch_ticks(min(128, M - tm_min * 128));
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
   int j = 0;
-  for (int kb = rank; kb < nkb; kb += nrank, ++j) {
-    const int64_t due = (int64_t)(kb - kPrefetchLead) * ticks;
+  for (int w = h; w < nkb * nu; w += nh, ++j) {
+    const int kb = w / nu;
+    uint64_t rest = units;  // the (w % nu)-th set bit: the lane holding this unit
+    for (int q = w - kb * nu; q > 0; --q) rest &= rest - 1;
+    const int ul = __builtin_ctzll(rest);
+    const int tm = __builtin_amdgcn_readlane(tmi, ul), tn = __builtin_amdgcn_readlane(tni, ul);
+    const int rows_valid = min(128, M - tm * 128), cols_valid = min(128, N - tn * 128);
+    const int64_t due = (int64_t)(kb - kPrefetchLead) * (isx ? prefetch_ticks(rows_valid) : col_ticks);
     while ((int64_t)(__builtin_amdgcn_s_memrealtime() - t0) < due) __builtin_amdgcn_s_sleep(2);
     BIGEMM_WAIT_VMCNT(3);  // at most four blocks' loads in flight (the four LDS corners below)
     const int k0 = kb * kBkBf16;
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(isx ? Xt + k0 : (kWT ? Wt + k0 : Wt + (int64_t)k0 * ldw));
     uint32_t o = kOob;
-    if (isx || kWT) {
-      if (ok && k0 + c * 8 < K) o = (uint32_t)((r * (isx ? ldx : ldw) + c * 8) * 2);
-    } else {
-      if (ok && k0 + r < K) o = (uint32_t)((r * ldw + c * 8) * 2);
+    __amdgpu_buffer_rsrc_t rs;
+    if (isx) {
+      rs = make_rsrc(X + (int64_t)tm * 128 * ldx + k0);
+      if (r < rows_valid && k0 + c * 8 < K) o = (uint32_t)((r * ldx + c * 8) * 2);
+    } else if constexpr (kWT) {   // W^T panel: 128 rows of K values, touched like X's
+      rs = make_rsrc(W + (int64_t)tn * 128 * ldw + k0);
+      if (r < cols_valid && k0 + c * 8 < K) o = (uint32_t)((r * ldw + c * 8) * 2);
+    } else {                      // W panel: the block's 64 rows of 128 columns
+      rs = make_rsrc(W + tn * 128 + (int64_t)k0 * ldw);
+      if (r < kBkBf16 && c * 8 < cols_valid && k0 + r < K) o = (uint32_t)((r * ldw + c * 8) * 2);
     }
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDS(void, scratch + (j & 3) * 2048 + wave * 256), 4, o, 0, 0, 0);
   }

@@ -3,8 +3,8 @@ waves skip the fragments and X loads that hold only rows past M.
 
 The bf16 / fp16 kernel pads its grid to one workgroup per CU when the 128 x 128 tiles fill at
 most half of the CUs (at most 128 tiles on the 256-CU MI355X) and K spans at least 32 K blocks
-(K >= 1985). The extra workgroups touch the lines of K blocks of their XCD's tiles ahead and
-store nothing. In a tile with rows past M, each wave runs the K loop for the number of its
+(K >= 1985). The extra workgroups of each XCD share out the K blocks of the distinct X and W
+panels of the XCD's tiles, touch their lines ahead and store nothing. In a tile with rows past M, each wave runs the K loop for the number of its
 fragments and X loads that hold rows below M. Checked here, over tile counts from 2 to 128 (XCDs
 with no tile, XCDs holding one tile more than others), K from 32 blocks to 256, K and N not
 multiples of 8, every count of rows in a tile from 1 to 130, both W layouts, fp16 inputs and

@@ -5,11 +5,12 @@
 //  - the tiles' workgroups cover every tile exactly once (grid or padded grid);
 //  - the grid is padded exactly when the tiles fill at most half of the CUs and
 //    K spans at least kPrefetchMinBlocks blocks, and then to one per CU;
-//  - every prefetch workgroup serves a tile whose own workgroup runs on the
-//    same XCD (bid % 8), or none when that XCD holds no tile;
-//  - the prefetchers of a tile hold ranks 0 .. nrank - 1 once each, with one
-//    nrank, so that their blocks rank, rank + nrank, ... cover K once;
-//  - on an XCD with at least as many prefetchers as tiles, every tile has one.
+//  - xcd_tiles counts the tiles' workgroups of each XCD (bid % 8), never more
+//    than the kernel's one lane per tile allows;
+//  - the prefetch workgroups of each XCD hold the indices 0 .. nh - 1 once each,
+//    with one nh, and every XCD that holds tiles has at least one;
+//  - the units of each XCD (prefetch_units) are distinct, and they are exactly
+//    the tile rows and tile columns of the XCD's tiles.
 #include <cstdio>
 #include <cstdlib>
 #include <vector>
@@ -51,38 +52,54 @@ static void check_case(int tiles_m, int tiles_n, int nkb, int cus) {
   }
   for (int i = 0; i < ntiles; ++i) CHECK(seen[i] == 1, "tile %d covered %d times (%dx%d)", i, seen[i], tiles_m, tiles_n);
   if (grid == ntiles) return;
-  // the prefetch workgroups
-  std::vector<std::vector<int>> ranks(ntiles);
-  std::vector<int> nr(ntiles, -1), tiles_on(kXcds, 0), pf_on(kXcds, 0);
-  for (int t = 0; t < ntiles; ++t) tiles_on[xcd_of_t[t]]++;
+  // the prefetch workgroups: per XCD, indices 0 .. nh - 1 once each
+  std::vector<std::vector<int>> hs(kXcds);
+  std::vector<int> nhs(kXcds, -1), tiles_on(kXcds, 0);
+  for (int bid = 0; bid < ntiles; ++bid) tiles_on[bid % kXcds]++;
   for (int bid = ntiles; bid < grid; ++bid) {
-    int rank, nrank;
-    const int t = prefetch_role(bid, grid, ntiles, rank, nrank);
+    int h, nh;
+    prefetch_helper(bid, grid, ntiles, h, nh);
     const int x = bid % kXcds;
-    pf_on[x]++;
-    if (tiles_on[x] == 0) {
-      CHECK(t == -1, "bid %d on an XCD without tiles got tile %d", bid, t);
-      continue;
-    }
-    CHECK(t >= 0 && t < ntiles, "bid %d: tile %d of %d", bid, t, ntiles);
-    if (t < 0 || t >= ntiles) continue;
-    CHECK(xcd_of_t[t] == x, "bid %d (XCD %d) serves tile %d on XCD %d", bid, x, t, xcd_of_t[t]);
-    CHECK(nrank >= 1 && rank >= 0 && rank < nrank, "bid %d: rank %d of %d", bid, rank, nrank);
-    CHECK(nr[t] == -1 || nr[t] == nrank, "tile %d: nrank %d and %d", t, nr[t], nrank);
-    if (nrank < 1 || (nr[t] != -1 && nr[t] != nrank)) continue;
-    nr[t] = nrank;
-    ranks[t].push_back(rank);
+    CHECK(nh >= 1 && h >= 0 && h < nh, "bid %d: index %d of %d", bid, h, nh);
+    CHECK(nhs[x] == -1 || nhs[x] == nh, "XCD %d: nh %d and %d", x, nhs[x], nh);
+    if (nh < 1 || h < 0 || h >= nh || (nhs[x] != -1 && nhs[x] != nh)) continue;
+    nhs[x] = nh;
+    hs[x].push_back(h);
   }
-  for (int t = 0; t < ntiles; ++t) {
-    if (ranks[t].empty()) {
-      CHECK(pf_on[xcd_of_t[t]] < tiles_on[xcd_of_t[t]], "tile %d has no prefetcher though its XCD has %d for %d tiles",
-            t, pf_on[xcd_of_t[t]], tiles_on[xcd_of_t[t]]);
-      continue;
+  for (int x = 0; x < kXcds; ++x) {
+    CHECK(xcd_tiles(x, ntiles) == tiles_on[x], "XCD %d: xcd_tiles %d, tiles %d", x, xcd_tiles(x, ntiles), tiles_on[x]);
+    CHECK(tiles_on[x] <= kPrefetchMaxXcdTiles, "XCD %d holds %d tiles", x, tiles_on[x]);
+    if (tiles_on[x] > 0) CHECK(nhs[x] >= 1, "XCD %d holds %d tiles and no prefetch workgroup", x, tiles_on[x]);
+    if (nhs[x] >= 1) {
+      std::vector<int> got(nhs[x], 0);
+      for (int h : hs[x]) got[h]++;
+      for (int h = 0; h < nhs[x]; ++h) CHECK(got[h] == 1, "XCD %d index %d held %d times", x, h, got[h]);
     }
-    std::vector<int> got(nr[t], 0);
-    for (int r : ranks[t])
-      if (r >= 0 && r < nr[t]) got[r]++;
-    for (int r = 0; r < nr[t]; ++r) CHECK(got[r] == 1, "tile %d rank %d held %d times", t, r, got[r]);
+    if (tiles_on[x] == 0 || tiles_on[x] > kPrefetchMaxXcdTiles) continue;
+    // units: distinct, and exactly the rows / columns of the XCD's tiles
+    std::vector<int> rows(tiles_on[x]), cols(tiles_on[x]);
+    int nrows = 0, ncols = 0;
+    prefetch_units(x, ntiles, tiles_m, tiles_n, rows.data(), nrows, cols.data(), ncols);
+    std::vector<int> row_used(tiles_m, 0), col_used(tiles_n, 0), row_unit(tiles_m, 0), col_unit(tiles_n, 0);
+    for (int b = x; b < ntiles; b += kXcds) {
+      int tm, tn;
+      tile_of(b, ntiles, tiles_m, tiles_n, tm, tn);
+      row_used[tm] = 1;
+      col_used[tn] = 1;
+    }
+    for (int i = 0; i < nrows; ++i) {
+      CHECK(rows[i] >= 0 && rows[i] < tiles_m, "XCD %d row unit %d", x, rows[i]);
+      if (rows[i] >= 0 && rows[i] < tiles_m) row_unit[rows[i]]++;
+    }
+    for (int i = 0; i < ncols; ++i) {
+      CHECK(cols[i] >= 0 && cols[i] < tiles_n, "XCD %d column unit %d", x, cols[i]);
+      if (cols[i] >= 0 && cols[i] < tiles_n) col_unit[cols[i]]++;
+    }
+    for (int tm = 0; tm < tiles_m; ++tm)
+      CHECK(row_unit[tm] == row_used[tm], "XCD %d tile row %d: %d units, used %d", x, tm, row_unit[tm], row_used[tm]);
+    for (int tn = 0; tn < tiles_n; ++tn)
+      CHECK(col_unit[tn] == col_used[tn], "XCD %d tile column %d: %d units, used %d", x, tn, col_unit[tn],
+            col_used[tn]);
   }
 }
 
