@@ -10,9 +10,9 @@
  * every shape uses. This library is that recipe on CDNA4: one fixed tile
  * configuration per input type, the K blocks walked in ascending order by a
  * single workgroup, one MFMA shape at every M, no atomics, no workspace.
- * (When a bf16 / fp16 product has few tiles and a long K, otherwise idle CUs
- * also run workgroups that only read the tiles' next K blocks into the L2
- * cache; they store nothing and change no output byte.)
+ * (When a product has few tiles and a long K, otherwise idle CUs also run
+ * workgroups that only read the tiles' next K blocks into the L2 cache; they
+ * store nothing and change no output byte.)
  * The same rules give the other entry points below: handles that take W as
  * [N, K] rows (a linear layer's weight layout) with the same output bytes, an
  * opt-in split-K whose split count follows K only, a batch-invariant RMSNorm,

@@ -165,8 +165,8 @@ hipError_t launch_unsplit(const bigemm_s* h, int64_t M, int64_t N, int64_t K, co
   const bigemm::Op op = h->op;
   const bool wt = h->w_trans;
   if (op.in == bigemm::kInMx)
-    return bigemm::launch_mxfp8(op, wt, X, W, Y, XS, WS, M, N, K, ldx, ldw, ldy, ldxs, ldws, stream);
-  if (op.in == bigemm::kInI8) return bigemm::launch_i8(wt, X, W, Y, M, N, K, ldx, ldw, ldy, stream);
+    return bigemm::launch_mxfp8(op, wt, X, W, Y, XS, WS, M, N, K, ldx, ldw, ldy, ldxs, ldws, h->cus, stream);
+  if (op.in == bigemm::kInI8) return bigemm::launch_i8(wt, X, W, Y, M, N, K, ldx, ldw, ldy, h->cus, stream);
   return bigemm::launch_bf16(op, wt, X, W, Y, M, N, K, ldx, ldw, ldy, h->cus, stream);
 }
 

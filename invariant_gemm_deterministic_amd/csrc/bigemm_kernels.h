@@ -20,8 +20,8 @@ struct Op {
 
 // wt (every launcher): W is given as its transpose, [N][ldw] with ldw >= K,
 // and for MXFP8 W_scale as [N][ldws] with ldws >= K/32.
-// cus: the device's compute units (the grid may be padded with prefetch
-// workgroups up to one per CU; see prefetch_grid).
+// cus (bf16 / fp16, MXFP8, int8): the device's compute units (the grid may be
+// padded with prefetch workgroups up to one per CU; see prefetch_grid).
 hipError_t launch_bf16(Op op, bool wt, const void* X, const void* W, void* Y, int64_t M, int64_t N, int64_t K,
                        int64_t ldx, int64_t ldw, int64_t ldy, int cus, hipStream_t stream);
 
@@ -40,9 +40,9 @@ hipError_t static_scratch_address(int device, void** out);
 
 hipError_t launch_mxfp8(Op op, bool wt, const void* X, const void* W, void* Y, const void* XS, const void* WS,
                         int64_t M, int64_t N, int64_t K, int64_t ldx, int64_t ldw, int64_t ldy,
-                        int64_t ldxs, int64_t ldws, hipStream_t stream);
+                        int64_t ldxs, int64_t ldws, int cus, hipStream_t stream);
 
 hipError_t launch_i8(bool wt, const void* X, const void* W, void* Y, int64_t M, int64_t N, int64_t K,
-                     int64_t ldx, int64_t ldw, int64_t ldy, hipStream_t stream);
+                     int64_t ldx, int64_t ldw, int64_t ldy, int cus, hipStream_t stream);
 
 }  // namespace bigemm

@@ -173,35 +173,71 @@ __device__ __forceinline__ int64_t prefetch_ticks(int rows_valid) {
   return rows_valid <= 32 ? 17 : (rows_valid <= 64 ? 21 : 33);
 }
 
+// The units of this prefetch workgroup's XCD (the rule of prefetch_units):
+// lane i < cx holds the XCD's i-th tile (tmi, tni); bit i of rows (cols) is
+// set where that tile is the first of the XCD with its tile row (column).
+struct PrefetchUnits {
+  int tmi, tni, tm_min;
+  uint64_t rows, cols;
+};
+__device__ __forceinline__ bool prefetch_lane_units(int tiles_m, int tiles_n, int lane, PrefetchUnits& u) {
+  const int ntiles = tiles_m * tiles_n;
+  const int xcd = blockIdx.x % kXcds;
+  const int cx = xcd_tiles(xcd, ntiles);  // at most kPrefetchMaxXcdTiles (prefetch_grid)
+  if (cx == 0) return false;
+  u.tmi = 0;
+  u.tni = 0;
+  if (lane < cx) tile_of(xcd + kXcds * lane, ntiles, tiles_m, tiles_n, u.tmi, u.tni);
+  bool first_row = lane < cx, first_col = lane < cx;
+  u.tm_min = tiles_m;
+  for (int j = 0; j < cx; ++j) {
+    const int tmj = __builtin_amdgcn_readlane(u.tmi, j), tnj = __builtin_amdgcn_readlane(u.tni, j);
+    if (j < lane) {
+      first_row = first_row && tmj != u.tmi;
+      first_col = first_col && tnj != u.tni;
+    }
+    u.tm_min = tmj < u.tm_min ? tmj : u.tm_min;
+  }
+  u.rows = __builtin_amdgcn_ballot_w64(first_row);
+  u.cols = __builtin_amdgcn_ballot_w64(first_col);
+  return true;
+}
+
+// This prefetch workgroup's items of one kind: the K blocks kb of the units in
+// `units` (a mask of u's lanes), item kb * (number of units) + unit, dealt
+// round-robin over the XCD's prefetch workgroups. For each it waits until
+// (kb - kPrefetchLead) * ticks(tm) ticks (s_memrealtime, 100 MHz) after t0,
+// then calls touch(kb, tm, tn, j), j counting this workgroup's items. The wait
+// is on the clock alone and always ends.
+template <class Ticks, class Touch>
+__device__ __forceinline__ void prefetch_walk(const PrefetchUnits& u, uint64_t units, int ntiles, int nkb,
+                                              uint64_t t0, Ticks ticks, Touch touch) {
+  int h, nh;
+  prefetch_helper(blockIdx.x, gridDim.x, ntiles, h, nh);
+  const int nu = __builtin_popcountll(units);
+  int j = 0;
+  for (int w = h; w < nkb * nu; w += nh, ++j) {
+    const int kb = w / nu;
+    uint64_t rest = units;  // the (w % nu)-th set bit: the lane holding this unit
+    for (int q = w - kb * nu; q > 0; --q) rest &= rest - 1;
+    const int ul = __builtin_ctzll(rest);
+    const int tm = __builtin_amdgcn_readlane(u.tmi, ul), tn = __builtin_amdgcn_readlane(u.tni, ul);
+    const int64_t due = (int64_t)(kb - kPrefetchLead) * ticks(tm);
+    while ((int64_t)(__builtin_amdgcn_s_memrealtime() - t0) < due) __builtin_amdgcn_s_sleep(2);
+    touch(kb, tm, tn, j);
+  }
+  BIGEMM_WAIT_VMCNT(0);  // no LDS-DMA load may outlive the workgroup
+}
+
 template <bool kWT>
 __device__ __forceinline__ void bf16_prefetch(const uint16_t* X, const uint16_t* W, int M, int N, int K,
                                               int64_t ldx, int64_t ldw, int tiles_m, int tiles_n, uint8_t* scratch,
                                               int tid) {
-  const int ntiles = tiles_m * tiles_n;
-  const int xcd = blockIdx.x % kXcds;
-  const int cx = xcd_tiles(xcd, ntiles);  // at most kPrefetchMaxXcdTiles (prefetch_grid)
-  if (cx == 0) return;
-  int h, nh;
-  prefetch_helper(blockIdx.x, gridDim.x, ntiles, h, nh);
-  const int lane = tid & 63;
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  PrefetchUnits u;
+  if (!prefetch_lane_units(tiles_m, tiles_n, tid & 63, u)) return;
   const int wave = __builtin_amdgcn_readfirstlane(tid) >> 6;
-  // Lane i < cx holds the XCD's i-th tile; a tile row (column) is a unit at
-  // the first lane that has it (prefetch_units is the same rule on the host).
-  int tmi = 0, tni = 0;
-  if (lane < cx) tile_of(xcd + kXcds * lane, ntiles, tiles_m, tiles_n, tmi, tni);
-  bool first_row = lane < cx, first_col = lane < cx;
-  int tm_min = tiles_m;
-  for (int j = 0; j < cx; ++j) {
-    const int tmj = __builtin_amdgcn_readlane(tmi, j), tnj = __builtin_amdgcn_readlane(tni, j);
-    if (j < lane) {
-      first_row = first_row && tmj != tmi;
-      first_col = first_col && tnj != tni;
-    }
-    tm_min = tmj < tm_min ? tmj : tm_min;
-  }
   const bool isx = wave < 4;  // waves 0-3: the X panels' lines, waves 4-7: the W panels'
-  const uint64_t units = __builtin_amdgcn_ballot_w64(isx ? first_row : first_col);
-  const int nu = __builtin_popcountll(units);
   int r, c;   // row of the panel block, 8-element chunk of that row touched by this lane
   if (isx || kWT) {
     r = (tid & 255) >> 1;
@@ -212,21 +248,13 @@ __device__ __forceinline__ void bf16_prefetch(const uint16_t* X, const uint16_t*
     c = q % 3 == 0 ? 0 : (q % 3 == 1 ? 8 : 15);
   }
   const int nkb = (K + kBkBf16 - 1) / kBkBf16;
-  // Pace: a row's X panel at that row's tiles' rate; a W panel at the rate of
-  // the XCD's fullest tile row, the slowest tiles that read it.
-  const int64_t col_ticks = prefetch_ticks(min(128, M - tm_min * 128));
-  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-  int j = 0;
-  for (int w = h; w < nkb * nu; w += nh, ++j) {
-    const int kb = w / nu;
-    uint64_t rest = units;  // the (w % nu)-th set bit: the lane holding this unit
-    for (int q = w - kb * nu; q > 0; --q) rest &= rest - 1;
-    const int ul = __builtin_ctzll(rest);
-    const int tm = __builtin_amdgcn_readlane(tmi, ul), tn = __builtin_amdgcn_readlane(tni, ul);
+  // A row's X panel at that row's tiles' pace; a W panel at the pace of the
+  // XCD's fullest tile row, the slowest tiles that read it.
+  const int64_t col_ticks = prefetch_ticks(min(128, M - u.tm_min * 128));
+  auto ticks = [&](int tm) { return isx ? prefetch_ticks(min(128, M - tm * 128)) : col_ticks; };
+  auto touch = [&](int kb, int tm, int tn, int j) {
     const int rows_valid = min(128, M - tm * 128), cols_valid = min(128, N - tn * 128);
-    const int64_t due = (int64_t)(kb - kPrefetchLead) * (isx ? prefetch_ticks(rows_valid) : col_ticks);
-    while ((int64_t)(__builtin_amdgcn_s_memrealtime() - t0) < due) __builtin_amdgcn_s_sleep(2);
-    BIGEMM_WAIT_VMCNT(3);  // at most four blocks' loads in flight (the four LDS corners below)
+    BIGEMM_WAIT_VMCNT(3);  // at most four items' loads in flight (the four LDS corners below)
     const int k0 = kb * kBkBf16;
     uint32_t o = kOob;
     __amdgpu_buffer_rsrc_t rs;
@@ -241,8 +269,8 @@ __device__ __forceinline__ void bf16_prefetch(const uint16_t* X, const uint16_t*
       if (r < kBkBf16 && c * 8 < cols_valid && k0 + r < K) o = (uint32_t)((r * ldw + c * 8) * 2);
     }
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDS(void, scratch + (j & 3) * 2048 + wave * 256), 4, o, 0, 0, 0);
-  }
-  BIGEMM_WAIT_VMCNT(0);  // no LDS-DMA load may outlive the workgroup
+  };
+  prefetch_walk(u, isx ? u.rows : u.cols, tiles_m * tiles_n, nkb, t0, ticks, touch);
 }
 
 // kSplit: the opt-in split-K variant. The grid is (chunk, tile) pairs; the
@@ -516,6 +544,56 @@ void bigemm_bf16_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
 // applied inside the instruction, fp32 accumulate. Per stage: X tile 128 x 128
 // bytes, W tile 128 x 128 bytes (both rows of 128 B).
 constexpr int kBkMx = 128;
+
+// A prefetch workgroup of the MXFP8 and int8 kernels (prefetch_grid; 256
+// threads, K blocks of 128 one-byte values, so 128 bytes of each panel row per
+// block): as in bf16_prefetch, the XCD's prefetch workgroups share out the K
+// blocks of its distinct X and W panels. Waves 0-1 take the X panel blocks,
+// waves 2-3 the W panel blocks, two loads per wave and panel block: lane slot
+// q = 64 (2 (wave & 1) + s) + lane for s = 0, 1 touches row q / 2 at chunk 0
+// or 7 of its 128 bytes (one or two lines). A [K, N] W panel's rows are the
+// block's 128 K rows of the tile's 128 columns, a W^T panel's the tile's 128
+// columns of the block's 128 K values. Only bytes the tiles' own loads read are
+// touched. The scales (1/32 of the bytes) are not.
+__device__ __forceinline__ int64_t prefetch_ticks_u8(int rows_valid) {
+  return rows_valid <= 32 ? 22 : (rows_valid <= 64 ? 34 : 44);
+}
+template <bool kWT>
+__device__ __forceinline__ void u8_prefetch(const uint8_t* X, const uint8_t* W, int M, int N, int K, int64_t ldx,
+                                            int64_t ldw, int tiles_m, int tiles_n, uint8_t* scratch, int tid) {
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  PrefetchUnits u;
+  if (!prefetch_lane_units(tiles_m, tiles_n, tid & 63, u)) return;
+  const int wave = __builtin_amdgcn_readfirstlane(tid) >> 6;
+  const bool isx = wave < 2;  // waves 0-1: the X panels' lines, waves 2-3: the W panels'
+  const int nkb = (K + kBkMx - 1) / kBkMx;
+  const int64_t col_ticks = prefetch_ticks_u8(min(128, M - u.tm_min * 128));
+  auto ticks = [&](int tm) { return isx ? prefetch_ticks_u8(min(128, M - tm * 128)) : col_ticks; };
+  auto touch = [&](int kb, int tm, int tn, int j) {
+    const int rows_valid = min(128, M - tm * 128), cols_valid = min(128, N - tn * 128);
+    BIGEMM_WAIT_VMCNT(6);  // at most four items' loads (two each) in flight: the four LDS corners below
+    const int k0 = kb * kBkMx;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(isx ? X + (int64_t)tm * 128 * ldx + k0
+                                                     : (kWT ? W + (int64_t)tn * 128 * ldw + k0
+                                                            : W + tn * 128 + (int64_t)k0 * ldw));
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const int q = 64 * (2 * (wave & 1) + s2) + (tid & 63);
+      const int r = q >> 1, c = (q & 1) ? 7 : 0;
+      uint32_t o = kOob;
+      if (isx) {
+        if (r < rows_valid && k0 + c * 16 < K) o = (uint32_t)(r * ldx + c * 16);
+      } else if (kWT) {
+        if (r < cols_valid && k0 + c * 16 < K) o = (uint32_t)(r * ldw + c * 16);
+      } else {
+        if (k0 + r < K && c * 16 < cols_valid) o = (uint32_t)(r * ldw + c * 16);
+      }
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDS(void, scratch + (j & 3) * 2048 + wave * 512 + s2 * 256), 4,
+                                                o, 0, 0, 0);
+    }
+  };
+  prefetch_walk(u, isx ? u.rows : u.cols, tiles_m * tiles_n, nkb, t0, ticks, touch);
+}
 // Staged scales: the scale bytes of kScaleGroup consecutive K blocks are
 // moved to LDS by DMA, once per workgroup (X: 128 rows x 4 kScaleGroup bytes;
 // W: 4 kScaleGroup scale rows x 128 bytes, whole lines), into one of two LDS
@@ -560,8 +638,12 @@ void bigemm_mxfp8_kernel(const uint8_t* __restrict__ X, const uint8_t* __restric
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  if (__builtin_expect((int)blockIdx.x >= tiles_m * tiles_n, 0)) {  // a prefetch workgroup
+    u8_prefetch<kWT>(X, W, M, N, K, ldx, ldw, tiles_m, tiles_n, stage0, tid);
+    return;
+  }
   int tm, tn;
-  tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+  tile_of(blockIdx.x, tiles_m * tiles_n, tiles_m, tiles_n, tm, tn);
   const int row0 = tm * 128;
   const int col0 = tn * 128;
   const int rows_valid = min(128, M - row0);
@@ -959,8 +1041,12 @@ void bigemm_i8_kernel(const uint8_t* __restrict__ X, const uint8_t* __restrict__
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  if (__builtin_expect((int)blockIdx.x >= tiles_m * tiles_n, 0)) {  // a prefetch workgroup
+    u8_prefetch<kWT>(X, W, M, N, K, ldx, ldw, tiles_m, tiles_n, stage0, tid);
+    return;
+  }
   int tm, tn;
-  tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+  tile_of(blockIdx.x, tiles_m * tiles_n, tiles_m, tiles_n, tm, tn);
   const int row0 = tm * 128;
   const int col0 = tn * 128;
   const int rows_valid = min(128, M - row0);
@@ -1296,9 +1382,11 @@ hipError_t launch_bf16_split(Op op, bool wt, int32_t k_chunk, const void* X, con
 
 hipError_t launch_mxfp8(Op op, bool wt, const void* X, const void* W, void* Y, const void* XS, const void* WS,
                         int64_t M, int64_t N, int64_t K, int64_t ldx, int64_t ldw, int64_t ldy,
-                        int64_t ldxs, int64_t ldws, hipStream_t stream) {
+                        int64_t ldxs, int64_t ldws, int cus, hipStream_t stream) {
   const int tiles_m = (int)((M + 127) / 128);
   const int tiles_n = (int)((N + 127) / 128);
+  // the same padding rule as the bf16 kernel, K counted in 64-deep blocks
+  const int grid = prefetch_grid(tiles_m * tiles_n, (int)((K + 63) / 64), cus);
   // The scale load path depends on the scale layout and K only (never on M);
   // both paths read the same scale values.
   const bool staged = K % 512 == 0 && ((uintptr_t)XS & 15) == 0 && ldxs % 16 == 0 && ((uintptr_t)WS & 15) == 0 &&
@@ -1308,17 +1396,18 @@ hipError_t launch_mxfp8(Op op, bool wt, const void* X, const void* W, void* Y, c
                            : (obf ? bigemm_mxfp8_kernel<false, true, true> : bigemm_mxfp8_kernel<false, false, true>))
                  : (staged ? (obf ? bigemm_mxfp8_kernel<true, true> : bigemm_mxfp8_kernel<true, false>)
                            : (obf ? bigemm_mxfp8_kernel<false, true> : bigemm_mxfp8_kernel<false, false>));
-  hipLaunchKernelGGL(kern, dim3(tiles_m * tiles_n), dim3(kThreads), 0, stream, (const uint8_t*)X,
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), 0, stream, (const uint8_t*)X,
                      (const uint8_t*)W, Y, (const uint8_t*)XS, (const uint8_t*)WS, (int)M, (int)N, (int)K, ldx, ldw,
                      ldy, ldxs, ldws, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
 hipError_t launch_i8(bool wt, const void* X, const void* W, void* Y, int64_t M, int64_t N, int64_t K, int64_t ldx,
-                     int64_t ldw, int64_t ldy, hipStream_t stream) {
+                     int64_t ldw, int64_t ldy, int cus, hipStream_t stream) {
   const int tiles_m = (int)((M + 127) / 128);
   const int tiles_n = (int)((N + 127) / 128);
-  hipLaunchKernelGGL(wt ? bigemm_i8_kernel<true> : bigemm_i8_kernel<false>, dim3(tiles_m * tiles_n), dim3(kThreads), 0,
+  const int grid = prefetch_grid(tiles_m * tiles_n, (int)((K + 63) / 64), cus);
+  hipLaunchKernelGGL(wt ? bigemm_i8_kernel<true> : bigemm_i8_kernel<false>, dim3(grid), dim3(kThreads), 0,
                      stream, (const uint8_t*)X, (const uint8_t*)W, (int32_t*)Y, (int)M, (int)N, (int)K, ldx, ldw, ldy,
                      tiles_m, tiles_n);
   return hipGetLastError();

@@ -25,11 +25,11 @@ hipError_t launch_bf16_split(Op, bool, int32_t, const void*, const void*, void*,
   return unreachable("launch_bf16_split");
 }
 hipError_t launch_mxfp8(Op, bool, const void*, const void*, void*, const void*, const void*, int64_t, int64_t,
-                        int64_t, int64_t, int64_t, int64_t, int64_t, int64_t, hipStream_t) {
+                        int64_t, int64_t, int64_t, int64_t, int64_t, int64_t, int, hipStream_t) {
   return unreachable("launch_mxfp8");
 }
 hipError_t launch_i8(bool, const void*, const void*, void*, int64_t, int64_t, int64_t, int64_t, int64_t, int64_t,
-                     hipStream_t) {
+                     int, hipStream_t) {
   return unreachable("launch_i8");
 }
 hipError_t static_scratch_address(int, void**) { return unreachable("static_scratch_address"); }

@@ -10,6 +10,9 @@ a tile from 1 to 130 (and 255):
   same row computed inside a full tile; parity with the oracle on the reference rows; seeded random
   shapes against the oracle and against rows inside a full tile;
 - int8, both W layouts: every row equal to numpy's exact int64 product.
+With at most 128 tiles and K >= 1985 both kernels pad the grid with prefetch workgroups, which store
+nothing: MXFP8 rows from such grids equal the same rows inside an unpadded product, and int8 stays
+exact.
 """
 import numpy as np
 import pytest
@@ -157,3 +160,39 @@ def test_int8_every_partial_tile_row_count(wt):
         if not np.array_equal(y.cpu().numpy().astype(np.int64), exact[:m]):
             bad.append(m)
     assert not bad, f"rows differ from the exact product at M = {bad}"
+
+
+@pytest.mark.parametrize("path", ["staged", "byte"])
+@pytest.mark.parametrize("wt", [False, True])
+def test_mxfp8_padded_grid_rows_equal_unpadded(path, wt):
+    """With at most 128 tiles and K >= 1985 the MXFP8 grid is padded with prefetch workgroups (one
+    per CU), which store nothing: rows 1, 37 and 100 of such products (32 tiles) must equal the same
+    rows inside a product of 5 x 32 = 160 tiles (a grid that is not padded)."""
+    K, N, BIG = 2048, 4096, 640
+    X, W, XS, WS = mx_inputs(150, BIG, N, K)
+    x, xs, w, ws = operands(X, W, XS, WS, path, wt)
+    big = bg.mm(x, w, xs, ws)
+    torch.cuda.synchronize()
+    for m in (1, 37, 100):
+        y = bg.mm(x[:m], w, xs[:m], ws)
+        torch.cuda.synchronize()
+        assert same_bytes(y, big[:m]), f"M = {m}"
+    rows = np.array([0, 36, 99, 639])
+    Y, S = oracle.gemm_mxfp8(X[rows], W, XS[rows], WS)
+    assert oracle.max_normalized_error(big.cpu().numpy()[rows], Y, S) <= TOL
+
+
+def test_int8_padded_grid_exact():
+    """int8 with a padded grid (32 tiles, K = 4096): exact against numpy's int64 product, rows of M = 1,
+    64 and 128."""
+    K, N = 4096, 4096
+    rng = np.random.default_rng(160)
+    X = rng.integers(-128, 128, size=(128, K)).astype(np.int8)
+    W = rng.integers(-128, 128, size=(K, N)).astype(np.int8)
+    exact = X.astype(np.int64) @ W.astype(np.int64)
+    x = rows_u8(X.view(np.uint8), K).view(torch.int8)
+    w = rows_u8(W.view(np.uint8), N).view(torch.int8)
+    for m in (1, 64, 128):
+        y = bg.mm(x[:m], w)
+        torch.cuda.synchronize()
+        assert np.array_equal(y.cpu().numpy().astype(np.int64), exact[:m]), f"M = {m}"
