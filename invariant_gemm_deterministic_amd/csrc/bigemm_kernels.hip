@@ -164,8 +164,8 @@ constexpr int kUnrollBf16 = 8 * kStagesBf16;
 //
 // Pacing: block kb is requested no earlier than (kb - kPrefetchLead) block
 // times after the workgroup started (s_memrealtime, 100 MHz), a block time
-// being roughly what the tile's workgroup takes per block when its lines come
-// from L2 (kPrefetchTicks, by the rows the tile multiplies). Running further
+// being roughly what a tile's workgroup takes per block when its lines come
+// from L2 (prefetch_ticks, by the rows the tile multiplies). Running further
 // ahead only evicts lines from the L2 before they are used. The wait is on
 // the clock alone, so it always ends.
 constexpr int kPrefetchLead = 16;
