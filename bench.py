@@ -238,14 +238,14 @@ def main():
     ap.add_argument("--m", type=int, default=4096, help="rows of the timed headline call (profiling other M)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="one 256 MiB device copy before the GEMMs (scale reference for byte counters)")
-    ap.add_argument("--kind", choices=("bf16", "mxfp8"), default="bf16",
-                    help="input family of the headline call (profiling the MXFP8 kernel; the bench line is bf16)")
+    ap.add_argument("--kind", choices=("bf16", "mxfp8", "i8"), default="bf16",
+                    help="input family of the headline call (profiling the MXFP8 or int8 kernel; the bench line is bf16)")
     ap.add_argument("--warm-s", type=float, default=WARM_S,
                     help="seconds of launches before each timed point (profiling runs under counters use 0)")
     args = ap.parse_args()
     WARM_S = args.warm_s
     if args.kind != "bf16" and not args.no_sweep:
-        ap.error("--kind mxfp8 profiles the MXFP8 kernel alone: use it with --no-sweep")
+        ap.error("--kind mxfp8 / i8 profiles that kernel alone: use it with --no-sweep")
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the GEMM would shard by rows "
               f"or columns with no exchange, and no multi-GPU launch is implemented.", file=sys.stderr)
@@ -285,6 +285,13 @@ def main():
         WSq = torch.from_numpy(e8m0_scales(SEED_W + SCALE_SEED_OFFSET, (K // 32, N), "var")).to(dev)
         head = lambda i: bg.mm(Xq, Wq, XSq, WSq, out=Ym)
         head_peak = PEAK_FP8_TFLOPS
+    elif args.kind == "i8":    # uniform int8 values, as in other_types
+        from bigemm_inputs import int_i8
+        Xq = torch.from_numpy(int_i8(SEED_X, (M, K))).to(dev)
+        Wq = torch.from_numpy(int_i8(SEED_W, (K, N))).to(dev)
+        Yq = torch.empty((M, N), dtype=torch.int32, device=dev)
+        head = lambda i: bg.mm(Xq, Wq, out=Yq)
+        head_peak = PEAK_I8_TOPS
     for i in range(args.warmup):
         head(i)
     if WARM_S > 0:
@@ -527,15 +534,20 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if args.kind == "bf16" else "e4m3",
+        "dtype": {"bf16": "bf16", "mxfp8": "e4m3", "i8": "int8"}[args.kind],
         "data": "synthetic",
         "config": {"workload": (f"bf16 projection GEMM Y[{M},4096] = X[{M},4096] . W[4096,4096], "
                                 "X~N(0,1), W~N(0,0.02), fp32 accumulate and output, batch-invariant fixed tile")
                    if args.kind == "bf16" else
                    (f"MXFP8 GEMM Y[{M},4096] = X[{M},4096] . W[4096,4096], E4M3 from N(0,1) with K-varying "
-                    "E8M0 scales in [-4,4] on both sides, fp32 accumulate and output (profiling run)"),
+                    "E8M0 scales in [-4,4] on both sides, fp32 accumulate and output (profiling run)")
+                   if args.kind == "mxfp8" else
+                   (f"int8 GEMM Y[{M},4096] = X[{M},4096] . W[4096,4096], uniform int8, int32 accumulate and "
+                    "output (profiling run)"),
                    "M": M, "N": N, "K": K,
-                   "tile": list(bg.bigemm_get_config(bg._handle("bf16" if args.kind == "bf16" else "mx", 0)))},
+                   "tile": list(bg.bigemm_get_config(
+                       bg._handle("i8", 0, bg.BIGEMM_I32) if args.kind == "i8"
+                       else bg._handle("bf16" if args.kind == "bf16" else "mx", 0)))},
         "pct_mfma_peak": round(100 * tflops / head_peak, 2),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": head_peak,
                      "unit": "TFLOP/s", "frac": round(tflops / head_peak, 4),
