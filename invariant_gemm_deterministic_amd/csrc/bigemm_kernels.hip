@@ -554,13 +554,18 @@ constexpr int kBkMx = 128;
 // or 7 of its 128 bytes (one or two lines). A [K, N] W panel's rows are the
 // block's 128 K rows of the tile's 128 columns, a W^T panel's the tile's 128
 // columns of the block's 128 K values. Only bytes the tiles' own loads read are
-// touched. The scales (1/32 of the bytes) are not.
+// touched. kScales (MXFP8): a W panel block also touches its W scales, the
+// block's 4 scale rows of the tile's 128 columns ([K/32, N]: wave 2, lanes
+// 0-7, chunks 0 and 7 of each row's 128 bytes) or the 4 scale bytes of each of
+// the tile's 128 columns ([N, K/32]: waves 2-3, one lane per column). The X
+// scales (one row's bytes of 32 blocks share a line) are not touched.
 __device__ __forceinline__ int64_t prefetch_ticks_u8(int rows_valid) {
   return rows_valid <= 32 ? 22 : (rows_valid <= 64 ? 34 : 44);
 }
-template <bool kWT>
-__device__ __forceinline__ void u8_prefetch(const uint8_t* X, const uint8_t* W, int M, int N, int K, int64_t ldx,
-                                            int64_t ldw, int tiles_m, int tiles_n, uint8_t* scratch, int tid) {
+template <bool kWT, bool kScales>
+__device__ __forceinline__ void u8_prefetch(const uint8_t* X, const uint8_t* W, const uint8_t* WS, int M, int N,
+                                            int K, int64_t ldx, int64_t ldw, int64_t ldws, int tiles_m, int tiles_n,
+                                            uint8_t* scratch, int tid) {
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
   PrefetchUnits u;
   if (!prefetch_lane_units(tiles_m, tiles_n, tid & 63, u)) return;
@@ -590,6 +595,25 @@ __device__ __forceinline__ void u8_prefetch(const uint8_t* X, const uint8_t* W, 
       }
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDS(void, scratch + (j & 3) * 2048 + wave * 512 + s2 * 256), 4,
                                                 o, 0, 0, 0);
+    }
+    if constexpr (kScales) {
+      if (!isx && (kWT || wave == 2)) {
+        const int lane = tid & 63, nsb = K / 32;
+        uint32_t o = kOob;
+        __amdgpu_buffer_rsrc_t rss;
+        if constexpr (kWT) {   // W_scale [N, K/32]: column 64 (wave - 2) + lane, bytes 4 kb .. 4 kb + 3
+          const int r = 64 * (wave - 2) + lane;
+          rss = make_rsrc(WS + (int64_t)tn * 128 * ldws);
+          if (r < cols_valid && 4 * kb < nsb) o = (uint32_t)(r * ldws + 4 * kb);
+        } else {               // W_scale [K/32, N]: scale row 4 kb + lane / 2, chunk 0 or 7 of the tile's columns
+          const int sr = 4 * kb + (lane >> 1), c = (lane & 1) ? 7 : 0;
+          rss = make_rsrc(WS + tn * 128);
+          if (lane < 8 && sr < nsb && c * 16 < cols_valid) o = (uint32_t)(sr * ldws + c * 16);
+        }
+        // one byte (the first scale byte the tiles read there): never past a scale row
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rss, LDS(void, scratch + 8192 + (j & 3) * 512 + (wave - 2) * 256), 1,
+                                                  o, 0, 0, 0);
+      }
     }
   };
   prefetch_walk(u, isx ? u.rows : u.cols, tiles_m * tiles_n, nkb, t0, ticks, touch);
@@ -639,7 +663,7 @@ void bigemm_mxfp8_kernel(const uint8_t* __restrict__ X, const uint8_t* __restric
   const int lane = tid & 63;
   const int wave = tid >> 6;
   if (__builtin_expect((int)blockIdx.x >= tiles_m * tiles_n, 0)) {  // a prefetch workgroup
-    u8_prefetch<kWT>(X, W, M, N, K, ldx, ldw, tiles_m, tiles_n, stage0, tid);
+    u8_prefetch<kWT, true>(X, W, WS, M, N, K, ldx, ldw, ldws, tiles_m, tiles_n, stage0, tid);
     return;
   }
   int tm, tn;
@@ -1042,7 +1066,7 @@ void bigemm_i8_kernel(const uint8_t* __restrict__ X, const uint8_t* __restrict__
   const int lane = tid & 63;
   const int wave = tid >> 6;
   if (__builtin_expect((int)blockIdx.x >= tiles_m * tiles_n, 0)) {  // a prefetch workgroup
-    u8_prefetch<kWT>(X, W, M, N, K, ldx, ldw, tiles_m, tiles_n, stage0, tid);
+    u8_prefetch<kWT, false>(X, W, nullptr, M, N, K, ldx, ldw, 0, tiles_m, tiles_n, stage0, tid);
     return;
   }
   int tm, tn;
