@@ -267,6 +267,19 @@ def test_bench_refuses_more_than_one_gpu():
     assert "one GPU only" in r.stderr and r.stdout == ""
 
 
+@pytest.mark.parametrize("kind", ["mxfp8", "i8"])
+def test_bench_profiling_kinds_need_no_sweep(kind):
+    """--kind mxfp8 / i8 (profiling runs of one kernel) are refused with the sweep on: exit status 2
+    with a message, before any device work."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--kind", kind], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "--no-sweep" in r.stderr and r.stdout == ""
+
+
 def test_check_args_split_k():
     """The split-K run's own limits: workspace present, aligned and large enough, and the fp32
     chunk sums addressable through 32-bit offsets within a 128-row tile (128 * N * 4 < 2^31)
