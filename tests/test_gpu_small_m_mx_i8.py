@@ -196,3 +196,36 @@ def test_int8_padded_grid_exact():
         y = bg.mm(x[:m], w)
         torch.cuda.synchronize()
         assert np.array_equal(y.cpu().numpy().astype(np.int64), exact[:m]), f"M = {m}"
+
+
+@pytest.mark.parametrize("path,wt", [("staged", False), ("byte", True)])
+def test_mxfp8_long_k_padded_grid(path, wt):
+    """64 x 1024 x 16384 (8 tiles, 128 K blocks of 128: the prefetch workgroups walk the whole K with
+    the W-scale touches): rows equal to the same rows inside a product of 17 x 8 = 136 tiles (not
+    padded), and parity with the oracle on sampled rows."""
+    K, N, BIG = 16384, 1024, 2176
+    X, W, XS, WS = mx_inputs(170, BIG, N, K)
+    x, xs, w, ws = operands(X, W, XS, WS, path, wt)
+    big = bg.mm(x, w, xs, ws)
+    y = bg.mm(x[:64], w, xs[:64], ws)
+    torch.cuda.synchronize()
+    assert same_bytes(y, big[:64])
+    rows = np.array([0, 31, 63])
+    Y, S = oracle.gemm_mxfp8(X[rows], W, XS[rows], WS)
+    assert oracle.max_normalized_error(y.cpu().numpy()[rows], Y, S) <= TOL
+
+
+@pytest.mark.parametrize("wt", [False, True])
+def test_int8_long_k_padded_grid_exact(wt):
+    """int8 64 x 1024 x 16384 (8 tiles, padded grid): exact against numpy's int64 product (K * 127^2 < 2^31)."""
+    K, N = 16384, 1024
+    rng = np.random.default_rng(180)
+    X = rng.integers(-128, 128, size=(64, K)).astype(np.int8)
+    W = rng.integers(-128, 128, size=(K, N)).astype(np.int8)
+    exact = X.astype(np.int64) @ W.astype(np.int64)
+    x = rows_u8(X.view(np.uint8), K).view(torch.int8)
+    w = (rows_u8(np.ascontiguousarray(W.T).view(np.uint8), K).view(torch.int8).t() if wt
+         else rows_u8(W.view(np.uint8), N).view(torch.int8))
+    y = bg.mm(x, w)
+    torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().numpy().astype(np.int64), exact)
