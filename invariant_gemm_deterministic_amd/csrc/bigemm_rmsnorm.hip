@@ -17,7 +17,10 @@
 //
 // The reduction tree depends on d only. A thread keeps its first four chunks
 // in registers between the passes (all of a row up to d = 8192); chunks past
-// them are read again in pass 2, from the caches.
+// them are read again in pass 2, from the caches. The gamma values of those
+// four chunks are requested with the row, before pass 1, so that pass 2 does
+// not start with a dependent round trip to the cache (bf16 keeps both as raw
+// 16-bit pairs and widens them where they are used).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -60,6 +63,33 @@ __device__ __forceinline__ void load8(const void* row, int c, float (&v)[8]) {
   }
 }
 
+// Eight consecutive elements of a row held as loaded: four dwords of bf16
+// pairs, or eight floats.
+template <bool kBf16>
+struct Raw8;
+template <>
+struct Raw8<true> {
+  i32x4 q;
+  __device__ __forceinline__ void load(const void* row, int c) { q = *((const i32x4*)row + c); }
+  __device__ __forceinline__ void get(float (&v)[8]) const {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t w = (uint32_t)q[e];
+      v[2 * e] = bf16_to_f32(w & 0xFFFFu);
+      v[2 * e + 1] = bf16_to_f32(w >> 16);
+    }
+  }
+};
+template <>
+struct Raw8<false> {
+  float v8[8];
+  __device__ __forceinline__ void load(const void* row, int c) { load8<false>(row, c, v8); }
+  __device__ __forceinline__ void get(float (&v)[8]) const {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = v8[e];
+  }
+};
+
 template <bool kBf16>
 __device__ __forceinline__ void store8(void* row, int c, const float (&v)[8]) {
   if (kBf16) {
@@ -84,17 +114,27 @@ void bigemm_rmsnorm_kernel(const uint8_t* __restrict__ X, int64_t ldx_bytes, con
   uint8_t* y = Y + (int64_t)blockIdx.x * ldy_bytes;
   const int nchunk = D / 8;
 
-  // The thread's first kCached chunks stay in registers for pass 2; chunks
-  // beyond them (D > 8192) are read again there. The order is the same.
-  float xv[kCached][8];
+  // The thread's first kCached chunks, and their gamma, stay in registers for
+  // pass 2; chunks beyond them (D > 8192) are read again there. The order is
+  // the same.
+  Raw8<kBf16> xr[kCached], gr[kCached];
+#pragma unroll
+  for (int i = 0; i < kCached; ++i) {
+    const int c = tid + i * kNormThreads;
+    if (c < nchunk) {
+      xr[i].load(x, c);
+      gr[i].load(gamma, c);
+    }
+  }
   float ss = 0.f;
 #pragma unroll
   for (int i = 0; i < kCached; ++i) {
     const int c = tid + i * kNormThreads;
     if (c < nchunk) {
-      load8<kBf16>(x, c, xv[i]);
+      float v[8];
+      xr[i].get(v);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) ss = fmaf(xv[i][e], xv[i][e], ss);
+      for (int e = 0; e < 8; ++e) ss = fmaf(v[e], v[e], ss);
     }
   }
   for (int c = tid + kCached * kNormThreads; c < nchunk; c += kNormThreads) {
@@ -114,11 +154,12 @@ void bigemm_rmsnorm_kernel(const uint8_t* __restrict__ X, int64_t ldx_bytes, con
   for (int i = 0; i < kCached; ++i) {
     const int c = tid + i * kNormThreads;
     if (c < nchunk) {
-      float g[8];
-      load8<kBf16>(gamma, c, g);
+      float v[8], g[8];
+      xr[i].get(v);
+      gr[i].get(g);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) xv[i][e] = (xv[i][e] * r) * g[e];
-      store8<kBf16>(y, c, xv[i]);
+      for (int e = 0; e < 8; ++e) v[e] = (v[e] * r) * g[e];
+      store8<kBf16>(y, c, v);
     }
   }
   for (int c = tid + kCached * kNormThreads; c < nchunk; c += kNormThreads) {
