@@ -7,14 +7,17 @@ ABI with inputs resident in HBM. Also reported:
 
 * ``m_sweep``: TFLOP/s and % of the bf16 MFMA peak for M = 1 ... 4096 at
   K = N = 4096 (small M rotates among buffer sets larger than the 256 MB
-  last-level cache, so W is read from HBM; ``us_warm_llc`` is the same call on
-  one buffer set), with achieved algorithmic HBM GB/s and % of the roofline
+  last-level cache, so W is read from HBM; ``us_graph`` is the same rotating
+  calls replayed from a captured HIP graph, without the host dispatch of each
+  Python call; ``us_warm_llc`` is the same call on one buffer set), with
+  achieved algorithmic HBM GB/s and % of the roofline
   bound max(flops / MFMA peak, algorithmic bytes / HBM peak);
 * ``other_types_k4096_n4096``: the MXFP8 kernel (E4M3, K-varying E8M0 scales),
   fp16 inputs, bf16 output and int8 inputs at M = 1024 and 4096, each against
   its dense MFMA peak (context, not the metric); MXFP8 and int8 also at M = 1
   and 64 with a cold last-level cache (W rotating over copies, as in
-  ``m_sweep``), with algorithmic HBM GB/s; for bf16, MXFP8 and int8 also
+  ``m_sweep``), with algorithmic HBM GB/s (and ``us_graph``, as in the
+  sweep); for bf16, MXFP8 and int8 also
   W given as [N, K] rows (MXFP8 scales [N, K/32]), timed in blocks of
   back-to-back launches alternating with blocks of the [K, N] call (median
   over four rounds); ``w_transposed_byte_diffs`` compares the [N, K]-row bf16
@@ -111,12 +114,16 @@ def _time_point(torch, stream, fn, reps, warm_s=None):
     return _blocks(torch, stream, fn, reps)[0]
 
 
-def _small_m_entry(kind, m, N, K, t, byts, peak):
-    """A small-M point of the other types (t in ms per call; byts the algorithmic bytes)."""
+def _small_m_entry(kind, m, N, K, t, byts, peak, tg=None):
+    """A small-M point of the other types (t in ms per call; byts the algorithmic bytes; tg the
+    same calls replayed from a HIP graph, ms per call)."""
     f = 2.0 * m * N * K
-    return {"kind": kind, "M": m, "us": round(t * 1e3, 2), "tflops": round(f / (t * 1e-3) / 1e12, 1),
-            "pct_peak": round(100 * f / (t * 1e-3) / 1e12 / peak, 2),
-            "hbm_gbs_algorithmic": round(byts / (t * 1e-3) / 1e9, 0), "cold_llc": True}
+    e = {"kind": kind, "M": m, "us": round(t * 1e3, 2), "tflops": round(f / (t * 1e-3) / 1e12, 1),
+         "pct_peak": round(100 * f / (t * 1e-3) / 1e12 / peak, 2),
+         "hbm_gbs_algorithmic": round(byts / (t * 1e-3) / 1e9, 0), "cold_llc": True}
+    if tg is not None:
+        e["us_graph"] = round(tg * 1e3, 2)
+    return e
 
 
 def _time_ab(torch, stream, fa, fb, reps=10, rounds=BLOCKS):
@@ -237,7 +244,7 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--m", type=int, default=4096, help="rows of the timed headline call (profiling other M)")
     ap.add_argument("--calib-copy", action="store_true",
-                    help="one 256 MiB device copy before the GEMMs (scale reference for byte counters)")
+                    help="one 256 MiB device copy kernel before the GEMMs (scale reference for byte counters)")
     ap.add_argument("--kind", choices=("bf16", "mxfp8", "i8"), default="bf16",
                     help="input family of the headline call (profiling the MXFP8 or int8 kernel; the bench line is bf16)")
     ap.add_argument("--warm-s", type=float, default=WARM_S,
@@ -265,9 +272,11 @@ def main():
     Y = torch.empty((4096, N), dtype=torch.float32, device=dev)
 
     if args.calib_copy:
+        # 256 MiB read and 256 MiB written by one elementwise kernel (b = a * 1), so that it shows
+        # under the counters as a dispatch (a plain copy_ may run on a DMA engine instead)
         a = torch.ones(64 << 20, dtype=torch.float32, device=dev)
         b = torch.empty_like(a)
-        b.copy_(a)
+        torch.mul(a, 1.0, out=b)
         torch.cuda.synchronize()
         del a, b
 
@@ -335,7 +344,12 @@ def main():
                      "hbm_gbs_algorithmic": round(byts / (t * 1e-3) / 1e9, 0),
                      "cold_llc": nsets > 1}
             if nsets > 1:
-                # the same call with one buffer set, W warm in the last-level cache
+                # the same rotating calls replayed from a HIP graph (no host dispatch per call: where
+                # one Python call takes longer to dispatch than the kernel runs, the events above time
+                # the host), and the call with one buffer set, W warm in the last-level cache
+                tg = _time_graph(torch, stream, lambda i: bg.mm(Xs[i % nsets], Ws[i % nsets], out=Ys[i % nsets]),
+                                 reps)
+                entry["us_graph"] = round(tg * 1e3, 2)
                 tw = _time_point(torch, stream, lambda i: bg.mm(Xs[0], Ws[0], out=Ys[0]), 20, 0.1)
                 entry["us_warm_llc"] = round(tw * 1e3, 2)
             sweep.append(entry)
@@ -469,9 +483,10 @@ def main():
             Wc = [Wm] + [Wm.clone() for _ in range(nsets - 1)]
             WSc = [WS] + [WS.clone() for _ in range(nsets - 1)]
             xm, xs, ym = Xm[:m], XS[:m], Y[:m]
-            t = _time_point(torch, stream, lambda i: bg.mm(xm, Wc[i % nsets], xs, WSc[i % nsets], out=ym),
-                            max(20, 2 * nsets))
-            mx.append(_small_m_entry("mxfp8", m, N, K, t, byts, PEAK_FP8_TFLOPS))
+            fn = lambda i: bg.mm(xm, Wc[i % nsets], xs, WSc[i % nsets], out=ym)
+            t = _time_point(torch, stream, fn, max(20, 2 * nsets))
+            tg = _time_graph(torch, stream, fn, max(20, 2 * nsets))
+            mx.append(_small_m_entry("mxfp8", m, N, K, t, byts, PEAK_FP8_TFLOPS, tg))
             del Wc, WSc
         del Xm, Wm, XS, WS, WmT, WST
         # fp16 inputs and int8 inputs on the same tile skeleton, and bf16 output (context)
@@ -514,8 +529,10 @@ def main():
             nsets = max(2, int(np.ceil(600e6 / byts)))
             Wc = [Wi] + [Wi.clone() for _ in range(nsets - 1)]
             xi, yi = Xi[:m], Yi[:m]
-            t = _time_point(torch, stream, lambda i: bg.mm(xi, Wc[i % nsets], out=yi), max(20, 2 * nsets))
-            mx.append(_small_m_entry("i8", m, N, K, t, byts, PEAK_I8_TOPS))
+            fn = lambda i: bg.mm(xi, Wc[i % nsets], out=yi)
+            t = _time_point(torch, stream, fn, max(20, 2 * nsets))
+            tg = _time_graph(torch, stream, fn, max(20, 2 * nsets))
+            mx.append(_small_m_entry("i8", m, N, K, t, byts, PEAK_I8_TOPS, tg))
             del Wc
         del X16, W16, Xi, Wi, WiT, Yi, Yb, WT
 

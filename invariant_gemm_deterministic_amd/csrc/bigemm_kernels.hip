@@ -107,15 +107,21 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(uint32_t u) {
 
 // Store one output element at element index e of the tile-relative buffer
 // (out-of-range e is the kOob sentinel and is dropped): the raw 32-bit
-// accumulator (fp32 or int32), or its bf16 rounding.
-template <bool kOutBf16>
+// accumulator (fp32 or int32), or its bf16 rounding. kStream: a final output,
+// which no kernel of the call reads again, is stored non-temporal (nt), so
+// that its lines do not displace in the XCD's L2 the X and W panel lines the
+// tiles still running there are reading (the same values are stored either
+// way). Split-K chunk sums, which the merge reads next, are stored plainly.
+constexpr int kCachePolicyNt = 2;  // the nt bit of the buffer instructions' cache-policy operand
+template <bool kOutBf16, bool kStream = true>
 __device__ __forceinline__ void store_out(__amdgpu_buffer_rsrc_t ry, bool ok, uint32_t e, uint32_t bits) {
+  constexpr int aux = kStream ? kCachePolicyNt : 0;
   if (kOutBf16) {
     const uint32_t o = ok ? e * 2 : kOob;
-    __builtin_amdgcn_raw_buffer_store_b16((unsigned short)f32_to_bf16_rne(bits), ry, o, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b16((unsigned short)f32_to_bf16_rne(bits), ry, o, 0, aux);
   } else {
     const uint32_t o = ok ? e * 4 : kOob;
-    __builtin_amdgcn_raw_buffer_store_b32(bits, ry, o, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(bits, ry, o, 0, aux);
   }
 }
 
@@ -533,8 +539,8 @@ void bigemm_bf16_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
       // Copy the element out first: bit-casting an ext_vector element
       // expression directly reads element 0 with this compiler.
       const float v = acc[f][r];
-      store_out<kOutBf16>(ry, rl < rows_valid && cl < cols_valid, (uint32_t)(rl * ldy + cl),
-                          __builtin_bit_cast(uint32_t, v));
+      store_out<kOutBf16, !kSplit>(ry, rl < rows_valid && cl < cols_valid, (uint32_t)(rl * ldy + cl),
+                                   __builtin_bit_cast(uint32_t, v));
     }
 }
 
