@@ -144,6 +144,9 @@ BIGEMM_API bigemm_status bigemm_create(const bigemm_desc* desc, bigemm_t* out);
  *
  * Memory: all buffers are device memory owned by the caller. The library
  * allocates nothing per call (this path has no split-K and hence no workspace).
+ * Y is written with non-temporal stores (a finished tile's output does not
+ * stay in the L2 that the other tiles' operands use), so a kernel reading Y
+ * right after the call finds it past the L2.
  * Device: the current HIP device must be the one the handle was created on
  * (BIGEMM_ERR_ARG otherwise, checked on the host before anything is launched).
  * Errors: BIGEMM_ERR_ARG as above; BIGEMM_ERR_DEVICE if the launch fails (the
