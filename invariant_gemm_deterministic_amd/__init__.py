@@ -75,6 +75,8 @@ def library_path() -> str:
 def load():
     """Load libbigemm.so (built in-tree by ``__graft_entry__.build()``); raise if absent."""
     global _lib
+    if _lib is not None:
+        return _lib
     with _lock:
         if _lib is not None:
             return _lib
@@ -234,7 +236,7 @@ def bigemm_run(h: int, M: int, N: int, K: int, X: int, ldx: int, W: int, ldw: in
                X_scale: int = 0, ldxs: int = 0, W_scale: int = 0, ldws: int = 0, stream: int = 0,
                check: bool = True) -> int:
     """Enqueue Y = X W (device pointers as integers). Raises BigemmError unless check=False."""
-    st = load().bigemm_run(ctypes.c_void_p(h) if h else None, M, N, K,
+    st = (_lib or load()).bigemm_run(ctypes.c_void_p(h) if h else None, M, N, K,
                            X or None, ldx, W or None, ldw, Y or None, ldy,
                            X_scale or None, ldxs, W_scale or None, ldws, stream or None)
     if check and st != BIGEMM_OK:
@@ -310,16 +312,6 @@ def _ld(t) -> int:
     return int(t.stride(0)) if t.shape[0] > 1 else int(t.shape[1])
 
 
-def _ld_rows(t) -> int:
-    """Leading dimension of an X, W or Y operand. A single row's stride is arbitrary in torch and
-    only that row is ever addressed, so it is given as the row width rounded up to whole
-    16-byte units (the library's row-alignment rule then holds for any width)."""
-    if t.shape[0] > 1:
-        return int(t.stride(0))
-    per = 16 // t.element_size()
-    return -(-int(t.shape[1]) // per) * per
-
-
 def mm(x, w, x_scale=None, w_scale=None, out=None, stream=None, out_dtype=None, k_chunk=None,
        workspace=None):
     """Y = X W on the GPU through libbigemm.
@@ -350,11 +342,11 @@ def mm(x, w, x_scale=None, w_scale=None, out=None, stream=None, out_dtype=None, 
     K2, N = w.shape
     if K != K2:
         raise ValueError(f"inner dimensions differ: {K} vs {K2}")
+    xst, wst = x.stride(), w.stride()
     # W given as the transposed view of an [N, K] array with contiguous rows.
-    wt = N > 1 and w.stride(1) != 1 and (K == 1 or w.stride(0) == 1)
-    for t in (x, w.t() if wt else w):
-        if not t.is_cuda or (t.shape[1] > 1 and t.stride(1) != 1):
-            raise ValueError("operands must be CUDA tensors with contiguous rows")
+    wt = N > 1 and wst[1] != 1 and (K == 1 or wst[0] == 1)
+    if not (x.is_cuda and w.is_cuda) or (K > 1 and xst[1] != 1) or (not wt and N > 1 and wst[1] != 1):
+        raise ValueError("operands must be CUDA tensors with contiguous rows")
     if x.dtype != w.dtype:
         raise ValueError(f"x and w must have one dtype ({x.dtype} vs {w.dtype})")
     mx = x_scale is not None or w_scale is not None
@@ -376,34 +368,44 @@ def mm(x, w, x_scale=None, w_scale=None, out=None, stream=None, out_dtype=None, 
         out_dtype = out.dtype
     elif out_dtype is None:
         out_dtype = torch.int32 if kind == "i8" else torch.float32
-    ytypes = {torch.float32: BIGEMM_F32, torch.bfloat16: BIGEMM_BF16, torch.int32: BIGEMM_I32}
-    if out_dtype not in ytypes:
+    ytype = _ytypes(torch).get(out_dtype)
+    if ytype is None:
         raise ValueError(f"unsupported output dtype {out_dtype}")
-    dev = x.device.index if x.device.index is not None else torch.cuda.current_device()
+    dev = x.get_device()
     if out is None:
         # rows start 16-byte aligned: for a width that leaves them short, allocate padded rows
         per = 16 // torch.empty((), dtype=out_dtype).element_size()
         ldo = -(-N // per) * per
         out = torch.empty((M, ldo), dtype=out_dtype, device=x.device)[:, :N]
-    if tuple(out.shape) != (M, N) or (N > 1 and out.stride(1) != 1):
+    ost = out.stride()
+    if out.shape != (M, N) or (N > 1 and ost[1] != 1):
         raise ValueError("out must be [M, N] with contiguous rows")
     if stream is None:
-        stream = torch.cuda.current_stream(x.device).cuda_stream
-    ldw = _ld_rows(w.t()) if wt else _ld_rows(w)
+        stream = _current_stream(torch, x)
+    # Leading dimensions (elements). A single row's stride is arbitrary in torch and only that row is
+    # addressed, so it is given as the row width rounded up to whole 16-byte units.
+    ldx = xst[0] if M > 1 else _ld_width(K, x.element_size())
+    if wt:   # rows of the [N, K] array w.t()
+        ldw = wst[1] if N > 1 else _ld_width(K, w.element_size())
+    else:
+        ldw = wst[0] if K > 1 else _ld_width(N, w.element_size())
+    ldy = ost[0] if M > 1 else _ld_width(N, out.element_size())
     # The handle belongs to x's device, and the library runs a handle only on its own device.
-    with torch.cuda.device(dev):
+    with _on_device(torch, dev):
         if k_chunk:
             if kind not in ("bf16", "f16"):
                 raise ValueError("split-K is provided for bf16 and fp16 inputs")
-            h = _handle(kind, dev, ytypes[out_dtype], int(k_chunk), wt)
+            h = _handle(kind, dev, ytype, int(k_chunk), wt)
             need = bigemm_workspace_size(h, M, N, K)
             if workspace is None:
                 workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
             ws_bytes = workspace.numel() * workspace.element_size()
-            bigemm_run_ws(h, M, N, K, x.data_ptr(), _ld_rows(x), w.data_ptr(), ldw, out.data_ptr(),
-                          _ld_rows(out), 0, 0, 0, 0, workspace.data_ptr(), ws_bytes, stream)
+            bigemm_run_ws(h, M, N, K, x.data_ptr(), ldx, w.data_ptr(), ldw, out.data_ptr(),
+                          ldy, 0, 0, 0, 0, workspace.data_ptr(), ws_bytes, stream)
             return out
-        h = _handle(kind, dev, ytypes[out_dtype], 0, wt)  # raises BigemmError for a combination not provided
+        h = _handles.get((kind, ytype, 0, wt, dev))
+        if h is None:
+            h = _handle(kind, dev, ytype, 0, wt)  # raises BigemmError for a combination not provided
         if mx:
             if tuple(x_scale.shape) != (M, K // 32) or tuple(w_scale.shape) != (K // 32, N):
                 raise ValueError(f"scales must be [M, K/32] = [{M}, {K // 32}] and [K/32, N] = [{K // 32}, {N}]")
@@ -412,12 +414,55 @@ def mm(x, w, x_scale=None, w_scale=None, out=None, stream=None, out_dtype=None, 
                 if not t.is_cuda or t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
                     raise ValueError("scales must be 2-D CUDA tensors with contiguous rows "
                                      "(w_scale in the same layout as w)")
-            bigemm_run(h, M, N, K, x.data_ptr(), _ld_rows(x), w.data_ptr(), ldw, out.data_ptr(), _ld_rows(out),
+            bigemm_run(h, M, N, K, x.data_ptr(), ldx, w.data_ptr(), ldw, out.data_ptr(), ldy,
                        x_scale.data_ptr(), _ld(x_scale), w_scale.data_ptr(), _ld(ws), stream)
         else:
-            bigemm_run(h, M, N, K, x.data_ptr(), _ld_rows(x), w.data_ptr(), ldw, out.data_ptr(), _ld_rows(out),
+            bigemm_run(h, M, N, K, x.data_ptr(), ldx, w.data_ptr(), ldw, out.data_ptr(), ldy,
                        0, 0, 0, 0, stream)
     return out
+
+
+_YTYPES = None
+
+
+def _ytypes(torch):
+    global _YTYPES
+    if _YTYPES is None:
+        _YTYPES = {torch.float32: BIGEMM_F32, torch.bfloat16: BIGEMM_BF16, torch.int32: BIGEMM_I32}
+    return _YTYPES
+
+
+def _ld_width(width: int, esize: int) -> int:
+    """A single row's leading dimension: its width rounded up to whole 16-byte units."""
+    per = 16 // esize
+    return -(-int(width) // per) * per
+
+
+def _current_stream(torch, t) -> int:
+    """The raw current stream of t's device (the private accessor skips building a Stream object)."""
+    get = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if get is not None:
+        return get(t.get_device())
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+class _NoDeviceSwitch:
+    def __enter__(self):
+        return None
+
+    def __exit__(self, *exc):
+        return False
+
+
+_NO_SWITCH = _NoDeviceSwitch()
+
+
+def _on_device(torch, dev: int):
+    """torch.cuda.device(dev), or nothing when dev is already the current device."""
+    get = getattr(torch._C, "_cuda_getDevice", None)
+    if get is not None and get() == dev:
+        return _NO_SWITCH
+    return torch.cuda.device(dev)
 
 
 def bigemm_rmsnorm(dtype: int, M: int, D: int, X: int, ldx: int, gamma: int, Y: int, ldy: int, eps: float,
