@@ -468,7 +468,7 @@ def _on_device(torch, dev: int):
 def bigemm_rmsnorm(dtype: int, M: int, D: int, X: int, ldx: int, gamma: int, Y: int, ldy: int, eps: float,
                    stream: int = 0, check: bool = True) -> int:
     """Enqueue the batch-invariant RMSNorm (device pointers as integers)."""
-    st = load().bigemm_rmsnorm(int(dtype), M, D, X or None, ldx, gamma or None, Y or None, ldy, float(eps),
+    st = (_lib or load()).bigemm_rmsnorm(int(dtype), M, D, X or None, ldx, gamma or None, Y or None, ldy, float(eps),
                                stream or None)
     if check and st != BIGEMM_OK:
         raise BigemmError(st, "bigemm_rmsnorm")
@@ -496,16 +496,20 @@ def rmsnorm(x, gamma, eps: float = 1e-6, out=None, stream=None):
     else:
         raise ValueError(f"unsupported dtype {x.dtype}")
     M, D = x.shape
-    if (D > 1 and x.stride(1) != 1) or not gamma.is_contiguous():
+    xst = x.stride()
+    if (D > 1 and xst[1] != 1) or not gamma.is_contiguous():
         raise ValueError("rows must be contiguous")
     if out is None:
         out = torch.empty_like(x)
-    if out.shape != x.shape or out.dtype != x.dtype or (D > 1 and out.stride(1) != 1):
+    ost = out.stride()
+    if out.shape != x.shape or out.dtype != x.dtype or (D > 1 and ost[1] != 1):
         raise ValueError("out must match x")
     if stream is None:
-        stream = torch.cuda.current_stream(x.device).cuda_stream
-    with torch.cuda.device(x.device):
-        bigemm_rmsnorm(dtype, M, D, x.data_ptr(), _ld(x), gamma.data_ptr(), out.data_ptr(), _ld(out), eps, stream)
+        stream = _current_stream(torch, x)
+    ldx = xst[0] if M > 1 else D
+    ldy = ost[0] if M > 1 else D
+    with _on_device(torch, x.get_device()):
+        bigemm_rmsnorm(dtype, M, D, x.data_ptr(), ldx, gamma.data_ptr(), out.data_ptr(), ldy, eps, stream)
     return out
 
 
