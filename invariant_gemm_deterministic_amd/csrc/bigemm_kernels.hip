@@ -1267,7 +1267,11 @@ void bigemm_i8_kernel(const uint8_t* __restrict__ X, const uint8_t* __restrict__
 // chunk order in fp32 (then rounded once to bf16 for a bf16 output). P is
 // [S][M][N] fp32. kVec4 (N a multiple of 4): one thread per four consecutive
 // outputs of a row, 16-byte loads; otherwise one thread per output. The sums
-// and their order are the same either way.
+// and their order are the same either way. The chunk sums are loaded up to
+// kMergeAhead at a time before they are added (a loop with a run-time count
+// otherwise waits for each load before issuing the next); the adds keep
+// ascending chunk order.
+constexpr int kMergeAhead = 8;
 template <bool kOutBf16, bool kVec4>
 __global__ __launch_bounds__(256)
 void bigemm_split_merge_kernel(const float* __restrict__ P, void* __restrict__ Y, int M, int N, int64_t ldy,
@@ -1280,12 +1284,19 @@ void bigemm_split_merge_kernel(const float* __restrict__ P, void* __restrict__ Y
     const int j = (int)(q - (int64_t)i * nq) * 4;
     const float* p = P + (int64_t)i * N + j;
     float4 acc = *(const float4*)p;
-    for (int s = 1; s < nsplit; ++s) {
-      const float4 v = *(const float4*)(p + s * split_stride);
-      acc.x += v.x;
-      acc.y += v.y;
-      acc.z += v.z;
-      acc.w += v.w;
+    for (int s = 1; s < nsplit; s += kMergeAhead) {
+      float4 v[kMergeAhead];
+#pragma unroll
+      for (int u = 0; u < kMergeAhead; ++u)
+        if (s + u < nsplit) v[u] = *(const float4*)(p + (s + u) * split_stride);
+#pragma unroll
+      for (int u = 0; u < kMergeAhead; ++u)
+        if (s + u < nsplit) {
+          acc.x += v[u].x;
+          acc.y += v[u].y;
+          acc.z += v[u].z;
+          acc.w += v[u].w;
+        }
     }
     if (kOutBf16) {
       const uint32_t b0 = f32_to_bf16_rne(__builtin_bit_cast(uint32_t, acc.x));
@@ -1306,7 +1317,15 @@ void bigemm_split_merge_kernel(const float* __restrict__ P, void* __restrict__ Y
     const int j = (int)(q - (int64_t)i * N);
     const float* p = P + (int64_t)i * N + j;
     float acc = *p;
-    for (int s = 1; s < nsplit; ++s) acc += p[s * split_stride];
+    for (int s = 1; s < nsplit; s += kMergeAhead) {
+      float v[kMergeAhead];
+#pragma unroll
+      for (int u = 0; u < kMergeAhead; ++u)
+        if (s + u < nsplit) v[u] = p[(s + u) * split_stride];
+#pragma unroll
+      for (int u = 0; u < kMergeAhead; ++u)
+        if (s + u < nsplit) acc += v[u];
+    }
     if (kOutBf16)
       ((uint16_t*)Y)[(int64_t)i * ldy + j] = (uint16_t)f32_to_bf16_rne(__builtin_bit_cast(uint32_t, acc));
     else
