@@ -125,3 +125,25 @@ def test_split_k_workspace_rules():
     assert bg.bigemm_run_ws(*args, ws.data_ptr(), need, 0, check=False) == bg.BIGEMM_OK
     torch.cuda.synchronize()
     assert not (y == 7.0).all()
+
+
+@pytest.mark.parametrize("N", [128, 130])
+def test_split_k_merge_adds_chunk_sums_in_ascending_order(N):
+    """Each chunk sum is the unsplit kernel's product over that K slice (the same MFMA chain from zero),
+    and the merge adds the chunk sums in ascending order in fp32: rebuilt on the CPU from unsplit calls
+    on the K slices, the split-K output matches bit for bit. 20 chunks cover the merge's look-ahead
+    groups of 8 and a partial group; N = 130 takes the one-output-per-thread merge (W rows padded to
+    keep them 16-byte aligned)."""
+    M, K, kc = 37, 2560, 128
+    X = normal_bf16(91, (M, K))
+    Wp = np.zeros((K, 136), dtype=X.dtype)
+    Wp[:, :N] = normal_bf16(92, (K, N))
+    xd, wpd = dev_bf16(X), dev_bf16(Wp)
+    wd = wpd[:, :N]
+    y = split(xd, wd, kc).cpu().numpy()
+    acc = None
+    for c in range(K // kc):
+        yc = run((xd[:, c * kc:(c + 1) * kc],), (wpd[c * kc:(c + 1) * kc, :N],)).cpu().numpy().astype(np.float32)
+        acc = yc if acc is None else (acc + yc).astype(np.float32)
+    assert y.dtype == np.float32 and acc.shape == y.shape
+    assert np.array_equal(y.view(np.int32), acc.view(np.int32))
