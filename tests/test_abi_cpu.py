@@ -306,3 +306,29 @@ def test_check_args_split_k():
     assert sk(1, n_bad, 1024, desc=BFO) == bg.BIGEMM_ERR_ARG
     assert chk((bg.BIGEMM_BF16, bg.BIGEMM_BF16, bg.BIGEMM_BF16, 0), 1, n_bad, 1024) == bg.BIGEMM_OK
     assert sk(1, n_bad, 512, desc=BFO, ws=0, wsb=0) == bg.BIGEMM_OK    # unsplit: the ordinary limits only
+
+
+def test_bench_traffic_figure_follows_the_kernel_source(tmp_path, monkeypatch):
+    """bench.py reports the counted HBM traffic only while the kernel source is the one the counters
+    were taken on: the summary's kernel_source_sha256 must equal the source's hash, else (or when
+    either file is missing) the figure is null. The committed summary carries every value it needs."""
+    import hashlib
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("bench_mod", os.path.join(ROOT, "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    committed = open(bench.TRAFFIC_SUMMARY).read()
+    for key in ("kernel_source_sha256=", "fetch_scale=", "write_scale=", "traffic_bytes_per_launch="):
+        assert key in committed
+    src = tmp_path / "kernels.hip"
+    src.write_bytes(b"// one kernel source\n")
+    digest = hashlib.sha256(src.read_bytes()).hexdigest()
+    summ = tmp_path / "traffic.md"
+    summ.write_text(f"# summary\n\n| a | b |\n\nkernel_source_sha256={digest}\ntraffic_bytes_per_launch=470109056\n")
+    monkeypatch.setattr(bench, "KERNEL_SOURCE", str(src))
+    monkeypatch.setattr(bench, "TRAFFIC_SUMMARY", str(summ))
+    assert bench.measured_traffic() == 470109056
+    src.write_bytes(b"// the source after an edit\n")
+    assert bench.measured_traffic() is None
+    monkeypatch.setattr(bench, "TRAFFIC_SUMMARY", str(tmp_path / "missing.md"))
+    assert bench.measured_traffic() is None
